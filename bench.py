@@ -1,0 +1,383 @@
+"""Benchmark of the fused low-bit dequant-GEMV hot path on one MI355X.
+
+Default workload: INT4 group-128 fused dequant-GEMV, W 8192 x 8192 (Student-t(4)
+* 0.015, synthetic), x bf16 N(0, 1), batch 1.  A step is one fused GEMV over the
+whole matrix.  The weights are cycled through a rotation pool of distinct
+device copies (>= 1.1 GiB in total) so every step reads HBM rather than the
+256 MB Infinity Cache; activations and outputs stay resident.  The K timed steps
+are captured once in a HIP graph and replayed, bracketed by device syncs, and
+timed with HIP events on the launch stream.
+
+Prints one JSON line: effective weight GB/s (algorithmic bytes per step / time),
+the roofline fraction against the 8 TB/s HBM peak and, for context, the fp64
+oracle timed on the host cores on the same workload.
+
+Other workloads (``--workload``): ternary_1k, int4_8k_b4, moe_t1, moe_t8,
+cassandra_spec, cassandra_restore, cassandra_verify, mx_verify and the FFN-shaped
+int4/ternary matrices; ``--all FILE`` measures every one and appends a JSON line
+per workload to FILE (the stdout line is still the default workload's).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+POOL_BYTES = int(1.1 * 2 ** 30)
+METRIC = "effective weight GB/s (fraction of HBM peak), fused dequant-GEMV batch 1"
+
+
+def _x_dev(x_bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(dev)
+
+
+class Workload:
+    """A device-resident workload: `launch(i)` enqueues step i (rotation copy i % n)."""
+    name = ""
+    kernel = ""          # kernel symbol substring, for profiles
+    fmt_name = ""
+    dtype = "bf16"
+
+    def bytes_per_step(self) -> int: ...
+    def launch(self, i: int) -> None: ...
+
+
+def _pool_copies(bytes_weights):
+    return max(1, math.ceil(POOL_BYTES / max(1, bytes_weights)))
+
+
+class BlockQuantGemv(Workload):
+    def __init__(self, kind, M, K, B, dev, name, seed_name):
+        import torch
+        import memory_bound_decode_amd as mbd
+        import synth
+        self.name, self.kind, self.M, self.K, self.B = name, kind, M, K, B
+        self.kernel = "gemv_bq_kernel"
+        self.fmt_name = {"int4": "int4_g128", "ternary": "ternary_b128"}[kind]
+        wl = synth.WORKLOADS[seed_name]
+        if (wl.M, wl.K) == (M, K):
+            self.w = synth.gen_weights(wl)
+        else:
+            self.w = synth.f32_to_bf16_bits(
+                synth.gen_weight_rows(wl.seed + 1000 * M + K, M, K, wl.dist, wl.scale).astype(np.float32))
+        self.x = synth.gen_x(wl, B, K)
+        fmt = mbd.MBD_INT4_G128 if kind == "int4" else mbd.MBD_TERNARY_B128
+        self.packed = mbd.mbd_pack(fmt, self.w)
+        st = self.packed.stats()
+        self.bpw = st.bpw
+        wbytes = sum(b for _, b in self.packed.sections().values())
+        self.weight_bytes = wbytes
+        self.n = _pool_copies(wbytes)
+        self.copies = [mbd.to_device(self.packed, dev) for _ in range(self.n)]
+        self.xt = _x_dev(self.x, dev)
+        self.y = torch.empty((B, M), dtype=torch.float32, device=dev)
+        self.mbd = mbd
+
+    def bytes_per_step(self):
+        return self.weight_bytes + self.B * self.K * 2 + self.B * self.M * 4
+
+    def launch(self, i):
+        self.mbd.mbd_gemv(self.copies[i % self.n], self.xt, self.y)
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "K": self.K, "batch": self.B,
+                "weight_format": self.fmt_name, "bits_per_weight": round(self.bpw, 4),
+                "rotation_copies": self.n, "bytes_per_step": self.bytes_per_step()}
+
+    def oracle_call(self):
+        """One oracle call: unpack + dequant from the packed sections + fp64 matvec."""
+        from oracle import gemv, int4, ternary
+        mod = int4 if self.kind == "int4" else ternary
+        codes = self.packed.section("codes", np.uint32).reshape(self.M, -1)
+        scales = self.packed.section("scales", np.uint16).reshape(self.M, -1)
+        return gemv.gemv(mod.unpack_dequant(codes, scales, self.K), self.x)
+
+    def device_output(self):
+        import torch
+        self.launch(0)
+        torch.cuda.synchronize()
+        return self.y.cpu().numpy()
+
+
+class MoeGemv(Workload):
+    def __init__(self, T, dev):
+        import torch
+        import memory_bound_decode_amd as mbd
+        import synth
+        wl = synth.WORKLOADS["ternary_moe"]
+        self.name, self.T, self.kernel, self.fmt_name = "ternary_moe_t%d" % T, T, "moe_bq_kernel", "ternary_b128"
+        self.routes = synth.gen_routes(wl, T)
+        ups = np.concatenate([synth.gen_expert(wl, e, "up") for e in range(wl.experts)])
+        dns = np.concatenate([synth.gen_expert(wl, e, "down") for e in range(wl.experts)])
+        pu = mbd.mbd_pack(mbd.MBD_TERNARY_B128, ups)
+        pd = mbd.mbd_pack(mbd.MBD_TERNARY_B128, dns)
+        per_expert = (sum(b for _, b in pu.sections().values()) + sum(b for _, b in pd.sections().values())) // wl.experts
+        self.distinct = len(set(self.routes.reshape(-1).tolist()))
+        self.weight_bytes = per_expert * self.distinct
+        self.n = _pool_copies(per_expert * wl.experts)
+        self.up = [mbd.to_device(pu, dev, n_mats=wl.experts) for _ in range(self.n)]
+        self.dn = [mbd.to_device(pd, dev, n_mats=wl.experts) for _ in range(self.n)]
+        self.x = _x_dev(synth.gen_x(wl, T, wl.K), dev)
+        self.a = _x_dev(synth.gen_down_inputs(wl, T).reshape(T * wl.topk, wl.M), dev)
+        self.r = torch.from_numpy(self.routes).to(dev)
+        self.yu = torch.empty((T, wl.topk, wl.M), dtype=torch.float32, device=dev)
+        self.yd = torch.empty((T, wl.topk, wl.K), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(mbd.mbd_moe_workspace_bytes(wl.experts, T, wl.topk), dtype=torch.uint8, device=dev)
+        self.wl, self.mbd = wl, mbd
+
+    def bytes_per_step(self):
+        wl, T = self.wl, self.T
+        act = T * wl.K * 2 + T * wl.topk * wl.M * 2 + T * wl.topk * 4
+        out = T * wl.topk * (wl.M + wl.K) * 4
+        return self.weight_bytes + act + out
+
+    def launch(self, i):
+        m = self.mbd
+        m.mbd_moe_gemv(self.up[i % self.n], self.r, self.x, False, self.yu, self.ws)
+        m.mbd_moe_gemv(self.dn[i % self.n], self.r, self.a, True, self.yd, self.ws)
+
+    def config(self):
+        return {"workload": self.name, "experts": 64, "topk": 8, "tokens": self.T, "distinct_experts": self.distinct,
+                "up": [1536, 4096], "down": [4096, 1536], "weight_format": self.fmt_name,
+                "rotation_copies": self.n, "bytes_per_step": self.bytes_per_step()}
+
+
+class CassandraWl(Workload):
+    def __init__(self, mode, dev):
+        import torch
+        import memory_bound_decode_amd as mbd
+        import synth
+        wl = synth.WORKLOADS["cassandra_spec" if mode == "spec" else "cassandra_verify"]
+        self.mode, self.M, self.K = mode, wl.M, wl.K
+        self.w = synth.gen_weights(wl)
+        norms = synth.gen_act_norms(wl)
+        self.fmt_name = "cassandra" if mode != "mx" else "mx32"
+        if mode == "mx":
+            p = mbd.mbd_pack(mbd.MBD_MX32, self.w)
+            used = list(p.sections().keys())
+        else:
+            p = mbd.mbd_pack(mbd.MBD_CASSANDRA, self.w, norms)
+            used = list(mbd.SPEC_SECTIONS) if mode == "spec" else list(mbd.SECTION_NAMES[mbd.MBD_CASSANDRA])
+        st = p.stats()
+        self.stats = {"spec_bpw": round(st.spec_bpw, 4), "bpw": round(st.bpw, 4),
+                      "exp_entropy_bits": round(st.exp_entropy_bits, 4), "unary_avg_bits": round(st.unary_avg_bits, 4),
+                      "n_sym": st.n_sym, "kept": st.n_kept}
+        secs = p.sections()
+        self.weight_bytes = sum(secs[k][1] for k in used)
+        self.n = _pool_copies(self.weight_bytes)
+        self.copies = [mbd.to_device(p, dev, only=used) for _ in range(self.n)]
+        self.B = {"spec": 1, "restore": 0, "verify": 16, "mx": 16}[mode]
+        self.name = {"spec": "cassandra_spec_gemv_4096x14336_b1", "restore": "cassandra_restore_8192x28672",
+                     "verify": "cassandra_verify_gemm_8192x28672_b16", "mx": "mx32_gemm_8192x28672_b16"}[mode]
+        self.kernel = {"spec": "spec_gemv_kernel", "restore": "decode_dense_kernel", "verify": "verify_gemm_kernel",
+                       "mx": "mx_gemm_kernel"}[mode]
+        if self.B:
+            self.xt = _x_dev(synth.gen_x(wl, self.B), dev)
+            self.y = torch.empty((self.B, self.M), dtype=torch.float32, device=dev)
+        else:
+            self.out = torch.empty((self.M, self.K), dtype=torch.int16, device=dev)
+        self.mbd = mbd
+
+    def bytes_per_step(self):
+        if self.mode == "restore":
+            return self.weight_bytes + self.M * self.K * 2
+        return self.weight_bytes + self.B * self.K * 2 + self.B * self.M * 4
+
+    def launch(self, i):
+        m, c = self.mbd, self.copies[i % self.n]
+        if self.mode == "spec":
+            m.mbd_spec_gemv(c, self.xt, self.y)
+        elif self.mode == "restore":
+            m.mbd_verify_restore(c, self.out)
+        else:
+            m.mbd_gemv(c, self.xt, self.y)
+
+    def config(self):
+        d = {"workload": self.name, "M": self.M, "K": self.K, "batch": self.B, "weight_format": self.fmt_name,
+             "rotation_copies": self.n, "bytes_per_step": self.bytes_per_step()}
+        d.update(self.stats)
+        return d
+
+
+def make_workload(name, dev):
+    if name == "int4_8k":
+        return BlockQuantGemv("int4", 8192, 8192, 1, dev, "int4_g128_gemv_8192x8192_b1", "int4_8k")
+    if name == "int4_8k_b4":
+        return BlockQuantGemv("int4", 8192, 8192, 4, dev, "int4_g128_gemv_8192x8192_b4", "int4_8k")
+    if name == "ternary_1k":
+        return BlockQuantGemv("ternary", 1024, 1024, 1, dev, "ternary_b128_gemv_1024x1024_b1", "ternary_1k")
+    for kind, tag in (("int4", "int4_8k"), ("ternary", "ternary_moe")):
+        for (M, K) in ((4096, 14336), (14336, 4096), (8192, 28672)):
+            if name == "%s_%dx%d" % (kind, M, K):
+                return BlockQuantGemv(kind, M, K, 1, dev, "%s_gemv_%dx%d_b1" % (
+                    "int4_g128" if kind == "int4" else "ternary_b128", M, K), tag)
+    if name == "moe_t1":
+        return MoeGemv(1, dev)
+    if name == "moe_t8":
+        return MoeGemv(8, dev)
+    if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify"):
+        return CassandraWl({"cassandra_spec": "spec", "cassandra_restore": "restore",
+                            "cassandra_verify": "verify", "mx_verify": "mx"}[name], dev)
+    raise SystemExit("unknown workload %s" % name)
+
+
+ALL = ["int4_8k", "int4_8k_b4", "ternary_1k", "int4_4096x14336", "int4_14336x4096", "int4_8192x28672",
+       "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
+       "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify"]
+
+
+def time_workload(wl, steps, warmup, use_graph=True):
+    """(seconds for `steps` steps, per-step ms) with HIP events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(min(warmup, 3)):
+        wl.launch(i)                                     # eager warm-up (first-call set-up)
+    torch.cuda.synchronize()
+    if use_graph:
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            for i in range(warmup):
+                wl.launch(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                wl.launch(warmup + i)
+        torch.cuda.synchronize()
+        gw.replay()
+    else:
+        for i in range(warmup):
+            wl.launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if use_graph:
+        g.replay()
+    else:
+        for i in range(steps):
+            wl.launch(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1000.0
+    return sec, 1000.0 * sec / steps
+
+
+def traffic_from_profiles(wl):
+    """Measured HBM bytes per step from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.json" % wl.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_step")
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for s in ("gemv.hip", "cassandra.hip"):
+        with open(os.path.join(ROOT, "memory_bound_decode_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """Time the fp64 oracle (unpack + dequant + matvec) on the host for ~budget_s."""
+    if not hasattr(wl, "oracle_call"):
+        return None, None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:                                    # pragma: no cover
+        blas = 1
+    t0 = time.perf_counter()
+    ref = wl.oracle_call()
+    calls, elapsed = 1, time.perf_counter() - t0
+    while elapsed < budget_s and calls < 50:
+        t1 = time.perf_counter()
+        wl.oracle_call()
+        elapsed += time.perf_counter() - t1
+        calls += 1
+    gbs = wl.bytes_per_step() * calls / elapsed / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+            "sample": "%d full oracle calls (unpack + fp64 dequant + numpy fp64 matvec) over the whole "
+                      "%s matrix in %.1f s; elementwise steps single-threaded, matvec on %d BLAS threads"
+                      % (calls, wl.name, elapsed, blas)}, ref
+
+
+def measure(name, dev, steps, warmup, with_cpu):
+    wl = make_workload(name, dev)
+    sec, ms = time_workload(wl, steps, warmup)
+    bps = wl.bytes_per_step()
+    gbs = bps * steps / sec / 1e9
+    traffic = traffic_from_profiles(wl)
+    out = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": wl.config(),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kernel": wl.kernel,
+    }
+    if hasattr(wl, "B") and getattr(wl, "B", 0):
+        out["tok_per_s_equiv"] = round(wl.B / (ms / 1000.0), 1)
+    if with_cpu:
+        cb, ref = cpu_baseline(wl)
+        out["cpu_baseline"] = cb
+        if ref is not None:
+            from oracle import gemv
+            out["parity_rel_l2"] = gemv.rel_l2(wl.device_output(), ref)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="int4_8k")
+    ap.add_argument("--all", default=None, help="append one JSON line per workload to this file")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the hot path is a single-GPU kernel and "
+              "multi-GPU runs are not part of this build (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.all:
+        for name in ALL:
+            if name == args.workload:
+                continue
+            print("measuring", name, file=sys.stderr, flush=True)
+            r = measure(name, dev, args.steps, args.warmup, with_cpu=False)
+            with open(args.all, "a") as f:
+                f.write(json.dumps(r) + "\n")
+            torch.cuda.empty_cache()
+    res = measure(args.workload, dev, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    if args.all:
+        with open(args.all, "a") as f:
+            f.write(json.dumps(res) + "\n")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

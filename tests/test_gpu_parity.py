@@ -1,0 +1,326 @@
+"""GPU parity: every libmbd device call against the fp64 oracle on the same seeded
+inputs -- bit-exact for packed/restored bits, rel-L2 <= 1e-3 for GEMV outputs
+(fp32 accumulation of bf16 activations) -- at small ragged shapes and at the full
+workload sizes in the launch configuration the bench uses."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import bits, cassandra, gemv, int4, mx, ternary
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import memory_bound_decode_amd as mbd
+    mbd.lib()
+    return torch.device("cuda:0")
+
+
+def _mbd():
+    import memory_bound_decode_amd as mbd
+    return mbd
+
+
+def _x_dev(x_bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(dev)
+
+
+def _rand_w(seed, M, K, scale=0.02):
+    rng = np.random.default_rng(seed)
+    return synth.f32_to_bf16_bits((rng.standard_t(4, (M, K)) * scale).astype(np.float32))
+
+
+def _rand_x(seed, B, K):
+    return synth.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal((B, K)).astype(np.float32))
+
+
+def _run_gemv(dw, x_bits, dev):
+    mbd = _mbd()
+    B = x_bits.shape[0]
+    y = torch.full((B, dw.M), float("nan"), dtype=torch.float32, device=dev)
+    mbd.mbd_gemv(dw, _x_dev(x_bits, dev), y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+QUANT = {"ternary": ternary, "int4": int4}
+
+
+def _fmt(kind):
+    mbd = _mbd()
+    return {"ternary": mbd.MBD_TERNARY_B128, "int4": mbd.MBD_INT4_G128}[kind]
+
+
+# ------------------------------------------------------------ ternary / INT4 GEMV
+
+RAGGED = [(1, 128), (3, 384), (100, 1152), (333, 1536), (64, 4096), (17, 8320), (5, 128 * 45)]
+
+
+@pytest.mark.parametrize("kind", ["ternary", "int4"])
+@pytest.mark.parametrize("M,K", RAGGED)
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 16])
+def test_gemv_ragged(dev, kind, M, K, B):
+    print("case gemv", kind, M, K, B, flush=True)
+    w = _rand_w(M * 7 + K, M, K)
+    x = _rand_x(B + K, B, K)
+    dw = _mbd().to_device(_mbd().mbd_pack(_fmt(kind), w), dev)
+    q, s = QUANT[kind].quantize(w)
+    ref = gemv.gemv(QUANT[kind].dequant(q, s), x)
+    y = _run_gemv(dw, x, dev)
+    assert np.all(np.isfinite(y))
+    assert gemv.rel_l2(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("kind", ["ternary", "int4"])
+def test_dequant_exact(dev, kind):
+    mbd = _mbd()
+    M, K = 77, 1152
+    w = _rand_w(5, M, K)
+    w[3, :128] = 0                                   # all-zero block / group
+    dw = mbd.to_device(mbd.mbd_pack(_fmt(kind), w), dev)
+    out = torch.empty((M, K), dtype=torch.float32, device=dev)
+    mbd.mbd_dequant(dw, out)
+    torch.cuda.synchronize()
+    q, s = QUANT[kind].quantize(w)
+    np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), QUANT[kind].dequant(q, s))
+
+
+def test_gemv_ternary_1k_full(dev):
+    wl = synth.WORKLOADS["ternary_1k"]
+    w = synth.gen_weights(wl)
+    x = synth.gen_x(wl, 1)
+    dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_TERNARY_B128, w), dev)
+    q, s = ternary.quantize(w)
+    ref = gemv.gemv(ternary.dequant(q, s), x)
+    assert gemv.rel_l2(_run_gemv(dw, x, dev), ref) <= TOL
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_gemv_int4_8k_full(dev, B):
+    wl = synth.WORKLOADS["int4_8k"]
+    w = synth.gen_weights(wl)
+    x = synth.gen_x(wl, B)
+    dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_INT4_G128, w), dev)
+    q, s = int4.quantize(w)
+    ref = gemv.gemv(int4.dequant(q, s), x)
+    y = _run_gemv(dw, x, dev)
+    err = gemv.rel_l2(y, ref)
+    print("int4_8k B=%d rel_l2=%.3e" % (B, err), flush=True)
+    assert err <= TOL
+
+
+def test_gemv_deterministic(dev):
+    wl = synth.WORKLOADS["int4_8k"]
+    w = synth.gen_weights(wl, 0, 1024)
+    x = synth.gen_x(wl, 1)
+    dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_INT4_G128, w), dev)
+    y1 = _run_gemv(dw, x, dev)
+    y2 = _run_gemv(dw, x, dev)
+    np.testing.assert_array_equal(y1, y2)
+
+
+def test_gemv_empty_and_errors(dev):
+    mbd = _mbd()
+    w = _rand_w(1, 4, 256)
+    dw = mbd.to_device(mbd.mbd_pack(mbd.MBD_INT4_G128, w), dev)
+    x = _x_dev(_rand_x(1, 1, 256), dev)
+    y = torch.empty((17, 4), dtype=torch.float32, device=dev)
+    with pytest.raises(mbd.MbdError) as e:
+        mbd.lib()  # noqa
+        st = mbd.lib().mbd_gemv(dw.ref(), mbd._ptr(x), 17, mbd._ptr(y), None)
+        mbd.check(st, "gemv")
+    assert e.value.status == mbd.MBD_ESHAPE
+    dw.desc.M = 0                                     # empty matrix: a no-op
+    mbd.mbd_gemv(dw, x, y[:1])
+
+
+# ------------------------------------------------------------ MoE
+
+def _moe_setup(dev, T, which):
+    mbd = _mbd()
+    wl = synth.WORKLOADS["ternary_moe"]
+    routes = synth.gen_routes(wl, T)
+    used = sorted(set(routes.reshape(-1).tolist()))
+    mats = {e: synth.gen_expert(wl, e, which) for e in used}
+    filler = mats[used[0]]
+    stack = np.concatenate([mats.get(e, filler) for e in range(wl.experts)])
+    dw = mbd.to_device(mbd.mbd_pack(mbd.MBD_TERNARY_B128, stack), dev, n_mats=wl.experts)
+    return wl, routes, mats, dw
+
+
+@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_moe_full(dev, T, which):
+    mbd = _mbd()
+    print("case moe", T, which, flush=True)
+    wl, routes, mats, dw = _moe_setup(dev, T, which)
+    K = dw.K
+    if which == "up":
+        xb = synth.gen_x(wl, T, K)
+        per_pair = False
+    else:
+        xb = synth.gen_down_inputs(wl, T).reshape(T * wl.topk, K)
+        per_pair = True
+    ws = torch.empty(mbd.mbd_moe_workspace_bytes(wl.experts, T, wl.topk), dtype=torch.uint8, device=dev)
+    y = torch.full((T, wl.topk, dw.M), float("nan"), dtype=torch.float32, device=dev)
+    r = torch.from_numpy(routes).to(dev)
+    mbd.mbd_moe_gemv(dw, r, _x_dev(xb, dev), per_pair, y, ws)
+    torch.cuda.synchronize()
+    deq = {}
+    for e, m in mats.items():
+        q, s = ternary.quantize(m)
+        deq[e] = ternary.dequant(q, s)
+    xv = bits.bf16_value(xb)
+    ref = np.zeros((T, wl.topk, dw.M))
+    for t in range(T):
+        for j in range(wl.topk):
+            ref[t, j] = deq[int(routes[t, j])] @ (xv[t * wl.topk + j] if per_pair else xv[t])
+    err = gemv.rel_l2(y.cpu().numpy(), ref)
+    print("moe T=%d %s rel_l2=%.3e" % (T, which, err), flush=True)
+    assert err <= TOL
+
+
+# ------------------------------------------------------------ Cassandra
+
+def _cas(dev, w, norms, only=None):
+    mbd = _mbd()
+    p = mbd.mbd_pack(mbd.MBD_CASSANDRA, w, norms)
+    return p, mbd.to_device(p, dev, only=only)
+
+
+CAS_SHAPES = [(1, 4096), (2, 1536), (5, 1000 - 1000 % 128 + 128), (3, 14336), (7, 8192), (33, 384)]
+
+
+@pytest.mark.parametrize("M,K", CAS_SHAPES)
+def test_cassandra_decode_ragged(dev, M, K):
+    mbd = _mbd()
+    print("case cassandra", M, K, flush=True)
+    rng = np.random.default_rng(M * K)
+    w = _rand_w(M + K, M, K)
+    norms = rng.lognormal(0, 1, K).astype(np.float32)
+    sec = cassandra.pack(w, norms)
+    _, cw = _cas(dev, w, norms)
+    out = torch.empty((M, K), dtype=torch.int16, device=dev)
+    mbd.mbd_verify_restore(cw, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), cassandra.restore(sec, M, K))
+    _, sw = _cas(dev, w, norms, only=mbd.SPEC_SECTIONS)
+    mbd.mbd_spec_decode(sw, out)
+    torch.cuda.synchronize()
+    spec = cassandra.spec_decode(sec, M, K)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), spec)
+    for B in (1, 3, 16):
+        x = _rand_x(B, B, K)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+        mbd.mbd_spec_gemv(sw, _x_dev(x, dev), y)
+        torch.cuda.synchronize()
+        ref = gemv.gemv(bits.bf16_value(spec), x)
+        assert gemv.rel_l2(y.cpu().numpy(), ref) <= TOL
+
+
+@pytest.fixture(scope="module")
+def spec_full():
+    wl = synth.WORKLOADS["cassandra_spec"]
+    w = synth.gen_weights(wl)
+    norms = synth.gen_act_norms(wl)
+    return wl, w, norms
+
+
+def test_cassandra_spec_full(dev, spec_full):
+    mbd = _mbd()
+    wl, w, norms = spec_full
+    M, K = w.shape
+    keep = cassandra.keep_mask(w, norms)
+    expect = np.where(keep, w & 0xFFF0, 0).astype(np.uint16)
+    _, sw = _cas(dev, w, norms, only=mbd.SPEC_SECTIONS)
+    out = torch.empty((M, K), dtype=torch.int16, device=dev)
+    mbd.mbd_spec_decode(sw, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), expect)
+    x = synth.gen_x(wl, 1)
+    y = torch.empty((1, M), dtype=torch.float32, device=dev)
+    mbd.mbd_spec_gemv(sw, _x_dev(x, dev), y)
+    torch.cuda.synchronize()
+    err = gemv.rel_l2(y.cpu().numpy(), gemv.gemv(bits.bf16_value(expect), x))
+    print("cassandra spec gemv rel_l2=%.3e" % err, flush=True)
+    assert err <= TOL
+
+
+@pytest.fixture(scope="module")
+def verify_full():
+    wl = synth.WORKLOADS["cassandra_verify"]
+    w = synth.gen_weights(wl)
+    norms = synth.gen_act_norms(wl)
+    x = synth.gen_x(wl, 16)
+    return wl, w, norms, x
+
+
+def test_cassandra_verify_full(dev, verify_full):
+    mbd = _mbd()
+    wl, w, norms, x = verify_full
+    M, K = w.shape
+    _, cw = _cas(dev, w, norms)
+    out = torch.empty((M, K), dtype=torch.int16, device=dev)
+    mbd.mbd_verify_restore(cw, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w)       # spec + verification = original
+    del out
+    y = torch.empty((16, M), dtype=torch.float32, device=dev)
+    mbd.mbd_gemv(cw, _x_dev(x, dev), y)
+    torch.cuda.synchronize()
+    ref = gemv.gemv(bits.bf16_value(w), x)
+    err = gemv.rel_l2(y.cpu().numpy(), ref)
+    print("cassandra verify gemm rel_l2=%.3e" % err, flush=True)
+    assert err <= TOL
+
+
+def test_mx_full(dev, verify_full):
+    mbd = _mbd()
+    wl, w, norms, x = verify_full
+    M, K = w.shape
+    dw = mbd.to_device(mbd.mbd_pack(mbd.MBD_MX32, w), dev)
+    y = torch.empty((16, M), dtype=torch.float32, device=dev)
+    mbd.mbd_gemv(dw, _x_dev(x, dev), y)
+    torch.cuda.synchronize()
+    sec = mx.encode(w)
+    ref = gemv.gemv(mx.value(sec, M, K), x)
+    err = gemv.rel_l2(y.cpu().numpy(), ref)
+    print("mx gemm rel_l2=%.3e" % err, flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M,K,B", [(16, 32, 1), (33, 96, 5), (40, 4096, 16)])
+def test_mx_ragged_and_dequant(dev, M, K, B):
+    mbd = _mbd()
+    w = _rand_w(M + K, M, K)
+    w[0, :32] = 0
+    dw = mbd.to_device(mbd.mbd_pack(mbd.MBD_MX32, w), dev)
+    sec = mx.encode(w)
+    out = torch.empty((M, K), dtype=torch.float32, device=dev)
+    mbd.mbd_dequant(dw, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), mx.value(sec, M, K))
+    x = _rand_x(B, B, K)
+    y = torch.empty((B, M), dtype=torch.float32, device=dev)
+    mbd.mbd_gemv(dw, _x_dev(x, dev), y)
+    torch.cuda.synchronize()
+    assert gemv.rel_l2(y.cpu().numpy(), gemv.gemv(mx.value(sec, M, K), x)) <= TOL
+
+
+def test_verify_gemm_needs_tile_aligned_k(dev):
+    mbd = _mbd()
+    w = _rand_w(3, 4, 1536)
+    _, cw = _cas(dev, w, np.ones(1536, np.float32))
+    x = _x_dev(_rand_x(3, 2, 1536), dev)
+    y = torch.empty((2, 4), dtype=torch.float32, device=dev)
+    with pytest.raises(mbd.MbdError) as e:
+        mbd.mbd_gemv(cw, x, y)
+    assert e.value.status == mbd.MBD_ESHAPE
