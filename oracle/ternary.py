@@ -9,6 +9,7 @@ gets scale 1 and is flagged all-zero.
 Readings where the page is silent (each listed in the design notes):
 * W is [M][K] row-major (row = output channel), blocks are 128 consecutive k of
   one row (the page's reshape(-1, 128) on a row-major weight).
+* The mean is the fp64 sum of |w| taken in index order, divided by 128.
 * The page adds eps = 1e-8 to the scale only to avoid dividing by zero; the
   all-zero rule covers that case, so eps is dropped.  The scale is stored as
   fp16 (round to nearest even from the exact fp64 mean) and the codes are taken
@@ -35,7 +36,10 @@ def quantize(w_bits: np.ndarray):
     if K % BLOCK:
         raise ValueError("K must be a multiple of 128")
     w = bf16_value(w_bits).reshape(M, K // BLOCK, BLOCK)
-    mean = np.abs(w).sum(axis=-1) / BLOCK             # fp64; /128 is exact
+    total = np.zeros((M, K // BLOCK))
+    for i in range(BLOCK):                            # fp64, in index order
+        total += np.abs(w[..., i])
+    mean = total / BLOCK                              # /128 is exact
     s_bits = fp16_rne(mean)
     if np.any((s_bits & 0x7FFF) == 0x7C00):
         raise ValueError("ternary scale overflows fp16")
