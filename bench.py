@@ -319,9 +319,9 @@ def cpu_baseline(wl, budget_s=15.0):
                       % (calls, wl.name, elapsed, blas)}, ref
 
 
-def measure(name, dev, steps, warmup, with_cpu):
+def measure(name, dev, steps, warmup, with_cpu, use_graph=True):
     wl = make_workload(name, dev)
-    sec, ms = time_workload(wl, steps, warmup)
+    sec, ms = time_workload(wl, steps, warmup, use_graph)
     bps = wl.bytes_per_step()
     gbs = bps * steps / sec / 1e9
     traffic = traffic_from_profiles(wl)
@@ -353,6 +353,7 @@ def main():
     ap.add_argument("--workload", default="int4_8k")
     ap.add_argument("--all", default=None, help="append one JSON line per workload to this file")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of one HIP graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the hot path is a single-GPU kernel and "
@@ -368,11 +369,11 @@ def main():
             if name == args.workload:
                 continue
             print("measuring", name, file=sys.stderr, flush=True)
-            r = measure(name, dev, args.steps, args.warmup, with_cpu=False)
+            r = measure(name, dev, args.steps, args.warmup, with_cpu=False, use_graph=not args.no_graph)
             with open(args.all, "a") as f:
                 f.write(json.dumps(r) + "\n")
             torch.cuda.empty_cache()
-    res = measure(args.workload, dev, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    res = measure(args.workload, dev, args.steps, args.warmup, with_cpu=not args.no_cpu, use_graph=not args.no_graph)
     if args.all:
         with open(args.all, "a") as f:
             f.write(json.dumps(res) + "\n")

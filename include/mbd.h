@@ -61,13 +61,19 @@ typedef enum {
 /* ------------------------------------------------------------------ packing
  * Offline, CPU only.  Section layouts (all little-endian, rows contiguous):
  *
- * MBD_TERNARY_B128  (sec 0) "codes"  uint32 [M][K/16]: code q+1 of element k at
- *                                    bits 2*(k%16) of word k/16 (3 never written)
+ * MBD_TERNARY_B128  (sec 0) "codes"  uint32 [M][K/16]: word w holds elements
+ *                                    16w..16w+15, the even ones in the low half and
+ *                                    the odd ones in the high half: code q+1 of
+ *                                    element 16w+t at bit 2*(t/2) (+16 if t is odd);
+ *                                    code 3 is never written
  *                   (sec 1) "scales" fp16 [M][K/128]: fp16(mean|w| of the block),
  *                                    round to nearest even; 1.0 for an all-zero
  *                                    block (whose codes are all q = 0).
  *                   q = clamp(round_half_even(w / scale), -1, 1).
- * MBD_INT4_G128     (sec 0) "codes"  uint32 [M][K/8]: code q+8 at bits 4*(k%8)
+ * MBD_INT4_G128     (sec 0) "codes"  uint32 [M][K/8]: word w holds elements
+ *                                    8w..8w+7, evens in the low half, odds in the high
+ *                                    half: code q+8 of element 8w+t at bit 4*(t/2)
+ *                                    (+16 if t is odd); code 0 is never written
  *                   (sec 1) "scales" fp16 [M][K/128]: fp16(max|w| / 7); 1.0 for
  *                                    an all-zero group.  q = clamp(rne(w/s), -7, 7).
  * MBD_CASSANDRA     Wanda keep count floor(K*keep_num/keep_den) per row, score

@@ -4,23 +4,29 @@
 //
 // Decode time is set by the weight bytes ([Bolt], background), so the kernel is
 // built around one coalesced 16-byte load per lane per "chunk" of packed codes
-// (64 ternary or 32 INT4 weights), decoded in registers with two-operation
-// shift/and-or sequences into bf16 pairs and consumed by v_dot2c_f32_bf16.
+// (64 ternary or 32 INT4 weights), decoded in registers into bf16 pairs and
+// consumed by v_dot2c_f32_bf16.
 //
-// Code -> bf16 trick: OR-ing a small field c into the mantissa of 0x4300 (128.0)
-// gives the exact bf16 value 128 + c * 2^p for a field at mantissa bit p.  A
-// dot2 against pre-arranged activation pairs therefore computes
-// sum (128 + c) x; the per-chunk constant sum_k base_k x_k ("bias", shared by
-// every row) is subtracted once per chunk and the group scale applied once per
-// chunk.  For ternary, fields sit at mantissa bits 0, 2 and 4, so the matching x
-// values are pre-scaled by 1, 1/4 and 1/16 when staged, which lets three fields
-// be extracted per shift.
+// Code -> bf16: OR-ing a small field c into the mantissa of 0x4300 (bf16 128.0)
+// gives the exact bf16 value 128 + c * 2^p for a field at mantissa bit p.  The
+// packed layout keeps the even elements of a word in its low half and the odd
+// ones in its high half, so one v_and_or_b32 (after a shift) yields the pair
+// (w[2t], w[2t+1]) that lines up with the natural activation pair
+// (x[2t], x[2t+1]).  A dot2 then accumulates sum (128 + c) x; the per-chunk
+// constant sum_k base_k x_k ("bias", shared by every row) is subtracted once
+// per chunk and the group scale applied once per chunk.  Ternary fields sit at
+// mantissa bits 0, 2 and 4 after a shift by 0, 6 or 12, giving three position
+// classes that are accumulated separately and combined with weights 1, 1/4,
+// 1/16, so three fields come out of every shift.
 //
 // Work split: lanes of a wave are grouped G to a row (G = largest power of two
-// <= 64 dividing the chunks per row), each lane walks its row's chunks with
-// stride G, and every wave covers RPW such row-steps so one x chunk held in
-// registers serves RPW rows.  The activations are staged once per workgroup in
-// LDS (pair-permuted, plus per-chunk bias), in K slabs when they do not fit.
+// <= 64 dividing the chunks per row); each lane walks its row's chunks with
+// stride G and every wave covers RPW such row-steps.  A ring of PF chunks of
+// 16-byte code loads stays in flight per lane.  The activations are staged once
+// per workgroup in LDS (raw bf16, quad-interleaved so that neighbouring lanes
+// read neighbouring 16-byte words, plus the per-chunk bias), in K slabs when
+// they do not fit.  The workgroup barrier waits on LDS traffic only: a plain
+// __syncthreads() would also drain every weight load in flight.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -40,111 +46,150 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// Round-to-nearest-even f32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return __half2float(__ushort_as_half(h));
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only (not for
+// vector-memory loads still in flight, unlike __syncthreads()).
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool TER>
 struct Fmt {
     static constexpr int WPC = TER ? 64 : 32;     // weights per 16-byte chunk
-    static constexpr int XW = WPC / 2;            // bf16 pair words per chunk
-    static constexpr int XQ = XW / 4;             // uint4 per chunk of x pairs
+    static constexpr int XQ = WPC / 8;            // 16-byte words of activations per chunk
     static constexpr int CPG = 128 / WPC;         // chunks per scale group
 };
 
-// Stage the activations of one chunk: pair-permuted (and, for ternary, scaled
-// by 1, 1/4, 1/16 per mantissa position class) plus its bias.
+// Stage the activations of one chunk: stage_load issues the 16-byte loads (ahead
+// of the weight stream: vector-memory counters retire in issue order),
+// stage_store writes them to LDS and the chunk's bias.
 template <bool TER>
-__device__ __forceinline__ void stage_chunk(const uint16_t* __restrict__ xs, uint4* __restrict__ dst,
-                                            int stride_q, float* __restrict__ bias) {
-    using F = Fmt<TER>;
+__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ xs, uint4 (&raw)[Fmt<TER>::XQ]) {
     const uint4* src = reinterpret_cast<const uint4*>(xs);
-    float b = 0.f;
-    if constexpr (TER) {
-        // word i covers k = 16i .. 16i+15: pair p = (x[16i+p], x[16i+p+8]), p = 0..7
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 lo = src[2 * i], hi = src[2 * i + 1];
-            uint32_t xl[4] = {lo.x, lo.y, lo.z, lo.w}, xh[4] = {hi.x, hi.y, hi.z, hi.w};
-            uint32_t pw[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                uint32_t a = (xl[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
-                uint32_t c = (xh[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
-                float fa = bf16_to_f32(a), fc = bf16_to_f32(c);
-                const int cls = p % 3;                      // 0: x1, 1: x1/4, 2: x1/16
-                const float sc = cls == 0 ? 1.f : (cls == 1 ? 0.25f : 0.0625f);
-                const float base = cls == 0 ? 129.f : (cls == 1 ? 33.f : 9.f);
-                b += base * (fa + fc);
-                pw[p] = f32_to_bf16(fa * sc) | (f32_to_bf16(fc * sc) << 16);
-            }
-            dst[(2 * i) * stride_q] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-            dst[(2 * i + 1) * stride_q] = make_uint4(pw[4], pw[5], pw[6], pw[7]);
-        }
-    } else {
-        // word i covers k = 8i .. 8i+7: pair p = (x[8i+p], x[8i+p+4]), p = 0..3
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 v = src[i];
-            uint32_t xv[4] = {v.x, v.y, v.z, v.w};
-            uint32_t pw[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t a = (xv[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
-                uint32_t c = (xv[2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
-                b += bf16_to_f32(a) + bf16_to_f32(c);
-                pw[p] = a | (c << 16);
-            }
-            dst[i * stride_q] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-        }
-        b *= 136.f;
-    }
-    (void)F::XW;
-    *bias = b;
+    for (int i = 0; i < Fmt<TER>::XQ; ++i) raw[i] = src[i];
 }
 
-// Unpack one 16-byte chunk of codes into bf16 pair words (128 + c * 2^p).
 template <bool TER>
-__device__ __forceinline__ void unpack_chunk(const uint4 w, uint32_t (&p)[Fmt<TER>::XW]) {
+__device__ __forceinline__ void stage_store(const uint4 (&raw)[Fmt<TER>::XQ], uint4* __restrict__ dst,
+                                            int stride_q, float* __restrict__ bias) {
+    float b = 0.f;
+#pragma unroll
+    for (int q = 0; q < Fmt<TER>::XQ; ++q) {
+        dst[q * stride_q] = raw[q];
+        const uint32_t v[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float pair = bf16_to_f32(v[j] & 0xFFFFu) + bf16_to_f32(v[j] >> 16);
+            if constexpr (TER) {
+                // pair p = 4 * (q & 1) + j of the 16-element word q >> 1: class p % 3
+                const int cls = (4 * (q & 1) + j) % 3;
+                b += (cls == 0 ? 129.f : (cls == 1 ? 33.f : 9.f)) * pair;
+            } else {
+                b += pair;
+            }
+        }
+    }
+    *bias = TER ? b : 136.f * b;
+}
+
+// (a & m) | o in one VALU op.  gfx9 VOP3 encodings cannot take a literal, so
+// left to itself the compiler splits this into v_and + v_or with literals; the
+// masks are kept in VGPRs instead (loaded once per kernel).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+    return r;
+}
+
+// Masks used by the unpackers, held in registers.
+struct UnpackConsts {
+    uint32_t magic, m2a, m2b, m2c, m4;
+    __device__ __forceinline__ void init() {
+        magic = 0x43004300u;   // bf16 128.0 in both halves
+        m2a = 0x00030003u; m2b = 0x000C000Cu; m2c = 0x00300030u;
+        m4 = 0x000F000Fu;
+        // an opaque copy keeps them in VGPRs instead of being folded back into literals
+        asm volatile("" : "+v"(magic), "+v"(m2a), "+v"(m2b), "+v"(m2c), "+v"(m4));
+    }
+};
+
+// One 32-bit word of codes -> bf16 pairs.  INT4: pair j = (w[2j], w[2j+1]).
+// Ternary: pair p = (w[2p], w[2p+1]) scaled by 1, 4 or 16 for p % 3 = 0, 1, 2.
+template <bool TER>
+__device__ __forceinline__ void unpack_word(const uint32_t v, uint32_t (&p)[TER ? 8 : 4], const UnpackConsts& k) {
+    if constexpr (TER) {
+        const uint32_t s6 = v >> 6, s12 = v >> 12;
+        p[0] = and_or(v, k.m2a, k.magic);
+        p[1] = and_or(v, k.m2b, k.magic);
+        p[2] = and_or(v, k.m2c, k.magic);
+        p[3] = and_or(s6, k.m2a, k.magic);
+        p[4] = and_or(s6, k.m2b, k.magic);
+        p[5] = and_or(s6, k.m2c, k.magic);
+        p[6] = and_or(s12, k.m2a, k.magic);
+        p[7] = and_or(s12, k.m2b, k.magic);
+    } else {
+        p[0] = and_or(v, k.m4, k.magic);
+        p[1] = and_or(v >> 4, k.m4, k.magic);
+        p[2] = and_or(v >> 8, k.m4, k.magic);
+        p[3] = and_or(v >> 12, k.m4, k.magic);
+    }
+}
+
+// Dot of one word's pairs with the matching activations (INT4: 4 pairs from one
+// 16-byte word; ternary: 8 pairs from two), into class accumulators.
+struct Acc3 {
+    float a, b, c, d;   // INT4: a, b chains; ternary: a/d class 1, b class 4, c class 16
+};
+
+template <bool TER>
+__device__ __forceinline__ void dot_word(const uint32_t (&pw)[TER ? 8 : 4], uint4 x0, uint4 x1, Acc3& t) {
+    if constexpr (TER) {
+        t.a = dot2(pw[0], x0.x, t.a);
+        t.b = dot2(pw[1], x0.y, t.b);
+        t.c = dot2(pw[2], x0.z, t.c);
+        t.d = dot2(pw[3], x0.w, t.d);
+        t.b = dot2(pw[4], x1.x, t.b);
+        t.c = dot2(pw[5], x1.y, t.c);
+        t.a = dot2(pw[6], x1.z, t.a);
+        t.b = dot2(pw[7], x1.w, t.b);
+    } else {
+        (void)x1;
+        t.a = dot2(pw[0], x0.x, t.a);
+        t.b = dot2(pw[1], x0.y, t.b);
+        t.a = dot2(pw[2], x0.z, t.a);
+        t.b = dot2(pw[3], x0.w, t.b);
+    }
+}
+
+template <bool TER>
+__device__ __forceinline__ float finish(const Acc3& t) {
+    if constexpr (TER) return (t.a + t.d) + 0.25f * t.b + 0.0625f * t.c;
+    else return t.a + t.b;
+}
+
+// Full chunk (4 code words) against the staged activations of one batch row:
+// xq points at quad 0 of the chunk, successive quads are `sq` uint4 apart.
+template <bool TER>
+__device__ __forceinline__ float chunk_dot(const uint4 w, const uint4* __restrict__ xq, int sq, float bias,
+                                           const UnpackConsts& k) {
     const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    constexpr uint32_t MAGIC = 0x43004300u;
+    Acc3 t{-bias, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t v = wv[i];
-        if constexpr (TER) {
-            const uint32_t s6 = v >> 6, s12 = v >> 12;
-            p[8 * i + 0] = (v & 0x00030003u) | MAGIC;
-            p[8 * i + 1] = (v & 0x000C000Cu) | MAGIC;
-            p[8 * i + 2] = (v & 0x00300030u) | MAGIC;
-            p[8 * i + 3] = (s6 & 0x00030003u) | MAGIC;
-            p[8 * i + 4] = (s6 & 0x000C000Cu) | MAGIC;
-            p[8 * i + 5] = (s6 & 0x00300030u) | MAGIC;
-            p[8 * i + 6] = (s12 & 0x00030003u) | MAGIC;
-            p[8 * i + 7] = (s12 & 0x000C000Cu) | MAGIC;
-        } else {
-            p[4 * i + 0] = (v & 0x000F000Fu) | MAGIC;
-            p[4 * i + 1] = ((v >> 4) & 0x000F000Fu) | MAGIC;
-            p[4 * i + 2] = ((v >> 8) & 0x000F000Fu) | MAGIC;
-            p[4 * i + 3] = ((v >> 12) & 0x000F000Fu) | MAGIC;
-        }
+        uint32_t pw[TER ? 8 : 4];
+        const uint4 x0 = xq[(TER ? 2 * i : i) * sq];
+        const uint4 x1 = TER ? xq[(2 * i + 1) * sq] : x0;
+        unpack_word<TER>(wv[i], pw, k);
+        dot_word<TER>(pw, x0, x1, t);
+#if MBD_WORD_FENCE
+        __builtin_amdgcn_sched_barrier(0);   // keep one word's pairs live at a time
+#endif
     }
-}
-
-template <int N>
-__device__ __forceinline__ float dot_pairs(const uint32_t (&p)[N], const uint32_t (&x)[N]) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < N; i += 2) {
-        a0 = dot2(p[i], x[i], a0);
-        a1 = dot2(p[i + 1], x[i + 1], a1);
-    }
-    return a0 + a1;
+    return finish<TER>(t);
 }
 
 struct BqArgs {
@@ -161,105 +206,178 @@ struct BqArgs {
     int topk, x_per_pair, row_blocks;
 };
 
+// Load-ring depth and rows per wave-step for each batch bucket.
+#ifndef MBD_WORD_FENCE
+#define MBD_WORD_FENCE 1
+#endif
+#ifndef MBD_CODES_NT
+#define MBD_CODES_NT 1     // stream the packed codes with non-temporal loads
+#endif
+#ifndef MBD_B1_RPW
+#define MBD_B1_RPW 1
+#endif
+#ifndef MBD_B1_PF
+#define MBD_B1_PF 2
+#endif
+#ifndef MBD_MAX_WAVES
+#define MBD_MAX_WAVES 16      // waves per workgroup (upper bound) for batch 1
+#endif
+#ifndef MBD_WPE
+#define MBD_WPE 4             // INT4 batch-1 target waves per SIMD (caps VGPRs at 512 / MBD_WPE)
+#endif
+#ifndef MBD_TWPE
+#define MBD_TWPE 4            // ternary batch-1 target waves per SIMD
+#endif
+#ifndef MBD_T1_RPW
+#define MBD_T1_RPW 1
+#endif
+#ifndef MBD_T1_PF
+#define MBD_T1_PF 2
+#endif
+template <bool TER, int BMAX> struct Shape;
+template <> struct Shape<false, 1> { static constexpr int RPW = MBD_B1_RPW, PF = MBD_B1_PF; };
+template <> struct Shape<true, 1> { static constexpr int RPW = MBD_T1_RPW, PF = MBD_T1_PF; };
+template <bool TER> struct Shape<TER, 2> { static constexpr int RPW = 2, PF = 2; };
+template <bool TER> struct Shape<TER, 4> { static constexpr int RPW = 2, PF = 2; };
+template <bool TER> struct Shape<TER, 8> { static constexpr int RPW = 2, PF = 2; };
+template <bool TER> struct Shape<TER, 16> { static constexpr int RPW = 2, PF = 1; };
+
 // Core: rows [row_base, row_base + rows_per_block) of one matrix, nb <= BMAX batch
 // rows whose activations / outputs are given by xrow(b) / yrow(b).
-template <bool TER, int BMAX, int RPW, class XRow, class YRow>
+template <bool TER, int BMAX, bool ONE_SLAB, class XRow, class YRow>
 __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int row_base, int nb,
                                         XRow xrow, YRow yrow) {
     using F = Fmt<TER>;
+    constexpr int RPW = Shape<TER, BMAX>::RPW, PF = Shape<TER, BMAX>::PF;
     extern __shared__ uint4 lds4[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = a.G, RS = 64 / G, C = a.C, K = a.K, M = a.M;
+    const int G = a.G, RS = 64 / G, C = a.C, K = a.K, M = a.M, SC = a.SC;
     const int sub = lane & (G - 1), rg = lane / G;
     const int row0 = row_base + wave * (RS * RPW) + rg;
     const int ngroups = K / 128;
+    const int nj = C / G;                // chunks per lane per row
+    const int SJ = SC / G;               // chunks per lane per LDS slab (multiple of PF unless one slab)
     uint4* xl = lds4;                                        // [BMAX][XQ][SC]
-    float* bl = reinterpret_cast<float*>(lds4 + BMAX * F::XQ * a.SC);   // [BMAX][SC]
+    float* bl = reinterpret_cast<float*>(lds4 + BMAX * F::XQ * SC);   // [BMAX][SC]
 
-    int rows[RPW];
+    const u32x4_t* rowp[RPW];
+    const uint16_t* srow[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) rows[r] = min(row0 + r * RS, M - 1);
+    for (int r = 0; r < RPW; ++r) {
+        const int row = min(row0 + r * RS, M - 1);
+        rowp[r] = reinterpret_cast<const u32x4_t*>(codes) + (size_t)row * C + sub;
+        srow[r] = scales + (size_t)row * ngroups;
+    }
 
     float acc[RPW][BMAX];
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) acc[r][b] = 0.f;
+    UnpackConsts kc;
+    kc.init();
 
-    // first chunk's codes are requested before the activations are staged
-    uint4 wc[RPW];
-    float sc[RPW];
-    auto load = [&](int c, uint4 (&w)[RPW], float (&s)[RPW]) {
+    uint4 w[PF][RPW];
+    uint32_t s[PF][RPW];     // raw fp16 scale bits: converting at issue time would make the
+                             // compiler wait for the load (and, in order, every load before it)
+    // Slots past the row's last chunk load a hot, in-bounds dummy (the first
+    // activation row) instead of branching: every issue is unconditional, so the
+    // count of loads in flight is static and the waits stay exact.
+    const u32x4_t* xdummy = reinterpret_cast<const u32x4_t*>(xrow(0)) + (lane & 15);
+    auto issue = [&](int j, int p) {
+        const bool real = j < nj;
+        const int c = sub + G * j;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(codes) + (size_t)rows[r] * C + c);
-            w[r] = make_uint4(v.x, v.y, v.z, v.w);
-            s[r] = half_bits_to_f32(scales[(size_t)rows[r] * ngroups + c / F::CPG]);
+            const u32x4_t* pc = real ? rowp[r] + G * j : xdummy;
+            const uint16_t* ps = real ? srow[r] + c / F::CPG : srow[r];
+#if MBD_CODES_NT
+            const u32x4_t v = __builtin_nontemporal_load(pc);
+#else
+            const u32x4_t v = *pc;
+#endif
+            w[p][r] = make_uint4(v.x, v.y, v.z, v.w);
+            s[p][r] = *ps;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // each slot's code + scale loads stay adjacent, in slot order
+    };
+
+    // Activation loads first, then the first PF chunks of codes, so that waiting
+    // for the activations does not wait for the weight stream.
+    const int scn0 = min(SC, C);
+    const bool one_pass = nb * scn0 <= (int)blockDim.x;
+    const int myjob = threadIdx.x;
+
+    auto compute = [&](int p, int cc) {
+        if constexpr (BMAX == 1) {
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+                acc[r][0] = fmaf(half_bits_to_f32(uint16_t(s[p][r])), chunk_dot<TER>(w[p][r], xl + cc, SC, bl[cc], kc),
+                                 acc[r][0]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b)
+                    if (b < nb)
+                        acc[r][b] = fmaf(half_bits_to_f32(uint16_t(s[p][r])),
+                                         chunk_dot<TER>(w[p][r], xl + (size_t)b * F::XQ * SC + cc, SC, bl[b * SC + cc], kc),
+                                         acc[r][b]);
+            }
         }
     };
-    load(sub, wc, sc);
 
-    for (int c0 = 0; c0 < C; c0 += a.SC) {
-        const int scn = min(a.SC, C - c0);
-        for (int job = threadIdx.x; job < nb * scn; job += blockDim.x) {
-            const int b = job / scn, cc = job - b * scn;
-            stage_chunk<TER>(xrow(b) + (size_t)(c0 + cc) * F::WPC, xl + (size_t)b * F::XQ * a.SC + cc,
-                             a.SC, bl + b * a.SC + cc);
+    if constexpr (ONE_SLAB) {
+        // every staging job fits in one pass (the launcher guarantees it)
+        uint4 xraw[F::XQ];
+        {
+            // threads without a job load the first chunk again (unconditional issue)
+            const bool has = myjob < nb * C;
+            const int b = has ? myjob / C : 0, cc = has ? myjob - b * C : 0;
+            stage_load<TER>(xrow(b) + (size_t)cc * F::WPC, xraw);
         }
-        __syncthreads();
-        for (int cc = sub; cc < scn; cc += G) {
-            uint4 wn[RPW];
-            float sn[RPW];
-            const int cn = c0 + cc + G;
-            if (cn < C) load(cn, wn, sn);
-            if constexpr (BMAX <= 4) {
-                uint32_t xr[BMAX][F::XW];
-                float bias[BMAX];
 #pragma unroll
-                for (int b = 0; b < BMAX; ++b) {
-                    if (b < nb) {
+        for (int p = 0; p < PF; ++p) issue(p, p);
+        __builtin_amdgcn_sched_barrier(0);          // keep the weight loads ahead of the staging waits
+        if (myjob < nb * C) {
+            const int b = myjob / C, cc = myjob - b * C;
+            stage_store<TER>(xraw, xl + (size_t)b * F::XQ * SC + cc, SC, bl + b * SC + cc);
+        }
+        barrier_lds();
+        for (int j = 0; j < nj; j += PF) {
 #pragma unroll
-                        for (int q = 0; q < F::XQ; ++q) {
-                            uint4 v = xl[((size_t)b * F::XQ + q) * a.SC + cc];
-                            xr[b][4 * q] = v.x; xr[b][4 * q + 1] = v.y; xr[b][4 * q + 2] = v.z; xr[b][4 * q + 3] = v.w;
-                        }
-                        bias[b] = bl[b * a.SC + cc];
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    uint32_t p[F::XW];
-                    unpack_chunk<TER>(wc[r], p);
-#pragma unroll
-                    for (int b = 0; b < BMAX; ++b)
-                        if (b < nb) acc[r][b] = fmaf(sc[r], dot_pairs(p, xr[b]) - bias[b], acc[r][b]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    uint32_t p[F::XW];
-                    unpack_chunk<TER>(wc[r], p);
-#pragma unroll
-                    for (int b = 0; b < BMAX; ++b) {
-                        if (b < nb) {
-                            uint32_t xr[F::XW];
-#pragma unroll
-                            for (int q = 0; q < F::XQ; ++q) {
-                                uint4 v = xl[((size_t)b * F::XQ + q) * a.SC + cc];
-                                xr[4 * q] = v.x; xr[4 * q + 1] = v.y; xr[4 * q + 2] = v.z; xr[4 * q + 3] = v.w;
-                            }
-                            acc[r][b] = fmaf(sc[r], dot_pairs(p, xr) - bl[b * a.SC + cc], acc[r][b]);
-                        }
-                    }
-                }
-            }
-            if (cn < C) {
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) { wc[r] = wn[r]; sc[r] = sn[r]; }
+            for (int p = 0; p < PF; ++p) {
+                const int jj = j + p;
+                if (jj < nj) compute(p, sub + G * jj);
+                issue(jj + PF, p);
             }
         }
-        __syncthreads();
+    } else {
+        (void)one_pass;
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(p, p);
+        for (int js = 0; js < nj; js += SJ) {
+            const int c0 = js * G;
+            const int scn = min(SC, C - c0);
+            for (int job = threadIdx.x; job < nb * scn; job += blockDim.x) {
+                const int b = job / scn, cc = job - b * scn;
+                uint4 raw[F::XQ];
+                stage_load<TER>(xrow(b) + (size_t)(c0 + cc) * F::WPC, raw);
+                stage_store<TER>(raw, xl + (size_t)b * F::XQ * SC + cc, SC, bl + b * SC + cc);
+            }
+            barrier_lds();
+            const int je = min(nj, js + SJ);
+            for (int j = js; j < je; j += PF) {
+#pragma unroll
+                for (int p = 0; p < PF; ++p) {
+                    const int jj = j + p;
+                    if (jj < je) compute(p, sub + G * (jj - js));
+                    issue(jj + PF, p);
+                }
+            }
+            barrier_lds();
+        }
     }
 
     // reduce across the G lanes of each row group; lane sub == 0 stores
@@ -275,18 +393,20 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
     }
 }
 
-template <bool TER, int BMAX, int RPW>
-__global__ __launch_bounds__(256) void gemv_bq_kernel(BqArgs a) {
+template <bool TER, int BMAX, bool ONE_SLAB>
+__global__ __launch_bounds__(BMAX == 1 ? 64 * MBD_MAX_WAVES : 256)
+__attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8))) void gemv_bq_kernel(BqArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    bq_core<TER, BMAX, RPW>(
+    bq_core<TER, BMAX, ONE_SLAB>(
         a, a.codes, a.scales, blockIdx.x * a.rows_per_block, a.B,
         [=](int b) { return x + (size_t)b * K; }, [=](int b) { return y + (size_t)b * M; });
 }
 
-template <bool TER, int BMAX, int RPW>
-__global__ __launch_bounds__(256) void moe_bq_kernel(BqArgs a) {
+template <bool TER, int BMAX, bool ONE_SLAB>
+__global__ __launch_bounds__(BMAX == 1 ? 64 * MBD_MAX_WAVES : 256)
+__attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8))) void moe_bq_kernel(BqArgs a) {
     const int job = blockIdx.x / a.row_blocks, rb = blockIdx.x - job * a.row_blocks;
     if (job >= *a.n_jobs) return;
     const int4 jd = a.jobs[job];
@@ -296,7 +416,7 @@ __global__ __launch_bounds__(256) void moe_bq_kernel(BqArgs a) {
     float* y = a.y;
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)a.M * a.C, per_scales = (size_t)a.M * (a.K / 128);
-    bq_core<TER, BMAX, RPW>(
+    bq_core<TER, BMAX, ONE_SLAB>(
         a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * a.rows_per_block, nb,
         [=](int b) {
             const int p = pids[b];
@@ -311,7 +431,6 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int* __restrict__ 
                                                         int* __restrict__ counts, int* __restrict__ offsets,
                                                         int* __restrict__ pair_ids, int4* __restrict__ jobs,
                                                         int* __restrict__ n_jobs) {
-    __shared__ int s_tot[2];
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int c = 0;
         for (int p = 0; p < P; ++p) c += (route[p] == e);
@@ -325,7 +444,6 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int* __restrict__ 
             for (int s = 0; s < counts[e]; s += bmax) jobs[nj++] = make_int4(e, off + s, min(bmax, counts[e] - s), 0);
             off += counts[e];
         }
-        s_tot[0] = nj;
         *n_jobs = nj;
     }
     __syncthreads();
@@ -336,7 +454,8 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int* __restrict__ 
     }
 }
 
-// Dense dequant of ternary / INT4: one thread per 16-byte chunk.
+// Dense dequant of ternary / INT4: one thread per 16-byte chunk.  Element t of a
+// word sits at bit (bits * (t / 2)) + (t odd ? 16 : 0).
 template <bool TER>
 __global__ __launch_bounds__(256) void dequant_bq_kernel(const uint4* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales, float* __restrict__ out,
@@ -355,12 +474,14 @@ __global__ __launch_bounds__(256) void dequant_bq_kernel(const uint4* __restrict
     for (int wi = 0; wi < 4; ++wi) {
 #pragma unroll
         for (int j = 0; j < per; j += 4) {
-            float4 v;
-            v.x = s * (float)((int)((wv[wi] >> (bits * (j + 0))) & mask) - off);
-            v.y = s * (float)((int)((wv[wi] >> (bits * (j + 1))) & mask) - off);
-            v.z = s * (float)((int)((wv[wi] >> (bits * (j + 2))) & mask) - off);
-            v.w = s * (float)((int)((wv[wi] >> (bits * (j + 3))) & mask) - off);
-            o[(wi * per + j) / 4] = v;
+            float e[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = j + u;
+                const int sh = bits * (t >> 1) + ((t & 1) ? 16 : 0);
+                e[u] = s * (float)((int)((wv[wi] >> sh) & mask) - off);
+            }
+            o[(wi * per + j) / 4] = make_float4(e[0], e[1], e[2], e[3]);
         }
     }
 }
@@ -381,20 +502,30 @@ mbd_status hip_check(const char* what) {
     return MBD_OK;
 }
 
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+
 struct BqPlan {
-    int C, G, RS, RPW, nw, rows_per_block, SC, blocks;
+    int C, G, RS, RPW, PF, nw, rows_per_block, SC, blocks;
     size_t lds;
+    bool one_slab;   // all activations staged at once, one staging job per thread at most
 };
 
 BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks) {
     BqPlan p{};
-    const int wpc = ter ? 64 : 32, xq = ter ? 8 : 4;
+    const int wpc = ter ? 64 : 32, xq = ter ? 8 : 4;   // uint4 of activations per chunk
     p.C = int(K / wpc);
     p.G = 64;
     while (p.C % p.G) p.G >>= 1;
     p.RS = 64 / p.G;
-    p.RPW = bmax <= 4 ? 4 : 2;
-    p.nw = 4;
+    switch (bmax) {
+        case 1: p.RPW = ter ? Shape<true, 1>::RPW : Shape<false, 1>::RPW;
+                p.PF = ter ? Shape<true, 1>::PF : Shape<false, 1>::PF; break;
+        case 2: p.RPW = Shape<false, 2>::RPW; p.PF = Shape<false, 2>::PF; break;
+        case 4: p.RPW = Shape<false, 4>::RPW; p.PF = Shape<false, 4>::PF; break;
+        case 8: p.RPW = Shape<false, 8>::RPW; p.PF = Shape<false, 8>::PF; break;
+        default: p.RPW = Shape<false, 16>::RPW; p.PF = Shape<false, 16>::PF; break;
+    }
+    p.nw = bmax == 1 ? MBD_MAX_WAVES : 4;
     auto blocks_for = [&](int nw) {
         int rpb = nw * p.RS * p.RPW;
         return int((M + rpb - 1) / rpb);
@@ -404,21 +535,28 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks) {
     p.blocks = blocks_for(p.nw);
     const size_t per_chunk = size_t(bmax) * (xq * 16 + 4);
     int sc = int(std::min<size_t>(p.C, (64 * 1024) / per_chunk));
-    sc = std::max(p.G, (sc / p.G) * p.G);
+    if (sc < p.C) {
+        const int unit = p.G * p.PF;   // a partial slab must keep the load ring aligned
+        sc = std::max(unit, (sc / unit) * unit);
+    }
     p.SC = sc;
-    p.lds = size_t(bmax) * sc * (xq * 16 + 4);
+    p.lds = size_t(bmax) * sc * (xq * 16 + 4);   // <= 160 KiB: checked by the caller
+    p.one_slab = sc >= p.C && int64_t(bmax) * p.C <= int64_t(64) * p.nw;
     return p;
 }
 
 template <bool TER>
 mbd_status launch_gemv_bq(const BqPlan& pl, BqArgs a, int bmax, hipStream_t st) {
     dim3 grid(pl.blocks), block(64 * pl.nw);
-#define MBD_GEMV_CASE(BM, R)                                                                          \
-    if (bmax == BM && pl.RPW == R) {                                                                  \
-        hipLaunchKernelGGL((gemv_bq_kernel<TER, BM, R>), grid, block, pl.lds, st, a);                 \
+#define MBD_GEMV_CASE(BM)                                                                             \
+    if (bmax == BM) {                                                                                 \
+        if (pl.one_slab)                                                                              \
+            hipLaunchKernelGGL((gemv_bq_kernel<TER, BM, true>), grid, block, pl.lds, st, a);          \
+        else                                                                                          \
+            hipLaunchKernelGGL((gemv_bq_kernel<TER, BM, false>), grid, block, pl.lds, st, a);         \
         return hip_check("gemv launch");                                                              \
     }
-    MBD_GEMV_CASE(1, 4) MBD_GEMV_CASE(2, 4) MBD_GEMV_CASE(4, 4) MBD_GEMV_CASE(8, 2) MBD_GEMV_CASE(16, 2)
+    MBD_GEMV_CASE(1) MBD_GEMV_CASE(2) MBD_GEMV_CASE(4) MBD_GEMV_CASE(8) MBD_GEMV_CASE(16)
 #undef MBD_GEMV_CASE
     return fail(MBD_EINVAL, "no gemv variant for batch %d", bmax);
 }
@@ -426,12 +564,15 @@ mbd_status launch_gemv_bq(const BqPlan& pl, BqArgs a, int bmax, hipStream_t st) 
 template <bool TER>
 mbd_status launch_moe_bq(const BqPlan& pl, BqArgs a, int bmax, int grid_blocks, hipStream_t st) {
     dim3 grid(grid_blocks), block(64 * pl.nw);
-#define MBD_MOE_CASE(BM, R)                                                                           \
-    if (bmax == BM && pl.RPW == R) {                                                                  \
-        hipLaunchKernelGGL((moe_bq_kernel<TER, BM, R>), grid, block, pl.lds, st, a);                  \
+#define MBD_MOE_CASE(BM)                                                                              \
+    if (bmax == BM) {                                                                                 \
+        if (pl.one_slab)                                                                              \
+            hipLaunchKernelGGL((moe_bq_kernel<TER, BM, true>), grid, block, pl.lds, st, a);           \
+        else                                                                                          \
+            hipLaunchKernelGGL((moe_bq_kernel<TER, BM, false>), grid, block, pl.lds, st, a);          \
         return hip_check("moe gemv launch");                                                          \
     }
-    MBD_MOE_CASE(1, 4) MBD_MOE_CASE(2, 4) MBD_MOE_CASE(4, 4) MBD_MOE_CASE(8, 2) MBD_MOE_CASE(16, 2)
+    MBD_MOE_CASE(1) MBD_MOE_CASE(2) MBD_MOE_CASE(4) MBD_MOE_CASE(8) MBD_MOE_CASE(16)
 #undef MBD_MOE_CASE
     return fail(MBD_EINVAL, "no expert gemv variant for batch %d", bmax);
 }
@@ -468,6 +609,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     const bool ter = w->fmt == MBD_TERNARY_B128;
     const int bmax = round_batch(B);
     BqPlan pl = plan_bq(ter, w->M, w->K, bmax, 512);
+    if (pl.lds > kMaxLds) return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
     BqArgs a{};
     a.codes = static_cast<const uint4*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
@@ -548,6 +690,7 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     if ((s = hip_check("expert grouping launch")) != MBD_OK) return s;
     const bool ter = w->fmt == MBD_TERNARY_B128;
     BqPlan pl = plan_bq(ter, w->M, w->K, bmax, 64);
+    if (pl.lds > kMaxLds) return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
     BqArgs a{};
     a.codes = static_cast<const uint4*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);

@@ -130,6 +130,7 @@ mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary) {
                 uint32_t* dst = codes + (m * K + g * 128) / cpw;
                 for (int wd = 0; wd < 128 / cpw; ++wd) {
                     uint32_t word = 0;
+                    // element j of the word: evens in the low half, odds in the high half
                     for (int j = 0; j < cpw; ++j) {
                         int q = 0;
                         if (!zero) {
@@ -137,7 +138,7 @@ mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary) {
                             q = int(std::max<double>(-qmax, std::min<double>(qmax, r)));
                         }
                         zeros[m] += (q == 0);
-                        word |= uint32_t(q + off) << (bits * j);
+                        word |= uint32_t(q + off) << (bits * (j >> 1) + ((j & 1) ? 16 : 0));
                     }
                     dst[wd] = word;
                 }

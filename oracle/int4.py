@@ -15,8 +15,10 @@ Readings where the page is silent:
 * A group with max |w| = 0, or whose fp16 scale underflows to 0, gets s = 1.0 and
   q = 0; an fp16 overflow of the scale is an error.
 * Packing (parity unpinned by the pages, fixed here): code c = q + 8 in [1, 15]
-  (0 is never written); element k of a row sits at bits 4*(k % 8) of 32-bit word
-  k // 8; row words are contiguous.
+  (0 is never written); 32-bit word w of a row holds elements 8w .. 8w+7, the
+  even ones in the low half and the odd ones in the high half: element 8w + t
+  sits at bit 4*(t // 2) when t is even and at bit 16 + 4*(t // 2) when t is odd.
+  Row words are contiguous.
 """
 from __future__ import annotations
 
@@ -45,18 +47,21 @@ def quantize(w_bits: np.ndarray):
     return q.reshape(M, K).astype(np.int8), s_bits
 
 
+# bit position of element t (0..7) inside its word: evens low half, odds high half
+SHIFTS = np.array([4 * (t // 2) + (16 if t % 2 else 0) for t in range(8)], dtype=np.int64)
+
+
 def pack_codes(q: np.ndarray) -> np.ndarray:
-    """q int8 [M][K] in [-7, 7] -> uint32 [M][K/8], code q+8 at bits 4*(k%8)."""
+    """q int8 [M][K] in [-7, 7] -> uint32 [M][K/8], code q+8 at SHIFTS[k % 8]."""
     M, K = q.shape
     c = (q.astype(np.int64) + 8).reshape(M, K // 8, 8)
-    shifts = 4 * np.arange(8, dtype=np.int64)
-    return (c << shifts).sum(axis=-1).astype(np.uint32)
+    return (c << SHIFTS).sum(axis=-1).astype(np.uint32)
 
 
 def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
     """uint32 [M][K/8] -> q int8 [M][K]; raises on the unused code 0."""
     M = words.shape[0]
-    shifts = 4 * np.arange(8, dtype=np.uint32)
+    shifts = SHIFTS.astype(np.uint32)
     c = (words.astype(np.uint32)[..., None] >> shifts) & 15
     if np.any(c == 0):
         raise ValueError("invalid int4 code 0")

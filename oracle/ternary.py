@@ -18,8 +18,10 @@ Readings where the page is silent (each listed in the design notes):
 * A block whose mean is 0, or whose fp16 scale underflows to 0, gets s = 1.0
   and q = 0 (the all-zero rule).  A scale that overflows fp16 is an error.
 * Packing (parity unpinned by the pages, fixed here): code c = q + 1 in
-  {0, 1, 2}; element k of a row sits at bits 2*(k % 16) of 32-bit word k // 16;
-  the words of a row are contiguous, rows follow each other.
+  {0, 1, 2}; 32-bit word w of a row holds elements 16w .. 16w+15, the even ones
+  in the low half and the odd ones in the high half: element 16w + t sits at bit
+  2*(t // 2) when t is even and at bit 16 + 2*(t // 2) when t is odd.  The words
+  of a row are contiguous, rows follow each other.
 """
 from __future__ import annotations
 
@@ -51,18 +53,21 @@ def quantize(w_bits: np.ndarray):
     return q.reshape(M, K).astype(np.int8), s_bits
 
 
+# bit position of element t (0..15) inside its word: evens low half, odds high half
+SHIFTS = np.array([2 * (t // 2) + (16 if t % 2 else 0) for t in range(16)], dtype=np.int64)
+
+
 def pack_codes(q: np.ndarray) -> np.ndarray:
-    """q int8 [M][K] in {-1,0,1} -> uint32 [M][K/16], code q+1 at bits 2*(k%16)."""
+    """q int8 [M][K] in {-1,0,1} -> uint32 [M][K/16], code q+1 at SHIFTS[k % 16]."""
     M, K = q.shape
     c = (q.astype(np.int64) + 1).reshape(M, K // 16, 16)
-    shifts = 2 * np.arange(16, dtype=np.int64)
-    return (c << shifts).sum(axis=-1).astype(np.uint32)
+    return (c << SHIFTS).sum(axis=-1).astype(np.uint32)
 
 
 def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
     """uint32 [M][K/16] -> q int8 [M][K]; raises on the unused code 3."""
     M = words.shape[0]
-    shifts = 2 * np.arange(16, dtype=np.uint32)
+    shifts = SHIFTS.astype(np.uint32)
     c = (words.astype(np.uint32)[..., None] >> shifts) & 3
     if np.any(c == 3):
         raise ValueError("invalid ternary code 3")

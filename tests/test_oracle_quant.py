@@ -91,9 +91,14 @@ def test_ternary_pack_layout_and_sizes():
     q = np.random.default_rng(4).integers(-1, 2, (M, K)).astype(np.int8)
     words = ternary.pack_codes(q)
     assert words.shape == (M, K // 16) and words.nbytes == M * K // 4
-    # element k at bits 2*(k%16) of word k//16
-    for (m, k) in [(0, 0), (1, 17), (2, 255), (0, 100)]:
-        assert (int(words[m, k // 16]) >> (2 * (k % 16))) & 3 == q[m, k] + 1
+    # element 16w + t at bit 2*(t//2) (t even) or 16 + 2*(t//2) (t odd) of word w
+    for (m, k) in [(0, 0), (1, 17), (2, 255), (0, 100), (1, 6), (2, 9)]:
+        t = k % 16
+        bit = 2 * (t // 2) + (16 if t % 2 else 0)
+        assert (int(words[m, k // 16]) >> bit) & 3 == q[m, k] + 1
+    one = np.zeros((1, 128), np.int8)
+    one[0, 1] = 1                                      # element 1: code 2 at bit 16
+    assert ternary.pack_codes(one)[0, 0] == 0x55555555 + (1 << 16)
     np.testing.assert_array_equal(ternary.unpack_codes(words, K), q)
     with pytest.raises(ValueError):
         ternary.unpack_codes(np.full((1, 8), 0xFFFFFFFF, np.uint32), 128)
@@ -113,7 +118,7 @@ def test_int4_clamp_and_max_code():
     assert q.min() >= -7 and q.max() <= 7
     g = np.abs(q.reshape(64, -1, 128)).max(axis=-1)
     assert np.all(g == 7)
-    c = (int4.pack_codes(q)[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 15
+    c = (int4.pack_codes(q)[..., None] >> int4.SHIFTS.astype(np.uint32)) & 15
     assert c.min() >= 1
 
 
@@ -163,8 +168,13 @@ def test_int4_pack_layout_and_sizes():
     q = np.random.default_rng(6).integers(-7, 8, (M, K)).astype(np.int8)
     words = int4.pack_codes(q)
     assert words.nbytes == M * K // 2
-    for (m, k) in [(0, 0), (1, 9), (1, 383)]:
-        assert (int(words[m, k // 8]) >> (4 * (k % 8))) & 15 == q[m, k] + 8
+    for (m, k) in [(0, 0), (1, 9), (1, 383), (0, 2), (1, 7)]:
+        t = k % 8
+        bit = 4 * (t // 2) + (16 if t % 2 else 0)
+        assert (int(words[m, k // 8]) >> bit) & 15 == q[m, k] + 8
+    one = np.zeros((1, 128), np.int8)
+    one[0, 3] = 7                                      # element 3: code 15 at bit 20
+    assert int4.pack_codes(one)[0, 0] == 0x88888888 + (7 << 20)
     np.testing.assert_array_equal(int4.unpack_codes(words, K), q)
     scales = int4.quantize(_tiny(7, M, K))[1]
     assert scales.nbytes == 2 * M * K // 128
