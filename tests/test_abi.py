@@ -1,0 +1,148 @@
+"""The C ABI: libmbd loads, exports every function include/mbd.h declares, and
+rejects bad arguments with the documented status before touching a GPU (every
+call here fails validation on the host, so no device work is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+mbd = pytest.importorskip("memory_bound_decode_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return mbd.lib()
+    except ImportError as e:                         # pragma: no cover
+        pytest.skip(str(e))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mbd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mbd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    from memory_bound_decode_amd import _native
+    assert set(names) == set(_native.SIGNATURES)
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.mbd_status_str(s)
+    assert L.mbd_status_str(99) == b"unknown status"
+
+
+def _pack_raw(L, fmt, w, M, K, norm=None):
+    h = ctypes.c_void_p()
+    st = L.mbd_pack(fmt, None if w is None else w.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                    M, K, None if norm is None else norm.ctypes.data, None, ctypes.byref(h))
+    if h.value:
+        L.mbd_packed_free(h)
+    return st
+
+
+def test_pack_errors(L):
+    w = np.zeros((4, 128), np.uint16)
+    assert _pack_raw(L, mbd.MBD_INT4_G128, None, 4, 128) == mbd.MBD_EINVAL
+    assert _pack_raw(L, 99, w, 4, 128) == mbd.MBD_EINVAL
+    assert _pack_raw(L, mbd.MBD_INT4_G128, w, 4, 100) == mbd.MBD_ESHAPE
+    assert _pack_raw(L, mbd.MBD_INT4_G128, w, 0, 128) == mbd.MBD_ESHAPE
+    assert _pack_raw(L, mbd.MBD_MX32, np.zeros((2, 96), np.uint16), 2, 96) == mbd.MBD_OK
+    assert _pack_raw(L, mbd.MBD_CASSANDRA, w, 4, 128) == mbd.MBD_EINVAL        # no act_norm
+    bad = w.copy()
+    bad[1, 7] = 0x7F80                                                          # +Inf
+    assert _pack_raw(L, mbd.MBD_TERNARY_B128, bad, 4, 128) == mbd.MBD_ERANGE
+    assert _pack_raw(L, mbd.MBD_MX32, bad, 4, 128) == mbd.MBD_ERANGE
+    big = np.full((1, 128), 0x7F00, np.uint16)                                  # 2^127: scale overflows fp16
+    assert _pack_raw(L, mbd.MBD_INT4_G128, big, 1, 128) == mbd.MBD_ERANGE
+    nrm = np.ones(128, np.float32)
+    nrm[3] = np.nan
+    assert _pack_raw(L, mbd.MBD_CASSANDRA, w, 4, 128, nrm) == mbd.MBD_ERANGE
+    assert L.mbd_last_error()
+
+
+def test_validate_detects_corruption(L):
+    w = np.zeros((2, 256), np.uint16)
+    p = mbd.mbd_pack(mbd.MBD_TERNARY_B128, w)
+    p.validate()
+    secs = (mbd.MbdSection * 4)()
+    n = ctypes.c_int32()
+    assert L.mbd_packed_sections(p._h, secs, 4, ctypes.byref(n)) == mbd.MBD_OK
+    codes = (ctypes.c_uint32 * 1).from_address(secs[0].data)
+    codes[0] = 0xFFFFFFFF                                                       # code 3 is invalid
+    with pytest.raises(mbd.MbdError) as e:
+        p.validate()
+    assert e.value.status == mbd.MBD_EFORMAT
+
+    rng = np.random.default_rng(0)
+    wc = synth_w = (rng.standard_normal((2, 256)) * 0.02).astype(np.float32)
+    import synth
+    wc = synth.f32_to_bf16_bits(synth_w)
+    pc = mbd.mbd_pack(mbd.MBD_CASSANDRA, wc, np.ones(256, np.float32))
+    pc.validate()
+    secs = (mbd.MbdSection * 8)()
+    assert L.mbd_packed_sections(pc._h, secs, 8, ctypes.byref(n)) == mbd.MBD_OK
+    kp = (ctypes.c_uint32 * 2).from_address(secs[5].data)
+    kp[1] += 1                                                                  # kept prefix off by one
+    with pytest.raises(mbd.MbdError) as e:
+        pc.validate()
+    assert e.value.status == mbd.MBD_EFORMAT
+
+
+def _desc(fmt, M, K, n_sym=0, ptr=0x1000, n_mats=1):
+    d = mbd.MbdDWeights()
+    d.fmt, d.M, d.K, d.n_sym, d.n_mats = fmt, M, K, n_sym, n_mats
+    for i in range(mbd._native.MBD_MAX_SECTIONS):
+        d.sec[i] = ptr
+    return d
+
+
+P16 = ctypes.c_void_p(0x10000)     # fake, never dereferenced: validation fails first
+
+
+def test_gemv_argument_errors(L):
+    d = _desc(mbd.MBD_INT4_G128, 16, 256)
+    assert L.mbd_gemv(None, P16, 1, P16, None) == mbd.MBD_EINVAL
+    assert L.mbd_gemv(ctypes.byref(d), None, 1, P16, None) == mbd.MBD_EINVAL
+    assert L.mbd_gemv(ctypes.byref(d), P16, 0, P16, None) == mbd.MBD_ESHAPE
+    assert L.mbd_gemv(ctypes.byref(d), P16, 17, P16, None) == mbd.MBD_ESHAPE
+    assert L.mbd_gemv(ctypes.byref(d), ctypes.c_void_p(0x10008), 1, P16, None) == mbd.MBD_EALIGN
+    d.K = 200
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_ESHAPE
+    d.K = 256
+    d.fmt = 42
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EINVAL
+    d = _desc(mbd.MBD_INT4_G128, 16, 256, ptr=0x10004)
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EALIGN
+    d = _desc(mbd.MBD_MX32, 16, 48)
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_ESHAPE
+
+
+def test_cassandra_and_moe_argument_errors(L):
+    d = _desc(mbd.MBD_CASSANDRA, 16, 256, n_sym=0)
+    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL      # n_sym 0
+    d.n_sym = 12
+    d.sec[2] = None
+    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL
+    d.sec[2] = 0x10000
+    assert L.mbd_spec_gemv(ctypes.byref(d), P16, 20, P16, None) == mbd.MBD_ESHAPE
+    d.sec[7] = None                                                             # verification data missing
+    assert L.mbd_verify_restore(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL
+    d = _desc(mbd.MBD_CASSANDRA, 16, 1536, n_sym=12)
+    assert L.mbd_gemv(ctypes.byref(d), P16, 16, P16, None) == mbd.MBD_ESHAPE    # K % 4096 != 0
+    e = _desc(mbd.MBD_TERNARY_B128, 64, 256, n_mats=8)
+    need = ctypes.c_uint64()
+    assert L.mbd_moe_workspace_bytes(8, 2, 4, ctypes.byref(need)) == mbd.MBD_OK and need.value > 0
+    assert L.mbd_moe_workspace_bytes(0, 2, 4, ctypes.byref(need)) == mbd.MBD_ESHAPE
+    assert L.mbd_moe_gemv(ctypes.byref(e), P16, 2, 4, P16, 0, P16, P16, 1, None) == mbd.MBD_EINVAL  # ws too small
+    e.fmt = mbd.MBD_CASSANDRA
+    assert L.mbd_moe_gemv(ctypes.byref(e), P16, 2, 4, P16, 0, P16, P16, need.value, None) == mbd.MBD_EINVAL
