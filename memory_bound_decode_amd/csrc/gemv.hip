@@ -192,12 +192,29 @@ __device__ __forceinline__ float chunk_dot(const uint4 w, const uint4* __restric
     return finish<TER>(t);
 }
 
+// Chunk against activations held in registers (one x chunk reused across rows).
+template <bool TER>
+__device__ __forceinline__ float chunk_dot_xreg(const uint4 w, const uint4 (&xr)[Fmt<TER>::XQ], float bias,
+                                                const UnpackConsts& k) {
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    Acc3 t{-bias, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t pw[TER ? 8 : 4];
+        unpack_word<TER>(wv[i], pw, k);
+        dot_word<TER>(pw, xr[TER ? 2 * i : i], xr[TER ? 2 * i + 1 : i], t);
+    }
+    return finish<TER>(t);
+}
+
 struct BqArgs {
     const uint4* codes;      // [n_mats][M][C] chunks
     const uint16_t* scales;  // [n_mats][M][K/128]
     const uint16_t* x;       // bf16 activations
     float* y;                // fp32 outputs
     int M, K, C, G, SC, B;
+    int gshift;              // log2(G)
+    float inv_c;             // 1 / C (division-free staging job split)
     int rows_per_block;
     // expert (grouped) mode
     const int4* jobs;        // {expert, pair_start, n_pairs, 0}
@@ -205,6 +222,9 @@ struct BqArgs {
     const int* pair_ids;     // pairs sorted by expert: pair id = t*k + slot
     int topk, x_per_pair, row_blocks;
 };
+
+// Scale loads per thread in the one-slab path (rows_per_block * K/128 <= this * threads).
+constexpr int kScaleLoads = 4;
 
 // Load-ring depth and rows per wave-step for each batch bucket.
 #ifndef MBD_WORD_FENCE
@@ -220,7 +240,7 @@ struct BqArgs {
 #define MBD_B1_PF 2
 #endif
 #ifndef MBD_MAX_WAVES
-#define MBD_MAX_WAVES 16      // waves per workgroup (upper bound) for batch 1
+#define MBD_MAX_WAVES 8       // waves per workgroup (upper bound) for batch 1
 #endif
 #ifndef MBD_WPE
 #define MBD_WPE 4             // INT4 batch-1 target waves per SIMD (caps VGPRs at 512 / MBD_WPE)
@@ -237,8 +257,11 @@ struct BqArgs {
 template <bool TER, int BMAX> struct Shape;
 template <> struct Shape<false, 1> { static constexpr int RPW = MBD_B1_RPW, PF = MBD_B1_PF; };
 template <> struct Shape<true, 1> { static constexpr int RPW = MBD_T1_RPW, PF = MBD_T1_PF; };
+#ifndef MBD_B4_RPW
+#define MBD_B4_RPW 2
+#endif
 template <bool TER> struct Shape<TER, 2> { static constexpr int RPW = 2, PF = 2; };
-template <bool TER> struct Shape<TER, 4> { static constexpr int RPW = 2, PF = 2; };
+template <bool TER> struct Shape<TER, 4> { static constexpr int RPW = MBD_B4_RPW, PF = 2; };
 template <bool TER> struct Shape<TER, 8> { static constexpr int RPW = 2, PF = 2; };
 template <bool TER> struct Shape<TER, 16> { static constexpr int RPW = 2, PF = 1; };
 
@@ -252,14 +275,17 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
     constexpr int RPW = Shape<TER, BMAX>::RPW, PF = Shape<TER, BMAX>::PF;
     extern __shared__ uint4 lds4[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = a.G, RS = 64 / G, C = a.C, K = a.K, M = a.M, SC = a.SC;
-    const int sub = lane & (G - 1), rg = lane / G;
+    // G is a power of two: all per-lane index math is shifts and masks (integer
+    // division would sit in front of the first load of every wave)
+    const int G = a.G, gs = a.gshift, RS = 64 >> gs, C = a.C, K = a.K, M = a.M, SC = a.SC;
+    const int sub = lane & (G - 1), rg = lane >> gs;
     const int row0 = row_base + wave * (RS * RPW) + rg;
-    const int ngroups = K / 128;
-    const int nj = C / G;                // chunks per lane per row
-    const int SJ = SC / G;               // chunks per lane per LDS slab (multiple of PF unless one slab)
+    const int ngroups = K >> 7;
+    const int nj = C >> gs;              // chunks per lane per row
+    const int SJ = SC >> gs;             // chunks per lane per LDS slab (multiple of PF unless one slab)
     uint4* xl = lds4;                                        // [BMAX][XQ][SC]
     float* bl = reinterpret_cast<float*>(lds4 + BMAX * F::XQ * SC);   // [BMAX][SC]
+    uint16_t* sl = reinterpret_cast<uint16_t*>(bl + BMAX * SC);       // one-slab: [rows_per_block][ngroups]
 
     const u32x4_t* rowp[RPW];
     const uint16_t* srow[RPW];
@@ -291,16 +317,15 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             const u32x4_t* pc = real ? rowp[r] + G * j : xdummy;
-            const uint16_t* ps = real ? srow[r] + c / F::CPG : srow[r];
 #if MBD_CODES_NT
             const u32x4_t v = __builtin_nontemporal_load(pc);
 #else
             const u32x4_t v = *pc;
 #endif
             w[p][r] = make_uint4(v.x, v.y, v.z, v.w);
-            s[p][r] = *ps;
+            if constexpr (!ONE_SLAB) s[p][r] = real ? srow[r][c / F::CPG] : srow[r][0];
         }
-        __builtin_amdgcn_sched_barrier(0);   // each slot's code + scale loads stay adjacent, in slot order
+        __builtin_amdgcn_sched_barrier(0);   // each slot's loads stay adjacent, in slot order
     };
 
     // Activation loads first, then the first PF chunks of codes, so that waiting
@@ -309,40 +334,99 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
     const bool one_pass = nb * scn0 <= (int)blockDim.x;
     const int myjob = threadIdx.x;
 
+    const int rloc0 = row0 - row_base;   // this lane's first row inside the block
+    Acc3 part[BMAX == 1 ? 1 : RPW][BMAX];    // per-chunk partial dots (batch > 1)
+#pragma unroll
+    for (int r = 0; r < (BMAX == 1 ? 1 : RPW); ++r)
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) part[r][b] = Acc3{0.f, 0.f, 0.f, 0.f};
+    auto scale = [&](int p, int r, int cc) {
+        if constexpr (ONE_SLAB) return half_bits_to_f32(sl[(rloc0 + r * RS) * ngroups + (cc / F::CPG)]);
+        else return half_bits_to_f32(uint16_t(s[p][r]));
+    };
     auto compute = [&](int p, int cc) {
-        if constexpr (BMAX == 1) {
+        if constexpr (BMAX == 1 && RPW == 1) {
+            acc[0][0] = fmaf(scale(p, 0, cc), chunk_dot<TER>(w[p][0], xl + cc, SC, bl[cc], kc), acc[0][0]);
+        } else if constexpr (BMAX == 1) {
+            // one read of the chunk's activations from LDS serves all RPW rows
+            uint4 xr[F::XQ];
+#pragma unroll
+            for (int q = 0; q < F::XQ; ++q) xr[q] = xl[q * SC + cc];
+            const float bias = bl[cc];
 #pragma unroll
             for (int r = 0; r < RPW; ++r)
-                acc[r][0] = fmaf(half_bits_to_f32(uint16_t(s[p][r])), chunk_dot<TER>(w[p][r], xl + cc, SC, bl[cc], kc),
-                                 acc[r][0]);
+                acc[r][0] = fmaf(scale(p, r, cc), chunk_dot_xreg<TER>(w[p][r], xr, bias, kc), acc[r][0]);
         } else {
+            // unpack every row's chunk once; each batch row's activations are read
+            // from LDS once and reused across the RPW rows
+            uint32_t pr[RPW][TER ? 32 : 16];
+            float sc[RPW];
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
+                sc[r] = scale(p, r, cc);
+                const uint32_t wv[4] = {w[p][r].x, w[p][r].y, w[p][r].z, w[p][r].w};
 #pragma unroll
-                for (int b = 0; b < BMAX; ++b)
-                    if (b < nb)
-                        acc[r][b] = fmaf(half_bits_to_f32(uint16_t(s[p][r])),
-                                         chunk_dot<TER>(w[p][r], xl + (size_t)b * F::XQ * SC + cc, SC, bl[b * SC + cc], kc),
-                                         acc[r][b]);
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t pw[TER ? 8 : 4];
+                    unpack_word<TER>(wv[i], pw, kc);
+#pragma unroll
+                    for (int e = 0; e < (TER ? 8 : 4); ++e) pr[r][(TER ? 8 : 4) * i + e] = pw[e];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                if (b < nb) {
+                    const uint4* xq = xl + (size_t)b * F::XQ * SC + cc;
+                    const float bias = bl[b * SC + cc];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 x0 = xq[(TER ? 2 * i : i) * SC];
+                        const uint4 x1 = TER ? xq[(2 * i + 1) * SC] : x0;
+#pragma unroll
+                        for (int r = 0; r < RPW; ++r) {
+                            uint32_t pw[TER ? 8 : 4];
+#pragma unroll
+                            for (int e = 0; e < (TER ? 8 : 4); ++e) pw[e] = pr[r][(TER ? 8 : 4) * i + e];
+                            dot_word<TER>(pw, x0, x1, part[r][b]);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) {
+                        acc[r][b] = fmaf(sc[r], finish<TER>(part[r][b]) - bias, acc[r][b]);
+                        part[r][b] = Acc3{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
             }
         }
     };
 
     if constexpr (ONE_SLAB) {
         // every staging job fits in one pass (the launcher guarantees it)
+        // job -> (batch row, chunk) without integer division: (job + 1/2) / C is
+        // never within float rounding of an integer for C <= 2^12
+        const bool has = myjob < nb * C;
+        const int jb = BMAX == 1 ? 0 : int((float(myjob) + 0.5f) * a.inv_c);
+        const int jc = myjob - jb * C;
         uint4 xraw[F::XQ];
-        {
-            // threads without a job load the first chunk again (unconditional issue)
-            const bool has = myjob < nb * C;
-            const int b = has ? myjob / C : 0, cc = has ? myjob - b * C : 0;
-            stage_load<TER>(xrow(b) + (size_t)cc * F::WPC, xraw);
+        // threads without a job load the first chunk again (unconditional issue)
+        stage_load<TER>(xrow(has ? jb : 0) + (size_t)(has ? jc : 0) * F::WPC, xraw);
+        // the block's fp16 scales: rows_per_block * ngroups contiguous values
+        const int nsc = a.rows_per_block * ngroups;
+        const int sc_lim = (M - row_base) * ngroups;          // rows past M are not read
+        uint16_t sraw[kScaleLoads];
+#pragma unroll
+        for (int i = 0; i < kScaleLoads; ++i) {
+            const int e = myjob + i * (int)blockDim.x;
+            sraw[i] = scales[(size_t)row_base * ngroups + ((e < nsc && e < sc_lim) ? e : 0)];
         }
 #pragma unroll
         for (int p = 0; p < PF; ++p) issue(p, p);
         __builtin_amdgcn_sched_barrier(0);          // keep the weight loads ahead of the staging waits
-        if (myjob < nb * C) {
-            const int b = myjob / C, cc = myjob - b * C;
-            stage_store<TER>(xraw, xl + (size_t)b * F::XQ * SC + cc, SC, bl + b * SC + cc);
+        if (has) stage_store<TER>(xraw, xl + (size_t)jb * F::XQ * SC + jc, SC, bl + jb * SC + jc);
+#pragma unroll
+        for (int i = 0; i < kScaleLoads; ++i) {
+            const int e = myjob + i * (int)blockDim.x;
+            if (e < nsc) sl[e] = sraw[i];
         }
         barrier_lds();
         for (int j = 0; j < nj; j += PF) {
@@ -394,7 +478,7 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
 }
 
 template <bool TER, int BMAX, bool ONE_SLAB>
-__global__ __launch_bounds__(BMAX == 1 ? 64 * MBD_MAX_WAVES : 256)
+__global__ __launch_bounds__(BMAX == 1 ? 1024 : 256)
 __attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8))) void gemv_bq_kernel(BqArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
@@ -405,7 +489,7 @@ __attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8
 }
 
 template <bool TER, int BMAX, bool ONE_SLAB>
-__global__ __launch_bounds__(BMAX == 1 ? 64 * MBD_MAX_WAVES : 256)
+__global__ __launch_bounds__(BMAX == 1 ? 1024 : 256)
 __attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8))) void moe_bq_kernel(BqArgs a) {
     const int job = blockIdx.x / a.row_blocks, rb = blockIdx.x - job * a.row_blocks;
     if (job >= *a.n_jobs) return;
@@ -526,6 +610,9 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks) {
         default: p.RPW = Shape<false, 16>::RPW; p.PF = Shape<false, 16>::PF; break;
     }
     p.nw = bmax == 1 ? MBD_MAX_WAVES : 4;
+    // batch 1: grow the workgroup (up to 16 waves) when that lets every staging
+    // job fit in one pass, i.e. the single-slab kernel
+    if (bmax == 1 && p.C > 64 * p.nw && p.C <= 64 * 16) p.nw = 16;
     auto blocks_for = [&](int nw) {
         int rpb = nw * p.RS * p.RPW;
         return int((M + rpb - 1) / rpb);
@@ -541,7 +628,10 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks) {
     }
     p.SC = sc;
     p.lds = size_t(bmax) * sc * (xq * 16 + 4);   // <= 160 KiB: checked by the caller
-    p.one_slab = sc >= p.C && int64_t(bmax) * p.C <= int64_t(64) * p.nw;
+    const int64_t nsc = int64_t(p.rows_per_block) * (K / 128);
+    p.one_slab = sc >= p.C && int64_t(bmax) * p.C <= int64_t(64) * p.nw && p.C <= 4096 &&
+                 nsc <= int64_t(kScaleLoads) * 64 * p.nw;
+    if (p.one_slab) p.lds += size_t(nsc) * 2;     // staged scales
     return p;
 }
 
@@ -616,6 +706,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     a.x = x;
     a.y = y;
     a.M = int(w->M); a.K = int(w->K); a.C = pl.C; a.G = pl.G; a.SC = pl.SC; a.B = B;
+    a.gshift = __builtin_ctz(unsigned(pl.G)); a.inv_c = 1.0f / float(pl.C);
     a.rows_per_block = pl.rows_per_block;
     return ter ? launch_gemv_bq<true>(pl, a, bmax, st) : launch_gemv_bq<false>(pl, a, bmax, st);
 }
@@ -696,6 +787,7 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
     a.x = x; a.y = y;
     a.M = int(w->M); a.K = int(w->K); a.C = pl.C; a.G = pl.G; a.SC = pl.SC; a.B = 0;
+    a.gshift = __builtin_ctz(unsigned(pl.G)); a.inv_c = 1.0f / float(pl.C);
     a.rows_per_block = pl.rows_per_block;
     a.jobs = jobs; a.n_jobs = n_jobs; a.pair_ids = pair_ids;
     a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0; a.row_blocks = pl.blocks;
