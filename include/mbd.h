@@ -179,9 +179,11 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
 /* Expert GEMV over n_mats stacked TERNARY or INT4 matrices (MoE; [Bolt] routes each
  * token to a subset of experts).  route [T][k] int32 expert ids in [0, n_mats) with
  * distinct ids per token.  x bf16: [T][K] (x_per_pair = 0) or [T][k][K]
- * (x_per_pair = 1).  y fp32 [T][k][M]: y[t][j] = W[route[t][j]] @ x_row.  Every
- * distinct expert's weights are read once per call.  ws: device workspace of at
- * least mbd_moe_workspace_bytes(n_mats, T, k) bytes, 16-byte aligned, contents
+ * (x_per_pair = 1).  y fp32 [T][k][M]: y[t][j] = W[route[t][j]] @ x_row.  An
+ * expert's weights are read once per group of up to 4 tokens routed to it.  At
+ * most 4096 experts (MBD_ESHAPE beyond).  Ids outside [0, n_mats) leave their y
+ * rows unwritten.  ws: device workspace of at least
+ * mbd_moe_workspace_bytes(n_mats, T, k) bytes, 16-byte aligned, contents
  * overwritten.  Calls that share a workspace must not overlap. */
 mbd_status mbd_moe_workspace_bytes(int64_t n_mats, int32_t T, int32_t k, uint64_t* bytes);
 mbd_status mbd_moe_gemv(const mbd_dweights* experts, const int32_t* route, int32_t T,

@@ -31,6 +31,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <climits>
 
 #include "mbd_internal.h"
 
@@ -215,16 +216,19 @@ struct BqArgs {
     int M, K, C, G, SC, B;
     int gshift;              // log2(G)
     float inv_c;             // 1 / C (division-free staging job split)
-    int rows_per_block;
+    int rows_per_block;      // n_iter * tile_rows
+    int tile_rows, n_iter;   // one-slab: the block walks n_iter tiles of tile_rows rows
     // expert (grouped) mode
     const int4* jobs;        // {expert, pair_start, n_pairs, 0}
     const int* n_jobs;
     const int* pair_ids;     // pairs sorted by expert: pair id = t*k + slot
     int topk, x_per_pair, row_blocks;
+    const int* route;        // set: group the routes inside the kernel (n_pairs <= kFusedPairs)
+    int n_pairs, n_experts;
 };
 
 // Scale loads per thread in the one-slab path (rows_per_block * K/128 <= this * threads).
-constexpr int kScaleLoads = 4;
+template <int BMAX> struct ScaleLoads { static constexpr int N = BMAX == 1 ? 4 : 16; };
 
 // Load-ring depth and rows per wave-step for each batch bucket.
 #ifndef MBD_WORD_FENCE
@@ -264,15 +268,24 @@ template <bool TER> struct Shape<TER, 2> { static constexpr int RPW = 2, PF = 2;
 template <bool TER> struct Shape<TER, 4> { static constexpr int RPW = MBD_B4_RPW, PF = 2; };
 template <bool TER> struct Shape<TER, 8> { static constexpr int RPW = 2, PF = 2; };
 template <bool TER> struct Shape<TER, 16> { static constexpr int RPW = 2, PF = 1; };
+#ifndef MBD_BN_WAVES
+#define MBD_BN_WAVES 4        // waves per workgroup for batch > 1
+#endif
+// Batch 1, short rows (one or two chunks per lane): more rows per wave, one load
+// each in flight per row, so that a lane still has several loads outstanding and
+// the block's staged activations serve more rows.
+#ifndef MBD_WIDE_RPW
+#define MBD_WIDE_RPW 4
+#endif
+template <bool TER, int BMAX> struct WideShape { static constexpr int RPW = MBD_WIDE_RPW, PF = 1; };
 
 // Core: rows [row_base, row_base + rows_per_block) of one matrix, nb <= BMAX batch
 // rows whose activations / outputs are given by xrow(b) / yrow(b).
-template <bool TER, int BMAX, bool ONE_SLAB, class XRow, class YRow>
+template <bool TER, int BMAX, int RPW, int PF, bool ONE_SLAB, class XRow, class YRow>
 __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int row_base, int nb,
                                         XRow xrow, YRow yrow) {
     using F = Fmt<TER>;
-    constexpr int RPW = Shape<TER, BMAX>::RPW, PF = Shape<TER, BMAX>::PF;
     extern __shared__ uint4 lds4[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // G is a power of two: all per-lane index math is shifts and masks (integer
@@ -295,6 +308,7 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
         rowp[r] = reinterpret_cast<const u32x4_t*>(codes) + (size_t)row * C + sub;
         srow[r] = scales + (size_t)row * ngroups;
     }
+    const int TR = a.tile_rows, NI = ONE_SLAB ? a.n_iter : 1;
 
     float acc[RPW][BMAX];
 #pragma unroll
@@ -327,6 +341,28 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
         }
         __builtin_amdgcn_sched_barrier(0);   // each slot's loads stay adjacent, in slot order
     };
+    // One-slab walk: items (tile it, chunk j) in order, the ring PF items ahead.
+    int iss_it = 0, iss_j = 0;
+    auto issue_next = [&](int p) {
+        const bool real = iss_it < NI;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int row = min(row0 + iss_it * TR + r * RS, M - 1);
+            const u32x4_t* pc = real ? reinterpret_cast<const u32x4_t*>(codes) + (size_t)row * C + sub + G * iss_j
+                                     : xdummy;
+#if MBD_CODES_NT
+            const u32x4_t v = __builtin_nontemporal_load(pc);
+#else
+            const u32x4_t v = *pc;
+#endif
+            w[p][r] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        if (++iss_j == nj) {
+            iss_j = 0;
+            ++iss_it;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
     // Activation loads first, then the first PF chunks of codes, so that waiting
     // for the activations does not wait for the weight stream.
@@ -340,9 +376,24 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
     for (int r = 0; r < (BMAX == 1 ? 1 : RPW); ++r)
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) part[r][b] = Acc3{0.f, 0.f, 0.f, 0.f};
+    int cur_it = 0;   // one-slab: tile being computed
     auto scale = [&](int p, int r, int cc) {
-        if constexpr (ONE_SLAB) return half_bits_to_f32(sl[(rloc0 + r * RS) * ngroups + (cc / F::CPG)]);
+        if constexpr (ONE_SLAB) return half_bits_to_f32(sl[(rloc0 + cur_it * TR + r * RS) * ngroups + (cc / F::CPG)]);
         else return half_bits_to_f32(uint16_t(s[p][r]));
+    };
+    // reduce across the G lanes of each row group; lane sub == 0 stores
+    auto flush = [&](int it) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                float v = acc[r][b];
+                for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+                const int row = row0 + it * TR + r * RS;
+                if (sub == 0 && b < nb && row < M) yrow(b)[row] = v;
+                acc[r][b] = 0.f;
+            }
+        }
     };
     auto compute = [&](int p, int cc) {
         if constexpr (BMAX == 1 && RPW == 1) {
@@ -412,29 +463,38 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
         stage_load<TER>(xrow(has ? jb : 0) + (size_t)(has ? jc : 0) * F::WPC, xraw);
         // the block's fp16 scales: rows_per_block * ngroups contiguous values
         const int nsc = a.rows_per_block * ngroups;
-        const int sc_lim = (M - row_base) * ngroups;          // rows past M are not read
-        uint16_t sraw[kScaleLoads];
+        const int sc_lim = min(M - row_base, a.rows_per_block) * ngroups;   // rows past M are not read
+        constexpr int NSL = ScaleLoads<BMAX>::N;
+        uint16_t sraw[NSL];
 #pragma unroll
-        for (int i = 0; i < kScaleLoads; ++i) {
+        for (int i = 0; i < NSL; ++i) {
             const int e = myjob + i * (int)blockDim.x;
             sraw[i] = scales[(size_t)row_base * ngroups + ((e < nsc && e < sc_lim) ? e : 0)];
         }
 #pragma unroll
-        for (int p = 0; p < PF; ++p) issue(p, p);
+        for (int p = 0; p < PF; ++p) issue_next(p);
         __builtin_amdgcn_sched_barrier(0);          // keep the weight loads ahead of the staging waits
         if (has) stage_store<TER>(xraw, xl + (size_t)jb * F::XQ * SC + jc, SC, bl + jb * SC + jc);
 #pragma unroll
-        for (int i = 0; i < kScaleLoads; ++i) {
+        for (int i = 0; i < NSL; ++i) {
             const int e = myjob + i * (int)blockDim.x;
             if (e < nsc) sl[e] = sraw[i];
         }
         barrier_lds();
-        for (int j = 0; j < nj; j += PF) {
+        const int total = NI * nj;
+        int cj = 0;
+        for (int f = 0; f < total; f += PF) {
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
-                const int jj = j + p;
-                if (jj < nj) compute(p, sub + G * jj);
-                issue(jj + PF, p);
+                if (f + p < total) {
+                    compute(p, sub + G * cj);
+                    if (++cj == nj) {
+                        flush(cur_it);
+                        cj = 0;
+                        ++cur_it;
+                    }
+                }
+                issue_next(p);
             }
         }
     } else {
@@ -464,43 +524,131 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
         }
     }
 
-    // reduce across the G lanes of each row group; lane sub == 0 stores
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) {
-            float v = acc[r][b];
-            for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-            const int row = row0 + r * RS;
-            if (sub == 0 && b < nb && row < M) yrow(b)[row] = v;
-        }
-    }
+    if constexpr (!ONE_SLAB) flush(0);
 }
 
-template <bool TER, int BMAX, bool ONE_SLAB>
-__global__ __launch_bounds__(BMAX == 1 ? 1024 : 256)
-__attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8))) void gemv_bq_kernel(BqArgs a) {
+#define MBD_BQ_ATTRS(TER, BMAX)                                                     \
+    __launch_bounds__(BMAX == 1 ? 1024 : 64 * MBD_BN_WAVES)                         \
+    __attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8)))
+
+template <bool TER, int BMAX, int RPW, int PF, bool ONE_SLAB>
+__global__ MBD_BQ_ATTRS(TER, BMAX) void gemv_bq_kernel(BqArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    bq_core<TER, BMAX, ONE_SLAB>(
+    bq_core<TER, BMAX, RPW, PF, ONE_SLAB>(
         a, a.codes, a.scales, blockIdx.x * a.rows_per_block, a.B,
         [=](int b) { return x + (size_t)b * K; }, [=](int b) { return y + (size_t)b * M; });
 }
 
-template <bool TER, int BMAX, bool ONE_SLAB>
-__global__ __launch_bounds__(BMAX == 1 ? 1024 : 256)
-__attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8))) void moe_bq_kernel(BqArgs a) {
+// Routes of up to kFusedPairs (token, slot) pairs are grouped inside the expert
+// kernel itself (every block redoes it: cheap only while the route is short);
+// up to kSortPairs by one workgroup of moe_group_sort_kernel; longer ones by
+// moe_group_kernel.
+constexpr int kFusedPairs = 32;
+constexpr int kSortPairs = 256;
+
+// Workgroup-wide grouping.  Pairs are ordered by (expert, pair id): a pair's rank
+// is the number of pairs with a smaller expert plus the number of earlier pairs
+// with the same expert, counted by all threads over segments of the pair list and
+// summed with integer LDS atomics, so the order never depends on timing.  A job
+// is a run of at most bmax consecutive pairs of one expert.  On return, for each
+// rank q: g[5][q] = pair id; g[4][q] = (expert << 5 | pairs) where a job starts
+// at q, else -1; g[1][q] = that job's index.
+template <int NP>
+__device__ void moe_sort_block(const int* __restrict__ route, int P, int E, int bmax, int (&g)[6][NP]) {
+    int *ge = g[0], *glo = g[1], *grk = g[2], *gcn = g[3], *ginfo = g[4], *gs = g[5];
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int i = tid; i < P; i += nt) {
+        const int e = route[i];
+        ge[i] = (e >= 0 && e < E) ? e : INT_MAX;   // ids out of range sort last and form no job
+        glo[i] = 0;
+        grk[i] = 0;
+        gcn[i] = 0;
+    }
+    __syncthreads();
+    const int S = max(1, nt / P), L = (P + S - 1) / S;
+    for (int t = tid; t < P * S; t += nt) {
+        const int s = t / P, i = t - s * P;
+        const int ei = ge[i], u1 = min(P, (s + 1) * L);
+        int lo = 0, rk = 0, cn = 0;
+        for (int u = s * L; u < u1; ++u) {
+            const int eu = ge[u];
+            lo += eu < ei;
+            cn += eu == ei;
+            rk += (eu == ei) & (u < i);
+        }
+        if (lo) atomicAdd(&glo[i], lo);
+        if (rk) atomicAdd(&grk[i], rk);
+        if (cn) atomicAdd(&gcn[i], cn);
+    }
+    __syncthreads();
+    for (int i = tid; i < P; i += nt) {
+        const int r = grk[i], rank = glo[i] + r;
+        gs[rank] = i;
+        ginfo[rank] = (ge[i] != INT_MAX && (r & (bmax - 1)) == 0) ? (ge[i] << 5) | min(bmax, gcn[i] - r) : -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < P; i += nt) glo[i] = 0;   // reused: jobs starting before each rank
+    __syncthreads();
+    for (int t = tid; t < P * S; t += nt) {
+        const int s = t / P, q = t - s * P;
+        if (ginfo[q] < 0) continue;
+        const int u1 = min(q, (s + 1) * L);
+        int n = 0;
+        for (int u = s * L; u < u1; ++u) n += ginfo[u] >= 0;
+        if (n) atomicAdd(&glo[q], n);
+    }
+    __syncthreads();
+}
+
+// One workgroup groups a route of at most kSortPairs pairs into the job table.
+__global__ __launch_bounds__(1024) void moe_group_sort_kernel(const int* __restrict__ route, int P, int E, int bmax,
+                                                              int* __restrict__ pair_ids, int4* __restrict__ jobs,
+                                                              int* __restrict__ n_jobs) {
+    __shared__ int g[6][kSortPairs];
+    __shared__ int total;
+    if (threadIdx.x == 0) total = 0;
+    moe_sort_block<kSortPairs>(route, P, E, bmax, g);
+    for (int q = threadIdx.x; q < P; q += blockDim.x) {
+        pair_ids[q] = g[5][q];
+        const int info = g[4][q];
+        if (info >= 0) {
+            jobs[g[1][q]] = make_int4(info >> 5, q, info & 31, 0);
+            atomicAdd(&total, 1);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *n_jobs = total;
+}
+
+template <bool TER, int BMAX, int RPW, int PF, bool ONE_SLAB>
+__global__ MBD_BQ_ATTRS(TER, BMAX) void moe_bq_kernel(BqArgs a) {
+    __shared__ int g[6][kFusedPairs];
+    __shared__ int4 gjob;
     const int job = blockIdx.x / a.row_blocks, rb = blockIdx.x - job * a.row_blocks;
-    if (job >= *a.n_jobs) return;
-    const int4 jd = a.jobs[job];
-    const int e = jd.x, start = jd.y, nb = jd.z;
-    const int* pids = a.pair_ids + start;
+    int4 jd;
+    const int* pids;
+    if (a.route) {
+        if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
+        moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, BMAX, g);
+        for (int q = threadIdx.x; q < a.n_pairs; q += blockDim.x)
+            if (g[4][q] >= 0 && g[1][q] == job) gjob = make_int4(g[4][q] >> 5, q, g[4][q] & 31, 0);
+        __syncthreads();
+        jd = gjob;
+        if (jd.x < 0) return;
+        pids = g[5] + jd.y;
+    } else {
+        if (job >= *a.n_jobs) return;
+        jd = a.jobs[job];
+        pids = a.pair_ids + jd.y;
+    }
+    const int e = jd.x, nb = jd.z;
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)a.M * a.C, per_scales = (size_t)a.M * (a.K / 128);
-    bq_core<TER, BMAX, ONE_SLAB>(
+    bq_core<TER, BMAX, RPW, PF, ONE_SLAB>(
         a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * a.rows_per_block, nb,
         [=](int b) {
             const int p = pids[b];
@@ -509,32 +657,56 @@ __attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8
         [=](int b) { return y + (size_t)pids[b] * M; });
 }
 
-// Group (token, slot) pairs by expert: counting sort, then jobs of <= bmax pairs.
-// One workgroup; deterministic (pairs keep ascending order within an expert).
-__global__ __launch_bounds__(256) void moe_group_kernel(const int* __restrict__ route, int P, int E, int bmax,
-                                                        int* __restrict__ counts, int* __restrict__ offsets,
-                                                        int* __restrict__ pair_ids, int4* __restrict__ jobs,
-                                                        int* __restrict__ n_jobs) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+// Group (token, slot) pairs by expert: a wave per expert counts its pairs with
+// ballots, one wave scans the counts into pair and job offsets, and the pairs
+// are written back in ascending pair order (deterministic), with jobs of at most
+// bmax pairs.  Pairs whose expert id is out of range are dropped.
+constexpr int kMaxExperts = 4096;
+
+__global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__ route, int P, int E, int bmax,
+                                                         int* __restrict__ pair_ids, int4* __restrict__ jobs,
+                                                         int* __restrict__ n_jobs) {
+    __shared__ int cnt[kMaxExperts], off[kMaxExperts], joff[kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int e = wave; e < E; e += nw) {
         int c = 0;
-        for (int p = 0; p < P; ++p) c += (route[p] == e);
-        counts[e] = c;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int off = 0, nj = 0;
-        for (int e = 0; e < E; ++e) {
-            offsets[e] = off;
-            for (int s = 0; s < counts[e]; s += bmax) jobs[nj++] = make_int4(e, off + s, min(bmax, counts[e] - s), 0);
-            off += counts[e];
+        for (int p0 = 0; p0 < P; p0 += 64) {
+            const int p = p0 + lane;
+            c += __popcll(__ballot(p < P && route[p] == e));
         }
-        *n_jobs = nj;
+        if (lane == 0) cnt[e] = c;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int o = offsets[e];
-        for (int p = 0; p < P; ++p)
-            if (route[p] == e) pair_ids[o++] = p;
+    if (wave == 0) {
+        int run = 0, jrun = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int c = e < E ? cnt[e] : 0, jc = (c + bmax - 1) / bmax;
+            int ic = c, ij = jc;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int tc = __shfl_up(ic, o, 64), tj = __shfl_up(ij, o, 64);
+                if (lane >= o) { ic += tc; ij += tj; }
+            }
+            if (e < E) { off[e] = run + ic - c; joff[e] = jrun + ij - jc; }
+            run += __shfl(ic, 63, 64);
+            jrun += __shfl(ij, 63, 64);
+        }
+        if (lane == 0) *n_jobs = jrun;
+    }
+    __syncthreads();
+    for (int e = wave; e < E; e += nw) {
+        int base = off[e];
+        for (int p0 = 0; p0 < P; p0 += 64) {
+            const int p = p0 + lane;
+            const bool hit = p < P && route[p] == e;
+            const unsigned long long m = __ballot(hit);
+            if (hit) pair_ids[base + __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0))] = p;
+            base += __popcll(m);
+        }
+        const int c = cnt[e], j0 = joff[e], o0 = off[e];
+        for (int sidx = lane * bmax; sidx < c; sidx += 64 * bmax)
+            jobs[j0 + sidx / bmax] = make_int4(e, o0 + sidx, min(bmax, c - sidx), 0);
     }
 }
 
@@ -590,36 +762,56 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
 struct BqPlan {
     int C, G, RS, RPW, PF, nw, rows_per_block, SC, blocks;
+    int tile_rows, n_iter;
     size_t lds;
     bool one_slab;   // all activations staged at once, one staging job per thread at most
+    bool wide;       // short rows: the many-rows-per-wave shape
 };
 
-BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks) {
+#ifndef MBD_MAX_TILES
+#define MBD_MAX_TILES 2       // row tiles one workgroup walks at most
+#endif
+#ifndef MBD_MOE_BLOCKS
+#define MBD_MOE_BLOCKS 512
+#endif
+
+// min_blocks: shrink the workgroup until the grid has at least this many blocks.
+// n_mats: matrices the call covers (the grid is n_mats times the plan's blocks).
+// In the single-slab kernel a block then walks several row tiles when there are
+// more tiles than about one round of resident workgroups, so its staged
+// activations serve more rows.
+BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks, int prefer_nw = MBD_MAX_WAVES,
+               int64_t n_mats = 1) {
     BqPlan p{};
     const int wpc = ter ? 64 : 32, xq = ter ? 8 : 4;   // uint4 of activations per chunk
     p.C = int(K / wpc);
     p.G = 64;
     while (p.C % p.G) p.G >>= 1;
     p.RS = 64 / p.G;
-    switch (bmax) {
-        case 1: p.RPW = ter ? Shape<true, 1>::RPW : Shape<false, 1>::RPW;
-                p.PF = ter ? Shape<true, 1>::PF : Shape<false, 1>::PF; break;
-        case 2: p.RPW = Shape<false, 2>::RPW; p.PF = Shape<false, 2>::PF; break;
-        case 4: p.RPW = Shape<false, 4>::RPW; p.PF = Shape<false, 4>::PF; break;
-        case 8: p.RPW = Shape<false, 8>::RPW; p.PF = Shape<false, 8>::PF; break;
-        default: p.RPW = Shape<false, 16>::RPW; p.PF = Shape<false, 16>::PF; break;
+    p.wide = bmax == 1 && p.C / p.G <= 2 && M * n_mats * p.G >= int64_t(2048) * 64 * MBD_WIDE_RPW;
+    if (p.wide) {
+        p.RPW = MBD_WIDE_RPW; p.PF = 1;
+    } else {
+        switch (bmax) {
+            case 1: p.RPW = ter ? Shape<true, 1>::RPW : Shape<false, 1>::RPW;
+                    p.PF = ter ? Shape<true, 1>::PF : Shape<false, 1>::PF; break;
+            case 2: p.RPW = Shape<false, 2>::RPW; p.PF = Shape<false, 2>::PF; break;
+            case 4: p.RPW = Shape<false, 4>::RPW; p.PF = Shape<false, 4>::PF; break;
+            case 8: p.RPW = Shape<false, 8>::RPW; p.PF = Shape<false, 8>::PF; break;
+            default: p.RPW = Shape<false, 16>::RPW; p.PF = Shape<false, 16>::PF; break;
+        }
     }
-    p.nw = bmax == 1 ? MBD_MAX_WAVES : 4;
+    p.nw = bmax == 1 ? prefer_nw : MBD_BN_WAVES;
     // batch 1: grow the workgroup (up to 16 waves) when that lets every staging
     // job fit in one pass, i.e. the single-slab kernel
     if (bmax == 1 && p.C > 64 * p.nw && p.C <= 64 * 16) p.nw = 16;
-    auto blocks_for = [&](int nw) {
-        int rpb = nw * p.RS * p.RPW;
-        return int((M + rpb - 1) / rpb);
+    auto tiles_for = [&](int nw) {
+        const int64_t tr = int64_t(nw) * p.RS * p.RPW;
+        return (M + tr - 1) / tr;
     };
-    while (p.nw > 1 && blocks_for(p.nw) < min_blocks) p.nw >>= 1;
-    p.rows_per_block = p.nw * p.RS * p.RPW;
-    p.blocks = blocks_for(p.nw);
+    while (p.nw > 1 && tiles_for(p.nw) < min_blocks) p.nw >>= 1;
+    p.tile_rows = p.nw * p.RS * p.RPW;
+    const int64_t tiles = tiles_for(p.nw);
     const size_t per_chunk = size_t(bmax) * (xq * 16 + 4);
     int sc = int(std::min<size_t>(p.C, (64 * 1024) / per_chunk));
     if (sc < p.C) {
@@ -628,43 +820,64 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks) {
     }
     p.SC = sc;
     p.lds = size_t(bmax) * sc * (xq * 16 + 4);   // <= 160 KiB: checked by the caller
-    const int64_t nsc = int64_t(p.rows_per_block) * (K / 128);
+    const int64_t ngroups = K / 128;
+    const int64_t scale_cap = int64_t(bmax == 1 ? ScaleLoads<1>::N : ScaleLoads<2>::N) * 64 * p.nw;
     p.one_slab = sc >= p.C && int64_t(bmax) * p.C <= int64_t(64) * p.nw && p.C <= 4096 &&
-                 nsc <= int64_t(kScaleLoads) * 64 * p.nw;
-    if (p.one_slab) p.lds += size_t(nsc) * 2;     // staged scales
+                 int64_t(p.tile_rows) * ngroups <= scale_cap;
+    p.n_iter = 1;
+    if (p.one_slab) {
+        // about one round of resident workgroups (waves per CU: 8 per SIMD at
+        // batch 1, 4 above), at least min_blocks
+        const int64_t waves_per_cu = bmax == 1 ? 32 : 16;
+        const int64_t round = std::max<int64_t>(min_blocks, 256 * waves_per_cu / p.nw / std::max<int64_t>(1, n_mats));
+        int64_t it = std::max<int64_t>(1, tiles / round);
+        it = std::min<int64_t>(it, scale_cap / (int64_t(p.tile_rows) * ngroups));
+        it = std::min<int64_t>(it, MBD_MAX_TILES);
+        p.n_iter = int(std::max<int64_t>(1, it));
+    }
+    p.rows_per_block = p.n_iter * p.tile_rows;
+    p.blocks = int((M + p.rows_per_block - 1) / p.rows_per_block);
+    if (p.one_slab) p.lds += size_t(p.rows_per_block) * ngroups * 2;     // staged scales
     return p;
 }
 
+// Kernel variants: batch bucket x (rows per wave, ring depth) x single/multi slab.
+#define MBD_BQ_DISPATCH(KERNEL, TER, pl, bmax, grid, st, a, what)                                        \
+    do {                                                                                                  \
+        dim3 blk_(64 * (pl).nw);                                                                          \
+        auto go_ = [&](auto kern) {                                                                       \
+            hipLaunchKernelGGL(kern, dim3(grid), blk_, (pl).lds, st, a);                                  \
+            return hip_check(what);                                                                       \
+        };                                                                                                \
+        const bool os_ = (pl).one_slab;                                                                   \
+        if ((pl).wide) {                                                                                  \
+            constexpr int WR = WideShape<TER, 1>::RPW;                                                    \
+            return os_ ? go_(KERNEL<TER, 1, WR, 1, true>) : go_(KERNEL<TER, 1, WR, 1, false>);             \
+        } else {                                                                                          \
+            constexpr int R1 = Shape<TER, 1>::RPW, P1 = Shape<TER, 1>::PF;                                \
+            constexpr int R2 = Shape<TER, 2>::RPW, P2 = Shape<TER, 2>::PF;                                \
+            constexpr int R4 = Shape<TER, 4>::RPW, P4 = Shape<TER, 4>::PF;                                \
+            constexpr int R8 = Shape<TER, 8>::RPW, P8 = Shape<TER, 8>::PF;                                \
+            constexpr int R16 = Shape<TER, 16>::RPW, P16 = Shape<TER, 16>::PF;                            \
+            switch (bmax) {                                                                               \
+                case 1: return os_ ? go_(KERNEL<TER, 1, R1, P1, true>) : go_(KERNEL<TER, 1, R1, P1, false>); \
+                case 2: return os_ ? go_(KERNEL<TER, 2, R2, P2, true>) : go_(KERNEL<TER, 2, R2, P2, false>); \
+                case 4: return os_ ? go_(KERNEL<TER, 4, R4, P4, true>) : go_(KERNEL<TER, 4, R4, P4, false>); \
+                case 8: return os_ ? go_(KERNEL<TER, 8, R8, P8, true>) : go_(KERNEL<TER, 8, R8, P8, false>); \
+                case 16: return os_ ? go_(KERNEL<TER, 16, R16, P16, true>) : go_(KERNEL<TER, 16, R16, P16, false>); \
+            }                                                                                             \
+        }                                                                                                 \
+        return fail(MBD_EINVAL, "no kernel variant for batch %d", bmax);                                  \
+    } while (0)
+
 template <bool TER>
 mbd_status launch_gemv_bq(const BqPlan& pl, BqArgs a, int bmax, hipStream_t st) {
-    dim3 grid(pl.blocks), block(64 * pl.nw);
-#define MBD_GEMV_CASE(BM)                                                                             \
-    if (bmax == BM) {                                                                                 \
-        if (pl.one_slab)                                                                              \
-            hipLaunchKernelGGL((gemv_bq_kernel<TER, BM, true>), grid, block, pl.lds, st, a);          \
-        else                                                                                          \
-            hipLaunchKernelGGL((gemv_bq_kernel<TER, BM, false>), grid, block, pl.lds, st, a);         \
-        return hip_check("gemv launch");                                                              \
-    }
-    MBD_GEMV_CASE(1) MBD_GEMV_CASE(2) MBD_GEMV_CASE(4) MBD_GEMV_CASE(8) MBD_GEMV_CASE(16)
-#undef MBD_GEMV_CASE
-    return fail(MBD_EINVAL, "no gemv variant for batch %d", bmax);
+    MBD_BQ_DISPATCH(gemv_bq_kernel, TER, pl, bmax, pl.blocks, st, a, "gemv launch");
 }
 
 template <bool TER>
 mbd_status launch_moe_bq(const BqPlan& pl, BqArgs a, int bmax, int grid_blocks, hipStream_t st) {
-    dim3 grid(grid_blocks), block(64 * pl.nw);
-#define MBD_MOE_CASE(BM)                                                                              \
-    if (bmax == BM) {                                                                                 \
-        if (pl.one_slab)                                                                              \
-            hipLaunchKernelGGL((moe_bq_kernel<TER, BM, true>), grid, block, pl.lds, st, a);           \
-        else                                                                                          \
-            hipLaunchKernelGGL((moe_bq_kernel<TER, BM, false>), grid, block, pl.lds, st, a);          \
-        return hip_check("moe gemv launch");                                                          \
-    }
-    MBD_MOE_CASE(1) MBD_MOE_CASE(2) MBD_MOE_CASE(4) MBD_MOE_CASE(8) MBD_MOE_CASE(16)
-#undef MBD_MOE_CASE
-    return fail(MBD_EINVAL, "no expert gemv variant for batch %d", bmax);
+    MBD_BQ_DISPATCH(moe_bq_kernel, TER, pl, bmax, grid_blocks, st, a, "expert gemv launch");
 }
 
 int round_batch(int B) {
@@ -707,7 +920,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     a.y = y;
     a.M = int(w->M); a.K = int(w->K); a.C = pl.C; a.G = pl.G; a.SC = pl.SC; a.B = B;
     a.gshift = __builtin_ctz(unsigned(pl.G)); a.inv_c = 1.0f / float(pl.C);
-    a.rows_per_block = pl.rows_per_block;
+    a.rows_per_block = pl.rows_per_block; a.tile_rows = pl.tile_rows; a.n_iter = pl.n_iter;
     return ter ? launch_gemv_bq<true>(pl, a, bmax, st) : launch_gemv_bq<false>(pl, a, bmax, st);
 }
 
@@ -735,19 +948,14 @@ mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
     return hip_check("dequant launch");
 }
 
-// Workspace: counts[E] offsets[E] n_jobs[4] pair_ids[P] jobs[max_jobs] (int4).
+// Workspace: n_jobs[4] pair_ids[P] (padded to 16 B) jobs[min(E, P) + P] (int4).
 mbd_status mbd_moe_workspace_bytes(int64_t n_mats, int32_t T, int32_t k, uint64_t* bytes) {
     if (!bytes) return fail(MBD_EINVAL, "bytes is NULL");
-    if (n_mats < 1 || n_mats > 65536 || T < 1 || k < 1 || int64_t(T) * k > (1 << 20))
-        return fail(MBD_ESHAPE, "bad expert routing shape");
+    if (n_mats < 1 || n_mats > kMaxExperts || T < 1 || k < 1 || int64_t(T) * k > (1 << 20))
+        return fail(MBD_ESHAPE, "bad expert routing shape (at most %d experts)", kMaxExperts);
     const int64_t P = int64_t(T) * k;
     const int64_t max_jobs = std::min<int64_t>(n_mats, P) + P;
-    uint64_t b = 0;
-    b += ((uint64_t(n_mats) * 4 + 15) / 16) * 16 * 2;   // counts, offsets
-    b += 16;                                             // n_jobs
-    b += ((uint64_t(P) * 4 + 15) / 16) * 16;             // pair ids
-    b += uint64_t(max_jobs) * 16;                        // jobs
-    *bytes = b;
+    *bytes = 16 + ((uint64_t(P) * 4 + 15) / 16) * 16 + uint64_t(max_jobs) * 16;
     return MBD_OK;
 }
 
@@ -768,29 +976,39 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int E = int(w->n_mats), P = T * k;
-    const int bmax = std::min(16, round_batch(T));
-    const int64_t max_jobs = std::min<int64_t>(E, P) + (P + bmax - 1) / bmax;
-    char* base = static_cast<char*>(ws);
-    int* counts = reinterpret_cast<int*>(base);
-    int* offsets = counts + ((E * 4 + 15) / 16) * 4;
-    int* n_jobs = offsets + ((E * 4 + 15) / 16) * 4;
+    // jobs of at most 4 pairs (the batch-4 kernel); an expert routed more than 4
+    // tokens is read once per group of 4
+    const int bmax = std::min(4, round_batch(T));
+    // sum over experts of ceil(pairs / bmax) <= D + (P - D) / bmax, D = distinct experts
+    const int64_t D = std::min<int64_t>(E, P), max_jobs = D + (P - D) / bmax;
+    const bool fused = P <= kFusedPairs;
+    int* n_jobs = static_cast<int*>(ws);
     int* pair_ids = n_jobs + 4;
     int4* jobs = reinterpret_cast<int4*>(pair_ids + ((P * 4 + 15) / 16) * 4);
-    hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), 0, st, route, P, E, bmax, counts, offsets, pair_ids,
-                       jobs, n_jobs);
-    if ((s = hip_check("expert grouping launch")) != MBD_OK) return s;
+    if (!fused) {
+        if (P <= kSortPairs)
+            hipLaunchKernelGGL(moe_group_sort_kernel, dim3(1), dim3(1024), 0, st, route, P, E, bmax, pair_ids, jobs, n_jobs);
+        else
+            hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, st, route, P, E, bmax, pair_ids, jobs, n_jobs);
+        if ((s = hip_check("expert grouping launch")) != MBD_OK) return s;
+    }
     const bool ter = w->fmt == MBD_TERNARY_B128;
-    BqPlan pl = plan_bq(ter, w->M, w->K, bmax, 64);
-    if (pl.lds > kMaxLds) return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
+    // about MBD_MOE_BLOCKS workgroups over the whole call
+    const int min_blocks = int(std::max<int64_t>(1, MBD_MOE_BLOCKS / std::max<int64_t>(1, D)));
+    BqPlan pl = plan_bq(ter, w->M, w->K, bmax, min_blocks, 16, D);
+    if (pl.lds + sizeof(int) * 6 * kFusedPairs + 16 > kMaxLds)
+        return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
     BqArgs a{};
     a.codes = static_cast<const uint4*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
     a.x = x; a.y = y;
     a.M = int(w->M); a.K = int(w->K); a.C = pl.C; a.G = pl.G; a.SC = pl.SC; a.B = 0;
     a.gshift = __builtin_ctz(unsigned(pl.G)); a.inv_c = 1.0f / float(pl.C);
-    a.rows_per_block = pl.rows_per_block;
+    a.rows_per_block = pl.rows_per_block; a.tile_rows = pl.tile_rows; a.n_iter = pl.n_iter;
     a.jobs = jobs; a.n_jobs = n_jobs; a.pair_ids = pair_ids;
     a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0; a.row_blocks = pl.blocks;
+    a.route = fused ? route : nullptr;
+    a.n_pairs = P; a.n_experts = E;
     const int64_t grid = max_jobs * pl.blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
     return ter ? launch_moe_bq<true>(pl, a, bmax, int(grid), st) : launch_moe_bq<false>(pl, a, bmax, int(grid), st);

@@ -188,6 +188,51 @@ def test_moe_full(dev, T, which):
     assert err <= TOL
 
 
+MOE_CASES = [
+    # (format, experts, M, K, T, k, x_per_pair): fused in-kernel grouping for T*k <= 256,
+    # the separate grouping kernel above; few experts => several jobs per expert
+    ("ternary", 16, 72, 384, 3, 4, False),
+    ("int4", 16, 40, 640, 5, 3, True),
+    ("ternary", 4, 24, 1536, 13, 3, False),
+    ("int4", 5, 130, 256, 40, 2, True),
+    ("ternary", 16, 96, 4096, 40, 8, False),
+    ("int4", 32, 33, 1024, 64, 8, True),
+    ("ternary", 3, 64, 128, 100, 3, False),
+]
+
+
+@pytest.mark.parametrize("case", MOE_CASES, ids=lambda c: "%s_E%d_%dx%d_T%d_k%d_%s" % (c[0], c[1], c[2], c[3], c[4], c[5], "pp" if c[6] else "tok"))
+def test_moe_ragged(dev, case):
+    mbd = _mbd()
+    kind, E, M, K, T, k, per_pair = case
+    print("case moe_ragged", case, flush=True)
+    rng = np.random.default_rng(E * 1000 + T)
+    routes = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    routes[T // 2, k - 1] = E                          # an id out of range: its row stays unwritten
+    mats = [_rand_w(100 + e, M, K) for e in range(E)]
+    dw = mbd.to_device(mbd.mbd_pack(_fmt(kind), np.concatenate(mats)), dev, n_mats=E)
+    xb = _rand_x(7, T * k if per_pair else T, K)
+    ws = torch.empty(mbd.mbd_moe_workspace_bytes(E, T, k), dtype=torch.uint8, device=dev)
+    y = torch.full((T, k, M), float("nan"), dtype=torch.float32, device=dev)
+    mbd.mbd_moe_gemv(dw, torch.from_numpy(routes).to(dev), _x_dev(xb, dev), per_pair, y, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    mod = QUANT[kind]
+    deq = [mod.dequant(*mod.quantize(m)) for m in mats]
+    xv = bits.bf16_value(xb)
+    ref = np.zeros((T, k, M))
+    for t in range(T):
+        for j in range(k):
+            if routes[t, j] < E:
+                ref[t, j] = deq[routes[t, j]] @ (xv[t * k + j] if per_pair else xv[t])
+    assert np.isnan(got[T // 2, k - 1]).all()
+    got[T // 2, k - 1] = 0.0
+    assert not np.isnan(got).any()
+    err = gemv.rel_l2(got, ref)
+    print("moe ragged rel_l2=%.3e" % err, flush=True)
+    assert err <= TOL
+
+
 # ------------------------------------------------------------ Cassandra
 
 def _cas(dev, w, norms, only=None):
