@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <type_traits>
 
 #include "mbd_internal.h"
 
@@ -209,31 +211,11 @@ __device__ __forceinline__ void decode_tile(const CasArgs& a, int64_t t, int tl,
     (void)np;
 }
 
-// ------------------------------------------------------------------ dense decode
+// ------------------------------------------------------------------ draft GEMV, any shape
 
-template <bool RESTORE>
-__global__ __launch_bounds__(256) void decode_dense_kernel(CasArgs a, uint16_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint16_t bufs[4][ROW_STRIDE];
-    __shared__ uint8_t cb[256];
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) cb[i] = i < a.n_sym ? a.codebook[i] : 0;
-    __syncthreads();
-    const int wave = threadIdx.x >> 6, lane = lane_id();
-    const int64_t t = int64_t(blockIdx.x) * 4 + wave;
-    if (t >= a.T) return;
-    const int tl = int(min<int64_t>(TILE, a.N - t * TILE));
-    uint32_t pairs[32];
-    decode_tile<RESTORE>(a, t, tl, bufs[wave], cb, pairs);
-    if (64 * lane < tl) {
-        uint4* dst = reinterpret_cast<uint4*>(out + t * TILE + 64 * lane);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = make_uint4(pairs[4 * i], pairs[4 * i + 1], pairs[4 * i + 2], pairs[4 * i + 3]);
-    }
-}
-
-// ------------------------------------------------------------------ draft GEMV
-
-// Block = R consecutive rows (flat range [r0*K, (r0+R)*K)); its waves take the
-// overlapping tiles round robin.  Lane partials are reduced per (row, batch).
+// Dense-walk fallback for K < 4096 or batches above 2.  Block = R consecutive rows
+// (flat range [r0*K, (r0+R)*K)); its waves take the overlapping tiles round robin.
+// Lane partials are reduced per (row, batch).
 template <int BMAX, int R>
 __global__ __launch_bounds__(256) void spec_gemv_kernel(CasArgs a, const uint16_t* __restrict__ x, int B,
                                                         float* __restrict__ y) {
@@ -303,60 +285,591 @@ __global__ __launch_bounds__(256) void spec_gemv_kernel(CasArgs a, const uint16_
     }
 }
 
+// ------------------------------------------------------------------ kept-domain decode
+//
+// The decoders below give every lane of a wave an equal share of a tile's kept
+// values (or of its pruned values) instead of an equal share of its positions,
+// so no lane walks the 70% of positions it has nothing to do for:
+//
+//   * staging: the tile's unary words and bitmap words go to the wave's LDS area
+//     with exclusive prefix counts of their one bits;
+//   * start: a lane's first kept index j0 is located in the unary stream (end of
+//     codeword j0 - 1) and in the bitmap (position of kept j0) by binary search
+//     over those prefix counts and a select inside the word;
+//   * walk: per kept value, the next one bit of the unary stream gives the rank
+//     (zero run length), the next set bit of the bitmap gives the position, and
+//     the spec nibble comes from a register window aligned once per 24 values.
+//
+// Tiles whose unary stream spans more than 128 words (over 4096 code bits, far
+// above the ~2.9 bits per kept value of an entropy-ranked codebook) take the same
+// walk with the words read from memory and a linear start search.
+
+constexpr int STAGE_UW = 128;   // unary words staged per wave
+constexpr int NIB_CHUNK = 32;   // kept values per aligned nibble window (128 bits)
+constexpr int GRP = 4;          // kept values decoded before their LDS reads are issued
+constexpr int PRU_CHUNK = 32;   // pruned values per aligned register window
+
+struct WaveArea {
+    uint32_t uw[STAGE_UW];      // unary words of the tile, bits outside it cleared
+    uint32_t bw[TILE / 32];     // bitmap words of the tile
+    uint16_t up[STAGE_UW];      // one bits before each unary word
+    uint16_t bp[TILE / 64];     // kept values before each 64-position pair of words
+};
+
+struct TileHdr {
+    int64_t f0;      // first flat element
+    int64_t kp0;     // kept values before the tile
+    int64_t bo0, bo1;  // unary bit range
+    int64_t ws;      // first unary word touched
+    int tl;          // elements in the tile
+    int nk;          // kept values in the tile
+    int nuw;         // unary words touched
+};
+
+__device__ __forceinline__ TileHdr tile_hdr(const CasArgs& a, int64_t t) {
+    TileHdr h;
+    h.f0 = t * TILE;
+    h.tl = int(min<int64_t>(TILE, a.N - h.f0));
+    h.kp0 = a.kprefix[t];
+    h.nk = int(int64_t(a.kprefix[t + 1]) - h.kp0);
+    h.bo0 = int64_t(a.bitoff[t]);
+    h.bo1 = int64_t(a.bitoff[t + 1]);
+    h.ws = h.bo0 >> 5;
+    h.nuw = int(((h.bo1 + 31) >> 5) - h.ws);
+    return h;
+}
+
+// Word k of the tile's unary window with the bits of neighbouring tiles cleared.
+__device__ __forceinline__ uint32_t unary_word(const CasArgs& a, const TileHdr& h, int k) {
+    const int64_t w = h.ws + k;
+    uint32_t v = a.unary[w];
+    const int64_t b0 = w * 32;
+    if (b0 < h.bo0) v &= ~0u << int(h.bo0 - b0);
+    const int64_t lim = h.bo1 - b0;
+    if (lim < 32) v &= lim <= 0 ? 0u : ((1u << int(lim)) - 1u);
+    return v;
+}
+
+// Position of the r-th (from 0) set bit of w; w has more than r set bits.
+__device__ __forceinline__ int select32(uint32_t w, int r) {
+    int pos = 0;
+#pragma unroll
+    for (int half = 16; half; half >>= 1) {
+        const int c = __popc(w & ((1u << half) - 1u));
+        if (r >= c) {
+            r -= c;
+            w >>= half;
+            pos += half;
+        }
+    }
+    return pos;
+}
+
+// Stage the tile's bitmap (and, when it fits, its unary words) with prefix counts.
+__device__ __forceinline__ void stage_tile(const CasArgs& a, const TileHdr& h, int64_t t, WaveArea& W) {
+    const int lane = lane_id();
+    if (h.nuw <= STAGE_UW) {
+        const uint32_t u0 = lane < h.nuw ? unary_word(a, h, lane) : 0u;
+        const uint32_t u1 = lane + 64 < h.nuw ? unary_word(a, h, lane + 64) : 0u;
+        // both counts in one scan: each prefix stays below 2^11
+        const int c0 = __popc(u0), c1 = __popc(u1);
+        const int inc = wave_incl_add(c0 | (c1 << 16));
+        const int tot0 = __shfl(inc, 63, 64) & 0xFFFF;
+        W.uw[lane] = u0;
+        W.uw[lane + 64] = u1;
+        W.up[lane] = uint16_t((inc & 0xFFFF) - c0);
+        W.up[lane + 64] = uint16_t(tot0 + (inc >> 16) - c1);
+    }
+    const int64_t wi = t * (TILE / 32) + 2 * lane;
+    const int64_t nwords = (a.N + 31) >> 5;
+    const uint32_t b0 = wi < nwords ? a.bitmap[wi] : 0u;
+    const uint32_t b1 = wi + 1 < nwords ? a.bitmap[wi + 1] : 0u;
+    W.bw[2 * lane] = b0;
+    W.bw[2 * lane + 1] = b1;
+    const int pc = __popc(b0) + __popc(b1);
+    W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+    wave_sync_lds();
+}
+
+// Cursor over the tile's unary codewords.
+template <bool FAST>
+struct UnaryCursor {
+    int k;          // current word
+    uint32_t cw;    // its unconsumed bits
+    int q;          // position of the last one bit consumed (window relative)
+    __device__ __forceinline__ uint32_t word(const CasArgs& a, const TileHdr& h, const WaveArea& W, int i) const {
+        if constexpr (FAST) return W.uw[i];
+        else return unary_word(a, h, i);
+    }
+    // position at codeword j0 (the first j0 codewords consumed)
+    __device__ __forceinline__ void start(const CasArgs& a, const TileHdr& h, const WaveArea& W, int j0) {
+        const int target = j0 - 1;      // the one bit that ends codeword j0 - 1
+        int kk = 0, base = 0;
+        if (j0 > 0) {
+            if constexpr (FAST) {
+#pragma unroll
+                for (int s = 64; s; s >>= 1)
+                    if (kk + s < h.nuw && int(W.up[kk + s]) <= target) kk += s;
+                base = W.up[kk];
+            } else {
+                for (;;) {
+                    const int c = __popc(word(a, h, W, kk));
+                    if (base + c > target) break;
+                    base += c;
+                    ++kk;
+                }
+            }
+        }
+        const uint32_t w = word(a, h, W, kk);
+        const int b = j0 > 0 ? select32(w, target - base) : int(h.bo0 & 31) - 1;
+        k = kk;
+        q = 32 * kk + b;
+        cw = j0 > 0 ? w & ~((2u << b) - 1u) : w;
+    }
+    // rank of the next codeword
+    __device__ __forceinline__ int next(const CasArgs& a, const TileHdr& h, const WaveArea& W) {
+        while (cw == 0) cw = word(a, h, W, ++k);
+        const int pos = 32 * k + __builtin_ctz(cw);
+        const int rank = pos - q - 1;
+        q = pos;
+        cw &= cw - 1u;
+        return rank;
+    }
+};
+
+// Cursor over set bits (kept positions) or clear bits (pruned positions) of the
+// tile's bitmap.
+template <bool ZEROS>
+struct BitCursor {
+    int k;
+    uint32_t cw;
+    __device__ __forceinline__ uint32_t word(const WaveArea& W, int i) const {
+        return ZEROS ? ~W.bw[i] : W.bw[i];
+    }
+    // position at the j0-th (from 0) set (or clear) bit
+    __device__ __forceinline__ void start(const WaveArea& W, int j0) {
+        int p = 0;
+#pragma unroll
+        for (int s = 32; s; s >>= 1) {
+            const int c = ZEROS ? 64 * (p + s) - int(W.bp[p + s]) : int(W.bp[p + s]);
+            if (c <= j0) p += s;
+        }
+        int r = j0 - (ZEROS ? 64 * p - int(W.bp[p]) : int(W.bp[p]));
+        uint32_t w = word(W, 2 * p);
+        k = 2 * p;
+        const int c = __popc(w);
+        if (r >= c) {
+            r -= c;
+            k = 2 * p + 1;
+            w = word(W, k);
+        }
+        cw = w & (~0u << select32(w, r));
+    }
+    __device__ __forceinline__ int next(const WaveArea& W) {
+        while (cw == 0) cw = word(W, ++k);
+        const int pos = 32 * k + __builtin_ctz(cw);
+        cw &= cw - 1u;
+        return pos;
+    }
+};
+
+// Nibble windows: the 5 words holding nibbles [n, n + 32) of a packed stream,
+// loaded early, then funnel-shifted so that nibble n + i sits at bits 4i.
+__device__ __forceinline__ void nib_load(const uint32_t* __restrict__ s, int64_t n, uint32_t (&raw)[5]) {
+    const uint32_t* p = s + (n >> 3);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) raw[i] = p[i];
+}
+
+__device__ __forceinline__ void nib_align(const uint32_t (&raw)[5], int64_t n, uint32_t (&win)[4]) {
+    const uint32_t sh = uint32_t(4 * (n & 7));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) win[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
+}
+
+// Walk kept values [j0, j0 + cnt) of the tile in kept order, GRP at a time:
+// sink.stage(u, rank, spec_nib, lo_nib) for each value of the group (u = its
+// slot), sink.skip(u) for slots past the lane's count, then sink.commit().  The
+// first nibble windows (nibble kp0 + j0) come preloaded.
+template <bool FAST, bool LO, class Sink>
+__device__ __forceinline__ void walk_kept(const CasArgs& a, const TileHdr& h, const WaveArea& W, int j0, int cnt,
+                                          const uint32_t (&sraw)[5], const uint32_t (&lraw)[5], Sink& sink) {
+    if (cnt <= 0) return;
+    UnaryCursor<FAST> uc;
+    uc.start(a, h, W, j0);
+    uint32_t sw[4], lw[4];
+    const int64_t n0 = h.kp0 + j0;
+    nib_align(sraw, n0, sw);
+    if constexpr (LO) nib_align(lraw, n0, lw);
+    for (int base = 0; base < cnt; base += NIB_CHUNK) {
+        if (base > 0) {
+            uint32_t r[5];
+            nib_load(a.spec_nib, n0 + base, r);
+            nib_align(r, n0 + base, sw);
+            if constexpr (LO) {
+                nib_load(a.lo_nib, n0 + base, r);
+                nib_align(r, n0 + base, lw);
+            }
+        }
+        const int rem = cnt - base;
+#pragma unroll
+        for (int g = 0; g < NIB_CHUNK / GRP; ++g) {
+            if (GRP * g < rem) {
+#pragma unroll
+                for (int u = 0; u < GRP; ++u) {
+                    const int i = GRP * g + u;
+                    if (i < rem) {
+                        const int rank = uc.next(a, h, W);
+                        sink.stage(u, rank, (sw[i / 8] >> (4 * (i % 8))) & 15u,
+                                   LO ? (lw[i / 8] >> (4 * (i % 8))) & 15u : 0u);
+                    } else {
+                        sink.skip(u);
+                    }
+                }
+                sink.commit();
+            }
+        }
+    }
+}
+
+// Even share of n items over the 64 lanes: [first, first + count).
+__device__ __forceinline__ void lane_share(int n, int lanes, int l, int& first, int& count) {
+    const int c = (n + lanes - 1) / lanes;
+    first = l * c;
+    count = max(0, min(c, n - first));
+}
+
+// Pruned values [p0, p0 + cnt) of the tile (raw bf16), PRU_CHUNK at a time:
+// emit(pos, value).  The first chunk's words come preloaded (pru_load at e0).
+constexpr int PRU_WORDS = PRU_CHUNK / 2 + 1;
+
+__device__ __forceinline__ void pru_load(const CasArgs& a, int64_t e, uint32_t (&raw)[PRU_WORDS]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.pruned) + (e >> 1);
+#pragma unroll
+    for (int i = 0; i < PRU_WORDS; ++i) raw[i] = src[i];
+}
+
+template <class Emit>
+__device__ __forceinline__ void walk_pruned(const CasArgs& a, const TileHdr& h, const WaveArea& W, int p0, int cnt,
+                                            const uint32_t (&raw0)[PRU_WORDS], Emit&& emit) {
+    if (cnt <= 0) return;
+    BitCursor<true> zc;
+    zc.start(W, p0);
+    const int64_t e0 = (h.f0 - h.kp0) + p0;          // pruned stream index of the first value
+    for (int base = 0; base < cnt; base += PRU_CHUNK) {
+        const int64_t e = e0 + base;
+        uint32_t raw[PRU_WORDS];
+        if (base == 0) {
+#pragma unroll
+            for (int i = 0; i < PRU_WORDS; ++i) raw[i] = raw0[i];
+        } else {
+            pru_load(a, e, raw);
+        }
+        const uint32_t sh = uint32_t(16 * (e & 1));
+        uint32_t v[PRU_CHUNK / 2];
+#pragma unroll
+        for (int i = 0; i < PRU_CHUNK / 2; ++i) v[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
+        const int rem = cnt - base;
+#pragma unroll
+        for (int i = 0; i < PRU_CHUNK; ++i) {
+            if (i < rem) {
+                const int pos = zc.next(W);
+                emit(pos, (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+            }
+        }
+    }
+}
+
+// bf16 bits of a kept value from its codebook exponent and nibbles.
+__device__ __forceinline__ uint32_t kept_bits(uint32_t E, uint32_t sn, uint32_t lo) {
+    return ((sn & 8u) << 12) | (E << 7) | ((sn & 7u) << 4) | lo;
+}
+
+// ------------------------------------------------------------------ sinks
+
+// Kept values scattered as bf16 bits into an LDS tile.
+struct ScatterSink {
+    BitCursor<false> kc;
+    const WaveArea* W;
+    const uint8_t* cb;
+    uint16_t* d;
+    int pos[GRP], rk[GRP];
+    uint32_t nib[GRP];
+    __device__ __forceinline__ void stage(int u, int rank, uint32_t sn, uint32_t lo) {
+        pos[u] = kc.next(*W);
+        rk[u] = min(rank, 255);
+        nib[u] = sn | (lo << 4);
+    }
+    __device__ __forceinline__ void skip(int u) {
+        pos[u] = -1;
+        rk[u] = 0;
+        nib[u] = 0;
+    }
+    __device__ __forceinline__ void commit() {
+        uint32_t E[GRP];
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) E[u] = cb[rk[u]];
+#pragma unroll
+        for (int u = 0; u < GRP; ++u)
+            if (pos[u] >= 0) d[pos[u]] = uint16_t(kept_bits(E[u], nib[u] & 15u, nib[u] >> 4));
+    }
+};
+
+// Kept values times activations (batch 1 or 2), into one accumulator per row, or,
+// when the tile meets two rows (SPLIT), kept index < jb into accA and the rest
+// into accB.  Slots past the lane's count read the LUT's zero entry.
+template <int BMAX, bool SPLIT>
+struct DotSink {
+    BitCursor<false> kc;
+    const WaveArea* W;
+    const float* lut;
+    const uint16_t* xs;
+    int K, colbase, nlast, zero, j, jb;
+    int idx[GRP], col[GRP];
+    bool inA[GRP];
+    float accA[BMAX], accB[BMAX];
+    __device__ __forceinline__ void stage(int u, int rank, uint32_t sn, uint32_t) {
+        // activation column: position in the tile relative to the start of its row
+        col[u] = colbase + kc.next(*W);
+        if constexpr (SPLIT) {
+            inA[u] = j < jb;
+            if (!inA[u]) col[u] -= K;
+        }
+        idx[u] = (min(rank, nlast) << 4) | int(sn);
+        ++j;
+    }
+    __device__ __forceinline__ void skip(int u) {
+        col[u] = 0;
+        idx[u] = zero;
+        if constexpr (SPLIT) inA[u] = true;
+        ++j;
+    }
+    __device__ __forceinline__ void commit() {
+        float w[GRP], xv[GRP][BMAX];
+#pragma unroll
+        for (int u = 0; u < GRP; ++u) {
+            w[u] = lut[idx[u]];
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) xv[u][b] = __uint_as_float(uint32_t(xs[b * K + col[u]]) << 16);
+        }
+#pragma unroll
+        for (int u = 0; u < GRP; ++u)
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                if constexpr (SPLIT) {
+                    const float pA = fmaf(w[u], xv[u][b], accA[b]), pB = fmaf(w[u], xv[u][b], accB[b]);
+                    accA[b] = inA[u] ? pA : accA[b];
+                    accB[b] = inA[u] ? accB[b] : pB;
+                } else {
+                    accA[b] = fmaf(w[u], xv[u][b], accA[b]);
+                }
+            }
+    }
+};
+
+// ------------------------------------------------------------------ dense decode
+
+constexpr int DD_WAVES = 4;
+
+// Restore (RESTORE) or draft decode of tile t into the LDS tile d.
+// The tile's global loads are issued before any of them is waited on (the first
+// pruned chunk too when PRE_PRUNED; otherwise it is loaded when reached).
+template <bool RESTORE, bool PRE_PRUNED = true>
+__device__ __forceinline__ void decode_tile_lds(const CasArgs& a, int64_t t, WaveArea& W, const uint8_t* cb,
+                                                uint16_t* d) {
+    const int lane = lane_id();
+    const TileHdr h = tile_hdr(a, t);
+    int j0, cnt, p0 = 0, pc = 0;
+    lane_share(h.nk, 64, lane, j0, cnt);
+    uint32_t sraw[5], lraw[5], praw[PRU_WORDS];
+    nib_load(a.spec_nib, h.kp0 + j0, sraw);
+    if constexpr (RESTORE) {
+        nib_load(a.lo_nib, h.kp0 + j0, lraw);
+        lane_share(h.tl - h.nk, 64, lane, p0, pc);
+        if constexpr (PRE_PRUNED) pru_load(a, (h.f0 - h.kp0) + p0, praw);
+    }
+    stage_tile(a, h, t, W);
+    ScatterSink sk;
+    sk.W = &W;
+    sk.cb = cb;
+    sk.d = d;
+    if (cnt > 0) sk.kc.start(W, j0);
+    if (h.nuw <= STAGE_UW) walk_kept<true, RESTORE>(a, h, W, j0, cnt, sraw, lraw, sk);
+    else walk_kept<false, RESTORE>(a, h, W, j0, cnt, sraw, lraw, sk);
+    if constexpr (RESTORE) {
+        if constexpr (!PRE_PRUNED) pru_load(a, (h.f0 - h.kp0) + p0, praw);
+        walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
+    }
+}
+
+// One wave per tile: kept values (and, when restoring, pruned values) are
+// scattered into the wave's LDS tile, which is then written out 16 bytes a lane.
+template <bool RESTORE>
+__global__ __launch_bounds__(64 * DD_WAVES) void decode_dense_kernel(CasArgs a, uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint16_t dense[DD_WAVES][TILE];
+    __shared__ WaveArea areas[DD_WAVES];
+    __shared__ uint8_t cb[256];
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) cb[i] = i < a.n_sym ? a.codebook[i] : 0;
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * DD_WAVES + wave);
+    if (t >= a.T) return;
+    uint16_t* d = dense[wave];
+    if constexpr (!RESTORE) {
+        uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+    }
+    decode_tile_lds<RESTORE>(a, t, areas[wave], cb, d);
+    wave_sync_lds();
+    const int tl = int(min<int64_t>(TILE, a.N - t * TILE));
+    uint4* o = reinterpret_cast<uint4*>(out + t * TILE);
+    for (int g = lane; g < tl / 8; g += 64) o[g] = *reinterpret_cast<const uint4*>(d + 8 * g);
+}
+
+// ------------------------------------------------------------------ draft GEMV (kept domain)
+
+// Block = R consecutive rows, NW waves taking the overlapping tiles round robin.
+// Needs K >= 4096 (a tile meets at most two rows).  Lanes share the tile's kept
+// values evenly; a lane whose values straddle the row boundary keeps two sums.
+// The two row sums are reduced across the wave and added to the wave's own
+// partial row sums in LDS, which are summed in wave order at the end.
+template <int BMAX>
+__global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const uint16_t* __restrict__ x, int B,
+                                                              float* __restrict__ y, int R) {
+    extern __shared__ __attribute__((aligned(16))) uint4 sl4[];
+    const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = lane_id();
+    const int K = int(a.K);
+    const int nsym = max(1, a.n_sym), nlut = nsym * 16;                  // entry nlut holds 0.0
+    uint16_t* xs = reinterpret_cast<uint16_t*>(sl4);                     // [BMAX][K]
+    WaveArea* areas = reinterpret_cast<WaveArea*>(xs + BMAX * K);        // [nw]
+    float* red = reinterpret_cast<float*>(areas + nw);                   // [nw][R][BMAX]
+    float* lutf = red + nw * R * BMAX;                                   // [nsym][16] + zero
+    for (int i = threadIdx.x; i <= nlut; i += blockDim.x) {
+        const int rank = i >> 4;
+        const uint32_t E = rank < a.n_sym ? a.codebook[rank] : 0u;
+        lutf[i] = i == nlut ? 0.f : __uint_as_float(kept_bits(E, uint32_t(i & 15), 0u) << 16);
+    }
+    for (int i = threadIdx.x; i < B * K / 8; i += blockDim.x)
+        reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    for (int i = threadIdx.x; i < nw * R * BMAX; i += blockDim.x) red[i] = 0.f;
+    __syncthreads();
+    const int64_t r0 = int64_t(blockIdx.x) * R, r1 = min<int64_t>(a.M, r0 + R);
+    const int64_t t_a = (r0 * K) / TILE, t_b = (r1 * K - 1) / TILE;
+    WaveArea& W = areas[wave];
+    float* wred = red + wave * R * BMAX;
+    for (int64_t t = t_a + wave; t <= t_b; t += nw) {
+        const TileHdr h = tile_hdr(a, t);
+        int j0, cnt;
+        lane_share(h.nk, 64, lane, j0, cnt);
+        uint32_t sraw[5];
+        nib_load(a.spec_nib, h.kp0 + j0, sraw);
+        stage_tile(a, h, t, W);
+        const int64_t row_a = h.f0 / K;
+        const int bnd = int(min<int64_t>(h.tl, (row_a + 1) * K - h.f0));   // first position of the next row
+        int jb = h.nk;                                                      // kept values before bnd
+        if (bnd < h.tl) {
+            const int p = bnd >> 6, rem = bnd & 63;
+            const uint32_t lo = W.bw[2 * p], hi = W.bw[2 * p + 1];
+            jb = int(W.bp[p]) + (rem >= 32 ? __popc(lo) + __popc(hi & ((1u << (rem - 32)) - 1u))
+                                            : __popc(lo & ((1u << rem) - 1u)));
+        }
+        float vA[BMAX], vB[BMAX];
+        auto run = [&](auto split) {
+            constexpr bool SPLIT = decltype(split)::value;
+            DotSink<BMAX, SPLIT> sk;
+            sk.W = &W;
+            sk.lut = lutf;
+            sk.xs = xs;
+            sk.K = K;
+            sk.colbase = int(h.f0 - row_a * K);
+            sk.nlast = nsym - 1;
+            sk.zero = nlut;
+            sk.j = j0;
+            sk.jb = jb;
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) sk.accA[b] = sk.accB[b] = 0.f;
+            if (cnt > 0) sk.kc.start(W, j0);
+            uint32_t none[5];
+            if (h.nuw <= STAGE_UW) walk_kept<true, false>(a, h, W, j0, cnt, sraw, none, sk);
+            else walk_kept<false, false>(a, h, W, j0, cnt, sraw, none, sk);
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                vA[b] = sk.accA[b];
+                vB[b] = SPLIT ? sk.accB[b] : 0.f;
+            }
+        };
+        if (bnd < h.tl) run(std::true_type{});
+        else run(std::false_type{});
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                vA[b] += __shfl_xor(vA[b], off, 64);
+                vB[b] += __shfl_xor(vB[b], off, 64);
+            }
+            if (lane == 0) {
+                if (row_a >= r0 && row_a < r1) wred[int(row_a - r0) * BMAX + b] += vA[b];
+                if (bnd < h.tl && row_a + 1 >= r0 && row_a + 1 < r1) wred[int(row_a + 1 - r0) * BMAX + b] += vB[b];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * BMAX; i += blockDim.x) {
+        const int r = i / BMAX, b = i - r * BMAX;
+        if (b < B && r0 + r < r1) {
+            float s = 0.f;
+            for (int w = 0; w < nw; ++w) s += red[(w * R + r) * BMAX + b];
+            y[int64_t(b) * a.M + r0 + r] = s;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ verify GEMM (fused restore + MFMA)
 
-// Block = 16 rows x all K (K % 4096 == 0), 8 waves.  Per 4096-column slab each
-// wave restores two of the 16 row tiles into LDS, then the waves split the slab's
-// 128 MFMA k-steps; partial 16x16 tiles are summed across waves at the end.
-constexpr int VG_WAVES = 8;
+// Block = 16 rows x all K (K % 4096 == 0), one wave per row.  Per 4096-column
+// slab each wave restores its row's tile straight into the block's LDS rows
+// (kept and pruned values scattered to their positions), then the 16 waves split
+// the slab's 128 MFMA k-steps; the waves' partial 16x16 tiles are summed at the end.
+constexpr int VG_WAVES = 16;
+constexpr int VROW = 4104;   // u16 per LDS row: 2052 dwords, 4 (mod 32) banks apart
 
-__global__ __launch_bounds__(512) void verify_gemm_kernel(CasArgs a, const uint16_t* __restrict__ x, int B,
-                                                          float* __restrict__ y) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t vlds[];
-    uint16_t* rows = vlds;                                              // [16][ROW_STRIDE]
-    uint8_t* cb = reinterpret_cast<uint8_t*>(vlds + 16 * ROW_STRIDE);  // [256]
-    float* red = reinterpret_cast<float*>(cb + 256);                    // [VG_WAVES][64][4]
+__global__ __launch_bounds__(64 * VG_WAVES) void verify_gemm_kernel(CasArgs a, const uint16_t* __restrict__ x, int B,
+                                                                   float* __restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) uint4 vl4[];
+    uint16_t* rows = reinterpret_cast<uint16_t*>(vl4);                        // [16][VROW]
+    WaveArea* areas = reinterpret_cast<WaveArea*>(rows + 16 * VROW);          // [VG_WAVES]
+    uint8_t* cb = reinterpret_cast<uint8_t*>(areas + VG_WAVES);               // [256]
     for (int i = threadIdx.x; i < 256; i += blockDim.x) cb[i] = i < a.n_sym ? a.codebook[i] : 0;
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = lane_id();
     const int64_t K = a.K, tpr = K / TILE;
-    const int64_t r0 = int64_t(blockIdx.x) * 16;
+    const int64_t r0 = int64_t(blockIdx.x) * 16, row = r0 + wave;
     const int n = lane & 15, kq = lane >> 4;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int64_t kt = 0; kt < tpr; ++kt) {
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int r = wave * 2 + rr;
-            uint16_t* buf = rows + r * ROW_STRIDE;
-            const int64_t row = r0 + r;
-            uint32_t pairs[32];
-            if (row < a.M) {
-                decode_tile<true>(a, row * tpr + kt, TILE, buf, cb, pairs);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 32; ++i) pairs[i] = 0u;
-            }
-            wave_sync_lds();
-            uint4* dst = reinterpret_cast<uint4*>(buf + 64 * lane);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = make_uint4(pairs[4 * i], pairs[4 * i + 1], pairs[4 * i + 2], pairs[4 * i + 3]);
-        }
-        __syncthreads();
-        // this wave's 16 k-steps of 32 columns
+        // this wave's activations for its 8 k-steps, loaded ahead of the decode
+        uint4 bv[8];
         const uint16_t* xrow = x + int64_t(n) * K + kt * TILE;
-        const bool xv = n < B;
-#pragma unroll 4
-        for (int s = 0; s < 16; ++s) {
-            const int k = (wave * 16 + s) * 32 + kq * 8;
-            const uint4 av = *reinterpret_cast<const uint4*>(rows + n * ROW_STRIDE + k);
-            uint4 bv = make_uint4(0, 0, 0, 0);
-            if (xv) bv = *reinterpret_cast<const uint4*>(xrow + k);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int k = (wave * 8 + s) * 32 + kq * 8;
+            bv[s] = n < B ? *reinterpret_cast<const uint4*>(xrow + k) : make_uint4(0, 0, 0, 0);
+        }
+        // rows past M are not decoded: the outputs they feed are never stored
+        if (row < a.M) decode_tile_lds<true, false>(a, row * tpr + kt, areas[wave], cb, rows + wave * VROW);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int k = (wave * 8 + s) * 32 + kq * 8;
+            const uint4 av = *reinterpret_cast<const uint4*>(rows + n * VROW + k);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                          __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+                                                          __builtin_bit_cast(bf16x8_t, bv[s]), acc, 0, 0, 0);
         }
         __syncthreads();
     }
     // C[row = 4*kq + j][col = n] of this wave's partial
+    float* red = reinterpret_cast<float*>(vl4);
     float* rw = red + (wave * 64 + lane) * 4;
     rw[0] = acc[0]; rw[1] = acc[1]; rw[2] = acc[2]; rw[3] = acc[3];
     __syncthreads();
@@ -367,8 +880,8 @@ __global__ __launch_bounds__(512) void verify_gemm_kernel(CasArgs a, const uint1
             for (int j = 0; j < 4; ++j) s[j] += red[(w * 64 + lane) * 4 + j];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t row = r0 + 4 * kq + j;
-            if (n < B && row < a.M) y[int64_t(n) * a.M + row] = s[j];
+            const int64_t r = r0 + 4 * kq + j;
+            if (n < B && r < a.M) y[int64_t(n) * a.M + r] = s[j];
         }
     }
 }
@@ -484,7 +997,8 @@ mbd_status cas_args(const mbd_dweights* w, bool need_verify, CasArgs* a) {
     if (!w) return fail(MBD_EINVAL, "NULL descriptor");
     if (w->fmt != MBD_CASSANDRA) return fail(MBD_EINVAL, "descriptor is not MBD_CASSANDRA");
     if (w->M < 0 || w->K < 128 || w->K % 128) return fail(MBD_ESHAPE, "Cassandra needs K a positive multiple of 128");
-    if (w->n_sym < 1 || w->n_sym > 256) return fail(MBD_EINVAL, "n_sym=%d outside [1, 256]", w->n_sym);
+    if (w->n_sym < 0 || w->n_sym > 256) return fail(MBD_EINVAL, "n_sym=%d outside [0, 256]", w->n_sym);
+    if (w->n_sym == 0 && w->M > 0 && w->n_kept > 0) return fail(MBD_EINVAL, "n_sym=0 with kept values");
     const int last = need_verify ? 8 : 6;
     for (int i = 0; i < last; ++i) {
         if (!w->sec[i]) return fail(MBD_EINVAL, "section %d is NULL", i);
@@ -506,6 +1020,16 @@ mbd_status cas_args(const mbd_dweights* w, bool need_verify, CasArgs* a) {
     return MBD_OK;
 }
 
+// Raise a kernel's dynamic LDS limit once per process (idempotent, so a race
+// between first calls only repeats the call).
+mbd_status lds_limit(const void* kern, std::atomic<int>& done, size_t bytes, const char* what) {
+    if (done.load(std::memory_order_acquire) >= int(bytes)) return MBD_OK;
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes)) != hipSuccess)
+        return fail(MBD_EHIP, "cannot raise the %s LDS limit to %zu bytes", what, bytes);
+    done.store(int(bytes), std::memory_order_release);
+    return MBD_OK;
+}
+
 int round_batch(int B) {
     int b = 1;
     while (b < B) b <<= 1;
@@ -519,7 +1043,7 @@ mbd_status decode_dense(const mbd_dweights* w, uint16_t* out, hipStream_t st, bo
     if (!out) return fail(MBD_EINVAL, "output is NULL");
     if (!aligned(out, 16)) return fail(MBD_EALIGN, "output must be 16-byte aligned");
     if (a.N == 0) return MBD_OK;
-    const unsigned blocks = unsigned((a.T + 3) / 4);
+    const unsigned blocks = unsigned((a.T + DD_WAVES - 1) / DD_WAVES);
     if (restore)
         hipLaunchKernelGGL(decode_dense_kernel<true>, dim3(blocks), dim3(256), 0, st, a, out);
     else
@@ -535,14 +1059,10 @@ mbd_status mbd_gemv_cassandra(const mbd_dweights* w, const uint16_t* x, int32_t 
     if (s != MBD_OK) return s;
     if (a.K % TILE) return fail(MBD_ESHAPE, "the fused verify GEMM needs K %% 4096 == 0 (K=%lld)", (long long)a.K);
     if (a.M == 0) return MBD_OK;
-    const size_t lds = size_t(16) * ROW_STRIDE * 2 + 256 + size_t(VG_WAVES) * 64 * 4 * 4;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(verify_gemm_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
-            return fail(MBD_EHIP, "cannot raise the verify GEMM LDS limit to %zu bytes", lds);
-        attr_set = true;
-    }
+    const size_t lds = size_t(16) * VROW * 2 + size_t(VG_WAVES) * sizeof(WaveArea) + 256;
+    static std::atomic<int> lds_done{0};
+    if ((s = lds_limit(reinterpret_cast<const void*>(verify_gemm_kernel), lds_done, lds, "verify GEMM")) != MBD_OK)
+        return s;
     const unsigned blocks = unsigned((a.M + 15) / 16);
     hipLaunchKernelGGL(verify_gemm_kernel, dim3(blocks), dim3(64 * VG_WAVES), lds, st, a, x, B, y);
     return hip_check("verify GEMM launch");
@@ -593,10 +1113,27 @@ mbd_status mbd_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, fl
     if (!aligned(x, 16) || !aligned(y, 4)) return fail(MBD_EALIGN, "x must be 16-byte and y 4-byte aligned");
     if (a.M == 0) return MBD_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int bmax = round_batch(B);
+    // kept-domain kernel: K >= 4096 (a tile meets at most two rows), batch <= 2,
+    // activations staged in LDS
+    constexpr int KW = 16, KR = 16;
+    const size_t kl = size_t(bmax) * a.K * 2 + KW * sizeof(WaveArea) + size_t(KW) * KR * bmax * 4 +
+                      (size_t(std::max(1, a.n_sym)) * 16 + 1) * 4;
+    if (a.K >= TILE && bmax <= 2 && kl <= 160 * 1024) {
+        static std::atomic<int> done1{0}, done2{0};
+        const void* kern = bmax == 1 ? reinterpret_cast<const void*>(spec_gemv_kept_kernel<1>)
+                                     : reinterpret_cast<const void*>(spec_gemv_kept_kernel<2>);
+        if ((s = lds_limit(kern, bmax == 1 ? done1 : done2, kl, "draft GEMV")) != MBD_OK) return s;
+        const unsigned blocks = unsigned((a.M + KR - 1) / KR);
+        if (bmax == 1)
+            hipLaunchKernelGGL(spec_gemv_kept_kernel<1>, dim3(blocks), dim3(64 * KW), kl, st, a, x, B, y, KR);
+        else
+            hipLaunchKernelGGL(spec_gemv_kept_kernel<2>, dim3(blocks), dim3(64 * KW), kl, st, a, x, B, y, KR);
+        return hip_check("spec GEMV launch");
+    }
     // rows per block: smallest R in {1, 2, 4} whose flat range is whole tiles
     int R = 1;
     if ((a.K % TILE) != 0) R = ((2 * a.K) % TILE == 0) ? 2 : 4;
-    const int bmax = round_batch(B);
     if (bmax > 4 && R > 2) R = 2;
     const int64_t fa_tiles = (int64_t(R) * a.K + TILE - 1) / TILE + 1;
     const int nw = int(std::min<int64_t>(4, fa_tiles));

@@ -129,7 +129,10 @@ def test_gemv_argument_errors(L):
 
 def test_cassandra_and_moe_argument_errors(L):
     d = _desc(mbd.MBD_CASSANDRA, 16, 256, n_sym=0)
-    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL      # n_sym 0
+    d.n_kept = 5
+    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL      # kept values, no codebook
+    d.n_sym = 300
+    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL
     d.n_sym = 12
     d.sec[2] = None
     assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL

@@ -235,10 +235,45 @@ def test_moe_ragged(dev, case):
 
 # ------------------------------------------------------------ Cassandra
 
-def _cas(dev, w, norms, only=None):
+def _cas(dev, w, norms, only=None, keep=(3, 10)):
     mbd = _mbd()
-    p = mbd.mbd_pack(mbd.MBD_CASSANDRA, w, norms)
+    p = mbd.mbd_pack(mbd.MBD_CASSANDRA, w, norms, *keep)
     return p, mbd.to_device(p, dev, only=only)
+
+
+def _check_cassandra(dev, w, norms, keep, batches, verify_batches):
+    """Restore, draft decode, draft GEMV and (K % 4096 == 0) verify GEMM against the oracle."""
+    mbd = _mbd()
+    M, K = w.shape
+    sec = cassandra.pack(w, norms, *keep)
+    _, cw = _cas(dev, w, norms, keep=keep)
+    out = torch.empty((M, K), dtype=torch.int16, device=dev)
+    mbd.mbd_verify_restore(cw, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), w)
+    _, sw = _cas(dev, w, norms, only=mbd.SPEC_SECTIONS, keep=keep)
+    mbd.mbd_spec_decode(sw, out)
+    torch.cuda.synchronize()
+    spec = cassandra.spec_decode(sec, M, K)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), spec)
+    for B in batches:
+        x = _rand_x(B, B, K)
+        y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+        mbd.mbd_spec_gemv(sw, _x_dev(x, dev), y)
+        torch.cuda.synchronize()
+        ref = gemv.gemv(bits.bf16_value(spec), x)
+        got = y.cpu().numpy()
+        if not ref.any():
+            assert not got.any()
+        else:
+            assert gemv.rel_l2(got, ref) <= TOL, B
+    if K % 4096 == 0:
+        for B in verify_batches:
+            x = _rand_x(B + 50, B, K)
+            y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+            mbd.mbd_gemv(cw, _x_dev(x, dev), y)
+            torch.cuda.synchronize()
+            assert gemv.rel_l2(y.cpu().numpy(), gemv.gemv(bits.bf16_value(w), x)) <= TOL, B
 
 
 CAS_SHAPES = [(1, 4096), (2, 1536), (5, 1000 - 1000 % 128 + 128), (3, 14336), (7, 8192), (33, 384)]
@@ -262,13 +297,43 @@ def test_cassandra_decode_ragged(dev, M, K):
     torch.cuda.synchronize()
     spec = cassandra.spec_decode(sec, M, K)
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), spec)
-    for B in (1, 3, 16):
+    for B in (1, 2, 3, 16):
         x = _rand_x(B, B, K)
         y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
         mbd.mbd_spec_gemv(sw, _x_dev(x, dev), y)
         torch.cuda.synchronize()
         ref = gemv.gemv(bits.bf16_value(spec), x)
         assert gemv.rel_l2(y.cpu().numpy(), ref) <= TOL
+    if K % 4096 == 0:
+        for B in (1, 7):
+            x = _rand_x(B + 9, B, K)
+            y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
+            mbd.mbd_gemv(cw, _x_dev(x, dev), y)
+            torch.cuda.synchronize()
+            assert gemv.rel_l2(y.cpu().numpy(), gemv.gemv(bits.bf16_value(w), x)) <= TOL
+
+
+@pytest.mark.parametrize("M,K,keep", [(4, 4096, (1, 1)), (3, 8192, (0, 1)), (5, 12288, (1, 2)), (17, 4096, (3, 10)),
+                                      (2, 4096 + 1024, (9, 10))])
+def test_cassandra_keep_fractions(dev, M, K, keep):
+    print("case cassandra keep", M, K, keep, flush=True)
+    w = _rand_w(M * 7 + K, M, K)
+    norms = np.random.default_rng(K).lognormal(0, 1, K).astype(np.float32)
+    _check_cassandra(dev, w, norms, keep, (1, 2, 3), (1, 5, 16))
+
+
+@pytest.mark.parametrize("keep", [(3, 10), (1, 1)])
+def test_cassandra_long_codes(dev, keep):
+    """Exponents spread evenly over 120 values: codewords average ~60 bits, so every
+    tile's unary stream is far longer than the words staged per wave."""
+    print("case cassandra long codes", keep, flush=True)
+    rng = np.random.default_rng(11)
+    M, K = 3, 8192
+    e = rng.integers(-70, 50, (M, K))
+    v = np.ldexp(1.0 + rng.integers(0, 128, (M, K)) / 128.0, e) * rng.choice([-1.0, 1.0], (M, K))
+    w = synth.f32_to_bf16_bits(v.astype(np.float32))
+    norms = rng.lognormal(0, 1, K).astype(np.float32)
+    _check_cassandra(dev, w, norms, keep, (1, 2), (1, 16))
 
 
 @pytest.fixture(scope="module")
