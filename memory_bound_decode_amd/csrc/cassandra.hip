@@ -585,6 +585,100 @@ __device__ __forceinline__ uint32_t kept_bits(uint32_t E, uint32_t sn, uint32_t 
     return ((sn & 8u) << 12) | (E << 7) | ((sn & 7u) << 4) | lo;
 }
 
+// ---- software pipeline: a tile's global loads are issued one tile ahead.
+
+// Tile-table entries of up to 64 tiles, lane i holding those of the i-th.
+struct HdrVec {
+    uint32_t kp0, kp1;
+    uint64_t bo0, bo1;
+};
+
+__device__ __forceinline__ HdrVec hdr_load(const CasArgs& a, int64_t t) {
+    HdrVec v;
+    v.kp0 = a.kprefix[t];
+    v.kp1 = a.kprefix[t + 1];
+    v.bo0 = a.bitoff[t];
+    v.bo1 = a.bitoff[t + 1];
+    return v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int i) {
+    const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), i);
+    const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(v >> 32), i);
+    return (uint64_t(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ TileHdr hdr_get(const CasArgs& a, const HdrVec& v, int i, int64_t t) {
+    TileHdr h;
+    h.f0 = t * TILE;
+    h.tl = int(min<int64_t>(TILE, a.N - h.f0));
+    h.kp0 = __builtin_amdgcn_readlane(v.kp0, i);
+    h.nk = int(__builtin_amdgcn_readlane(v.kp1, i) - uint32_t(h.kp0));
+    h.bo0 = int64_t(readlane64(v.bo0, i));
+    h.bo1 = int64_t(readlane64(v.bo1, i));
+    h.ws = h.bo0 >> 5;
+    h.nuw = int(((h.bo1 + 31) >> 5) - h.ws);
+    return h;
+}
+
+// A tile's header and the raw words its lanes need first.  Every load is
+// unconditional (indices clamped), so the number in flight is static.
+struct TileWords {
+    TileHdr h;
+    int64_t t;
+    int j0, cnt;
+    uint32_t u0, u1, b0, b1;
+    uint32_t sraw[5];
+};
+
+__device__ __forceinline__ void tile_issue(const CasArgs& a, const TileHdr& h, int64_t t, TileWords& tw) {
+    const int lane = lane_id();
+    tw.h = h;
+    tw.t = t;
+    lane_share(h.nk, 64, lane, tw.j0, tw.cnt);
+    nib_load(a.spec_nib, h.kp0 + tw.j0, tw.sraw);
+    const int64_t ulast = max<int64_t>(0, h.ws + h.nuw - 1);
+    tw.u0 = a.unary[min<int64_t>(h.ws + lane, ulast)];
+    tw.u1 = a.unary[min<int64_t>(h.ws + 64 + lane, ulast)];
+    const int64_t nwords = (a.N + 31) >> 5;
+    const int64_t wi = t * (TILE / 32) + 2 * lane;
+    tw.b0 = a.bitmap[min<int64_t>(wi, nwords - 1)];
+    tw.b1 = a.bitmap[min<int64_t>(wi + 1, nwords - 1)];
+}
+
+// stage_tile from words loaded by tile_issue.
+__device__ __forceinline__ void tile_stage(const CasArgs& a, const TileWords& tw, WaveArea& W) {
+    const int lane = lane_id();
+    const TileHdr& h = tw.h;
+    if (h.nuw <= STAGE_UW) {
+        auto mask = [&](uint32_t v, int k) {
+            const int64_t b0 = (h.ws + k) * 32;
+            if (b0 < h.bo0) v &= ~0u << int(h.bo0 - b0);
+            const int64_t lim = h.bo1 - b0;
+            if (lim < 32) v &= lim <= 0 ? 0u : ((1u << int(lim)) - 1u);
+            return v;
+        };
+        const uint32_t u0 = lane < h.nuw ? mask(tw.u0, lane) : 0u;
+        const uint32_t u1 = lane + 64 < h.nuw ? mask(tw.u1, lane + 64) : 0u;
+        const int c0 = __popc(u0), c1 = __popc(u1);
+        const int inc = wave_incl_add(c0 | (c1 << 16));
+        const int tot0 = __shfl(inc, 63, 64) & 0xFFFF;
+        W.uw[lane] = u0;
+        W.uw[lane + 64] = u1;
+        W.up[lane] = uint16_t((inc & 0xFFFF) - c0);
+        W.up[lane + 64] = uint16_t(tot0 + (inc >> 16) - c1);
+    }
+    const int64_t wi = tw.t * (TILE / 32) + 2 * lane;
+    const int64_t nwords = (a.N + 31) >> 5;
+    const uint32_t b0 = wi < nwords ? tw.b0 : 0u;
+    const uint32_t b1 = wi + 1 < nwords ? tw.b1 : 0u;
+    W.bw[2 * lane] = b0;
+    W.bw[2 * lane + 1] = b1;
+    const int pc = __popc(b0) + __popc(b1);
+    W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+    wave_sync_lds();
+}
+
 // ------------------------------------------------------------------ sinks
 
 // Kept values scattered as bf16 bits into an LDS tile.
@@ -738,7 +832,8 @@ template <int BMAX>
 __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const uint16_t* __restrict__ x, int B,
                                                               float* __restrict__ y, int R) {
     extern __shared__ __attribute__((aligned(16))) uint4 sl4[];
-    const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = lane_id();
+    const int nw = blockDim.x >> 6, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int K = int(a.K);
     const int nsym = max(1, a.n_sym), nlut = nsym * 16;                  // entry nlut holds 0.0
     uint16_t* xs = reinterpret_cast<uint16_t*>(sl4);                     // [BMAX][K]
@@ -758,13 +853,21 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
     const int64_t t_a = (r0 * K) / TILE, t_b = (r1 * K - 1) / TILE;
     WaveArea& W = areas[wave];
     float* wred = red + wave * R * BMAX;
-    for (int64_t t = t_a + wave; t <= t_b; t += nw) {
-        const TileHdr h = tile_hdr(a, t);
-        int j0, cnt;
-        lane_share(h.nk, 64, lane, j0, cnt);
-        uint32_t sraw[5];
-        nib_load(a.spec_nib, h.kp0 + j0, sraw);
-        stage_tile(a, h, t, W);
+    const int64_t tw0 = t_a + wave;
+    const int ntiles = t_b >= tw0 ? int((t_b - tw0) / nw) + 1 : 0;
+    HdrVec hv;
+    // loads of tile i (clamped to the last tile) into dst
+    // (tile-table entries of the wave's first 64 tiles sit in hv; later ones, only
+    // for rows longer than 64 * 16 tiles, come through scalar loads)
+    auto issue_at = [&](int i, TileWords& dst) {
+        i = min(i, ntiles - 1);
+        const int64_t tn = tw0 + int64_t(i) * nw;
+        tile_issue(a, i < 64 ? hdr_get(a, hv, i, tn) : tile_hdr(a, tn), tn, dst);
+    };
+    auto process = [&](const TileWords& cur) {
+        const TileHdr h = cur.h;
+        const int j0 = cur.j0, cnt = cur.cnt;
+        tile_stage(a, cur, W);
         const int64_t row_a = h.f0 / K;
         const int bnd = int(min<int64_t>(h.tl, (row_a + 1) * K - h.f0));   // first position of the next row
         int jb = h.nk;                                                      // kept values before bnd
@@ -791,8 +894,8 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
             for (int b = 0; b < BMAX; ++b) sk.accA[b] = sk.accB[b] = 0.f;
             if (cnt > 0) sk.kc.start(W, j0);
             uint32_t none[5];
-            if (h.nuw <= STAGE_UW) walk_kept<true, false>(a, h, W, j0, cnt, sraw, none, sk);
-            else walk_kept<false, false>(a, h, W, j0, cnt, sraw, none, sk);
+            if (h.nuw <= STAGE_UW) walk_kept<true, false>(a, h, W, j0, cnt, cur.sraw, none, sk);
+            else walk_kept<false, false>(a, h, W, j0, cnt, cur.sraw, none, sk);
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 vA[b] = sk.accA[b];
@@ -813,6 +916,18 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
                 if (bnd < h.tl && row_a + 1 >= r0 && row_a + 1 < r1) wred[int(row_a + 1 - r0) * BMAX + b] += vB[b];
             }
         }
+    };
+    // two tile buffers, so a buffer is never copied while its loads are in flight
+    TileWords ta, tb;
+    if (ntiles > 0) {
+        hv = hdr_load(a, tw0 + int64_t(min(lane, ntiles - 1)) * nw);
+        issue_at(0, ta);
+    }
+    for (int it = 0; it < ntiles; it += 2) {
+        issue_at(it + 1, tb);
+        process(ta);
+        issue_at(it + 2, ta);
+        if (it + 1 < ntiles) process(tb);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < R * BMAX; i += blockDim.x) {
@@ -895,56 +1010,117 @@ struct MxArgs {
     int64_t M, K;
 };
 
-// Eight MX elements (one lane's MFMA operand) -> bf16x8: mag * 2^(X-134), sign.
-__device__ __forceinline__ uint4 mx_to_bf16x8(uint2 m8, uint32_t X, uint32_t sgn8) {
+// Eight MX elements (bytes of m8, sign bits sgn8 bit i = element i) -> bf16x8
+// holding (-1)^s * mag * 2^(X-134): the product of an 8-bit integer and a power of
+// two is exact in fp32 and keeps at most 8 significant bits, so its top 16 bits
+// are the exact bf16.
+__device__ __forceinline__ uint4 mx_to_bf16x8(uint2 m8, float scale, uint32_t sgn8) {
     uint32_t out[4];
     const uint32_t mw[2] = {m8.x, m8.y};
-    const int ex = int(X) - 134;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t w = mw[i >> 1];
         const int b0 = (i & 1) * 2;
-        const float f0 = __builtin_ldexpf(float((w >> (8 * b0)) & 0xFFu), ex);
-        const float f1 = __builtin_ldexpf(float((w >> (8 * (b0 + 1))) & 0xFFu), ex);
-        uint32_t v = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-        v |= ((sgn8 >> (2 * i)) & 1u) << 15;
-        v |= ((sgn8 >> (2 * i + 1)) & 1u) << 31;
-        out[i] = v;
+        const float f0 = float((w >> (8 * b0)) & 0xFFu) * scale;
+        const float f1 = float((w >> (8 * (b0 + 1))) & 0xFFu) * scale;
+        // sign bits 2i, 2i+1 -> bits 15, 31 of the packed pair
+        const uint32_t s2 = (sgn8 >> (2 * i)) & 3u;
+        const uint32_t sm = ((s2 << 15) | (s2 << 30)) & 0x80008000u;
+        out[i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u) | sm;
     }
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-// Block = 16 rows, 4 waves splitting K in 32-column steps; MFMA bf16 16x16x32.
-__global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs a, const uint16_t* __restrict__ x, int B,
-                                                      float* __restrict__ y) {
-    __shared__ float red[4][64][4];
-    const int wave = threadIdx.x >> 6, lane = lane_id();
-    const int n = lane & 15, kq = lane >> 4;
-    const int64_t r0 = int64_t(blockIdx.x) * 16;
-    const int64_t row = min<int64_t>(r0 + n, a.M - 1);
-    const int64_t G = a.K / 32, steps = G;
-    const bool xv = n < B;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* xrow = x + int64_t(n) * a.K;
-    for (int64_t s = wave; s < steps; s += 4) {
-        const int64_t g = row * G + s;
-        const uint32_t X = a.exp[g];
-        const uint32_t sg = (a.sign[g] >> (8 * kq)) & 0xFFu;
-        const uint2 m8 = *reinterpret_cast<const uint2*>(a.mag + row * a.K + s * 32 + kq * 8);
-        const uint4 av = mx_to_bf16x8(m8, X, sg);
-        uint4 bv = make_uint4(0, 0, 0, 0);
-        if (xv) bv = *reinterpret_cast<const uint4*>(xrow + s * 32 + kq * 8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
-                                                      acc, 0, 0, 0);
+// Block = 32 rows (two 16-row MFMA tiles) x all K.  K is walked in 128-column
+// chunks, chunk c by wave c % MX_WAVES.  In a chunk, lane (n, q) = (lane % 16,
+// lane / 16) holds the 32-element MX group q of row n of each tile (32 bytes of
+// magnitudes, its exponent and sign word) and the same 32 activation columns of
+// batch row n; the MFMA k slots of sub-step s take the group's elements
+// 8s..8s+7, the same columns on both operands.  The next chunk's loads are issued
+// before the current chunk is computed.  Partial tiles are summed across the
+// waves at the end.
+constexpr int MX_WAVES = 16;
+
+struct MxChunk {
+    uint4 ma0, ma1, mb0, mb1;   // magnitudes, tiles A and B
+    uint32_t ea, eb, sa, sb;    // exponents, sign words
+    uint4 xv[4];                // activations
+};
+
+__global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const uint16_t* __restrict__ x, int B,
+                                                               float* __restrict__ y) {
+    __shared__ float red[MX_WAVES][2][64][4];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n = lane & 15, q = lane >> 4;
+    const int64_t K = a.K, G = K / 32;
+    const int64_t r0 = int64_t(blockIdx.x) * 32;
+    const int64_t rA = min<int64_t>(r0 + n, a.M - 1), rB = min<int64_t>(r0 + 16 + n, a.M - 1);
+    const int nchunks = int((K + 127) / 128);
+    const bool xv_ok = n < B;
+    const uint16_t* xrow = x + int64_t(xv_ok ? n : 0) * K;
+    auto load = [&](int c, MxChunk& d) {
+        // the group's columns; a chunk past K (only when K % 128 != 0) reloads group 0
+        int64_t g = int64_t(c) * 4 + q;
+        if (g >= G) g = 0;
+        const uint4* pa = reinterpret_cast<const uint4*>(a.mag + rA * K + g * 32);
+        const uint4* pb = reinterpret_cast<const uint4*>(a.mag + rB * K + g * 32);
+        d.ma0 = pa[0]; d.ma1 = pa[1];
+        d.mb0 = pb[0]; d.mb1 = pb[1];
+        d.ea = a.exp[rA * G + g];
+        d.eb = a.exp[rB * G + g];
+        d.sa = a.sign[rA * G + g];
+        d.sb = a.sign[rB * G + g];
+        const uint4* px = reinterpret_cast<const uint4*>(xrow + g * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d.xv[i] = px[i];
+    };
+    f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int c, const MxChunk& d) {
+        const bool live = int64_t(c) * 4 + q < G;    // group past K: contributes nothing
+        const float sa = live ? __builtin_ldexpf(1.f, int(d.ea) - 134) : 0.f;
+        const float sb = live ? __builtin_ldexpf(1.f, int(d.eb) - 134) : 0.f;
+        const uint2 ma[4] = {make_uint2(d.ma0.x, d.ma0.y), make_uint2(d.ma0.z, d.ma0.w),
+                             make_uint2(d.ma1.x, d.ma1.y), make_uint2(d.ma1.z, d.ma1.w)};
+        const uint2 mb[4] = {make_uint2(d.mb0.x, d.mb0.y), make_uint2(d.mb0.z, d.mb0.w),
+                             make_uint2(d.mb1.x, d.mb1.y), make_uint2(d.mb1.z, d.mb1.w)};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 bv = xv_ok ? d.xv[s] : make_uint4(0, 0, 0, 0);
+            const uint4 av = mx_to_bf16x8(ma[s], sa, (d.sa >> (8 * s)) & 0xFFu);
+            const uint4 aw = mx_to_bf16x8(mb[s], sb, (d.sb >> (8 * s)) & 0xFFu);
+            accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                           __builtin_bit_cast(bf16x8_t, bv), accA, 0, 0, 0);
+            accB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw),
+                                                           __builtin_bit_cast(bf16x8_t, bv), accB, 0, 0, 0);
+        }
+    };
+    // two chunk buffers, so a buffer is never copied while its loads are in flight
+    MxChunk c0, c1;
+    int c = wave;
+    if (c < nchunks) load(c, c0);
+    for (; c < nchunks; c += 2 * MX_WAVES) {
+        const int cn = c + MX_WAVES;
+        load(min(cn, nchunks - 1), c1);
+        compute(c, c0);
+        load(min(cn + MX_WAVES, nchunks - 1), c0);
+        if (cn < nchunks) compute(cn, c1);
     }
-    red[wave][lane][0] = acc[0]; red[wave][lane][1] = acc[1]; red[wave][lane][2] = acc[2]; red[wave][lane][3] = acc[3];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        red[wave][0][lane][j] = accA[j];
+        red[wave][1][lane][j] = accB[j];
+    }
     __syncthreads();
-    if (wave == 0) {
+    // C[row = 4q + j][col = n]; waves 0 and 1 sum tiles A and B
+    if (wave < 2) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < MX_WAVES; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s4[j] += red[w][wave][lane][j];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float s = red[0][lane][j] + red[1][lane][j] + red[2][lane][j] + red[3][lane][j];
-            const int64_t r = r0 + 4 * kq + j;
-            if (n < B && r < a.M) y[int64_t(n) * a.M + r] = s;
+            const int64_t r = r0 + 16 * wave + 4 * q + j;
+            if (n < B && r < a.M) y[int64_t(n) * a.M + r] = s4[j];
         }
     }
 }
@@ -1076,8 +1252,8 @@ mbd_status mbd_gemv_mx32(const mbd_dweights* w, const uint16_t* x, int32_t B, fl
     if (w->M == 0) return MBD_OK;
     MxArgs a{static_cast<const uint8_t*>(w->sec[0]), static_cast<const uint32_t*>(w->sec[1]),
              static_cast<const uint8_t*>(w->sec[2]), w->M, w->K};
-    const unsigned blocks = unsigned((w->M + 15) / 16);
-    hipLaunchKernelGGL(mx_gemm_kernel, dim3(blocks), dim3(256), 0, st, a, x, B, y);
+    const unsigned blocks = unsigned((w->M + 31) / 32);
+    hipLaunchKernelGGL(mx_gemm_kernel, dim3(blocks), dim3(64 * MX_WAVES), 0, st, a, x, B, y);
     return hip_check("MX GEMM launch");
 }
 
