@@ -261,13 +261,6 @@ template <int BMAX> struct ScaleLoads { static constexpr int N = BMAX == 1 ? 4 :
 template <bool TER, int BMAX> struct Shape;
 template <> struct Shape<false, 1> { static constexpr int RPW = MBD_B1_RPW, PF = MBD_B1_PF; };
 template <> struct Shape<true, 1> { static constexpr int RPW = MBD_T1_RPW, PF = MBD_T1_PF; };
-#ifndef MBD_B4_RPW
-#define MBD_B4_RPW 2
-#endif
-template <bool TER> struct Shape<TER, 2> { static constexpr int RPW = 2, PF = 2; };
-template <bool TER> struct Shape<TER, 4> { static constexpr int RPW = MBD_B4_RPW, PF = 2; };
-template <bool TER> struct Shape<TER, 8> { static constexpr int RPW = 2, PF = 2; };
-template <bool TER> struct Shape<TER, 16> { static constexpr int RPW = 2, PF = 1; };
 #ifndef MBD_BN_WAVES
 #define MBD_BN_WAVES 4        // waves per workgroup for batch > 1
 #endif
@@ -371,11 +364,6 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
     const int myjob = threadIdx.x;
 
     const int rloc0 = row0 - row_base;   // this lane's first row inside the block
-    Acc3 part[BMAX == 1 ? 1 : RPW][BMAX];    // per-chunk partial dots (batch > 1)
-#pragma unroll
-    for (int r = 0; r < (BMAX == 1 ? 1 : RPW); ++r)
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) part[r][b] = Acc3{0.f, 0.f, 0.f, 0.f};
     int cur_it = 0;   // one-slab: tile being computed
     auto scale = [&](int p, int r, int cc) {
         if constexpr (ONE_SLAB) return half_bits_to_f32(sl[(rloc0 + cur_it * TR + r * RS) * ngroups + (cc / F::CPG)]);
@@ -408,46 +396,7 @@ __device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict
             for (int r = 0; r < RPW; ++r)
                 acc[r][0] = fmaf(scale(p, r, cc), chunk_dot_xreg<TER>(w[p][r], xr, bias, kc), acc[r][0]);
         } else {
-            // unpack every row's chunk once; each batch row's activations are read
-            // from LDS once and reused across the RPW rows
-            uint32_t pr[RPW][TER ? 32 : 16];
-            float sc[RPW];
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                sc[r] = scale(p, r, cc);
-                const uint32_t wv[4] = {w[p][r].x, w[p][r].y, w[p][r].z, w[p][r].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint32_t pw[TER ? 8 : 4];
-                    unpack_word<TER>(wv[i], pw, kc);
-#pragma unroll
-                    for (int e = 0; e < (TER ? 8 : 4); ++e) pr[r][(TER ? 8 : 4) * i + e] = pw[e];
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < BMAX; ++b) {
-                if (b < nb) {
-                    const uint4* xq = xl + (size_t)b * F::XQ * SC + cc;
-                    const float bias = bl[b * SC + cc];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint4 x0 = xq[(TER ? 2 * i : i) * SC];
-                        const uint4 x1 = TER ? xq[(2 * i + 1) * SC] : x0;
-#pragma unroll
-                        for (int r = 0; r < RPW; ++r) {
-                            uint32_t pw[TER ? 8 : 4];
-#pragma unroll
-                            for (int e = 0; e < (TER ? 8 : 4); ++e) pw[e] = pr[r][(TER ? 8 : 4) * i + e];
-                            dot_word<TER>(pw, x0, x1, part[r][b]);
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < RPW; ++r) {
-                        acc[r][b] = fmaf(sc[r], finish<TER>(part[r][b]) - bias, acc[r][b]);
-                        part[r][b] = Acc3{0.f, 0.f, 0.f, 0.f};
-                    }
-                }
-            }
+            static_assert(BMAX == 1, "batches above 1 run on the matrix-core kernel");
         }
     };
 
@@ -710,6 +659,222 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
     }
 }
 
+// ------------------------------------------------------------------ batch >= 2: MFMA
+
+// Batch 2..16 is a skinny GEMM: the codes become bf16 MFMA operands directly.
+// A code c of a pair-friendly word, OR'ed into the bf16 pattern of 128, is the
+// exact value 128 + c = q + K0 (K0 = 136 for INT4, 129 for ternary), so
+// v_mfma_f32_16x16x32_bf16 over one 128-column scale group gives
+// sum (q + K0) x; subtracting K0 * sum x and applying the group's fp16 scale
+// once per group gives the dequantized dot product.  A block is 32 rows (two
+// 16-row tiles) by all of K; its waves take the 128-column groups round robin,
+// with the next group's loads in flight while one is computed, and the waves'
+// partial tiles are summed at the end.  Lane (n, q) = (lane % 16, lane / 16)
+// holds columns [32q, 32q + 32) of the group for weight row n of each tile and
+// for batch row n; MFMA sub-step s uses columns 32q + 8s .. + 8 on both operands,
+// so every k slot sees the same column on A and B.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int MQ_TILES = 2;
+constexpr int MQ_MAXW = 16;
+#ifndef MBD_MQ_GPW
+#define MBD_MQ_GPW 4          // scale groups per wave (sets the waves per block)
+#endif
+
+inline int mq_waves(int64_t K) {
+    return int(std::max<int64_t>(1, std::min<int64_t>(MQ_MAXW, (K / 128) / MBD_MQ_GPW)));
+}
+
+struct MqGroup {
+    uint4 code[MQ_TILES];          // INT4: 4 words (32 codes); ternary: .x, .y (32 codes)
+    uint32_t sc[MQ_TILES][2];      // fp16 scales of the lane's 4 output rows, packed in pairs
+    uint4 xv[4];                   // 32 activations of batch row n
+};
+
+struct MqArgs {
+    const uint8_t* codes;   // [n_mats][M][K * bits / 8]
+    const uint16_t* scales; // [n_mats][M][K / 128]
+    const uint16_t* x;
+    float* y;
+    int M, K;
+    // expert mode
+    const int4* jobs;
+    const int* n_jobs;
+    const int* pair_ids;
+    const int* route;       // grouped in the kernel when set (at most kFusedPairs pairs)
+    int n_pairs, n_experts, topk, x_per_pair, row_blocks, B;
+};
+
+template <bool TER>
+__device__ __forceinline__ uint4 mq_unpack(const uint4 c, int s) {
+    uint32_t o[4];
+    if constexpr (TER) {
+        const uint32_t w = (s < 2) ? c.x : c.y;        // 16 codes per word
+        const int p0 = 4 * (s & 1);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o[p] = ((w >> (2 * (p0 + p))) & 0x00030003u) | 0x43004300u;
+    } else {
+        const uint32_t w = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;   // 8 codes per word
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o[p] = ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Rows [row_base, row_base + 32) of one matrix; nb <= 16 batch rows whose
+// activations / outputs are xrow(b) / yrow(b).
+template <bool TER, class XRow, class YRow>
+__device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restrict__ codes,
+                                        const uint16_t* __restrict__ scales, int row_base, int nb, XRow xrow,
+                                        YRow yrow) {
+    constexpr float K0 = TER ? 129.f : 136.f;
+    constexpr int BPR = TER ? 4 : 2;                       // elements per byte
+    __shared__ float red[MQ_MAXW][MQ_TILES][64][4];
+    const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    const int K = a.K, M = a.M, ngroups = K >> 7;
+    const size_t row_bytes = size_t(K) / BPR;
+    int rowc[MQ_TILES];                                    // weight rows this lane loads (clamped)
+    int orow[MQ_TILES];                                    // first output row of this lane in each tile
+#pragma unroll
+    for (int t = 0; t < MQ_TILES; ++t) {
+        rowc[t] = min(row_base + 16 * t + n, M - 1);
+        orow[t] = row_base + 16 * t + 4 * q;
+    }
+    const bool xlive = n < nb;
+    const uint16_t* xr = xrow(xlive ? n : 0);
+    auto load = [&](int g, MqGroup& d) {
+#pragma unroll
+        for (int t = 0; t < MQ_TILES; ++t) {
+            const uint8_t* cp = codes + size_t(rowc[t]) * row_bytes + size_t(g) * (128 / BPR) + q * (32 / BPR);
+            if constexpr (TER) {
+                const uint2 v = *reinterpret_cast<const uint2*>(cp);
+                d.code[t] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
+                d.code[t] = *reinterpret_cast<const uint4*>(cp);
+            }
+            uint32_t sv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[j] = scales[size_t(min(orow[t] + j, M - 1)) * ngroups + g];
+            d.sc[t][0] = sv[0] | (sv[1] << 16);
+            d.sc[t][1] = sv[2] | (sv[3] << 16);
+        }
+        const uint4* px = reinterpret_cast<const uint4*>(xr + size_t(g) * 128 + 32 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d.xv[i] = px[i];
+    };
+    f32x4_t acc[MQ_TILES];
+#pragma unroll
+    for (int t = 0; t < MQ_TILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Lanes n >= nb carry batch row 0's activations: B column n only reaches
+    // output column n, which is not stored.
+    auto compute = [&](const MqGroup& d) {
+        const uint4* xb = d.xv;
+        float sx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sx = dot2(xb[i].x, 0x3F803F80u, sx);
+            sx = dot2(xb[i].y, 0x3F803F80u, sx);
+            sx = dot2(xb[i].z, 0x3F803F80u, sx);
+            sx = dot2(xb[i].w, 0x3F803F80u, sx);
+        }
+        sx += __shfl_xor(sx, 16, 64);
+        sx += __shfl_xor(sx, 32, 64);
+        const float bias = K0 * sx;
+#pragma unroll
+        for (int t = 0; t < MQ_TILES; ++t) {
+            f32x4_t cg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, mq_unpack<TER>(d.code[t], s)),
+                                                             __builtin_bit_cast(bf16x8_t, xb[s]), cg, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sc = half_bits_to_f32(uint16_t(d.sc[t][j >> 1] >> (16 * (j & 1))));
+                acc[t][j] = fmaf(sc, cg[j] - bias, acc[t][j]);
+            }
+        }
+    };
+    // two group buffers, so a buffer is never copied while its loads are in flight
+    MqGroup g0, g1;
+    int g = wave;
+    if (g < ngroups) load(g, g0);
+    for (; g < ngroups; g += 2 * nw) {
+        const int gn = g + nw;
+        load(min(gn, ngroups - 1), g1);
+        compute(g0);
+        load(min(gn + nw, ngroups - 1), g0);
+        if (gn < ngroups) compute(g1);
+    }
+#pragma unroll
+    for (int t = 0; t < MQ_TILES; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave][t][lane][j] = acc[t][j];
+    __syncthreads();
+    // C[row = 4q + j][col = n]: wave t (or wave t - nw, ... when there are fewer
+    // waves than tiles) sums tile t over the waves
+    for (int t = wave; t < MQ_TILES; t += nw) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nw; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s4[j] += red[w][t][lane][j];
+        if (n < nb) {
+            float* yr = yrow(n);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = row_base + 16 * t + 4 * q + j;
+                if (r < M) yr[r] = s4[j];
+            }
+        }
+    }
+}
+
+template <bool TER>
+__global__ __launch_bounds__(64 * MQ_MAXW) void gemv_mq_kernel(MqArgs a) {
+    const uint16_t* x = a.x;
+    float* y = a.y;
+    const int K = a.K, M = a.M;
+    mq_core<TER>(a, a.codes, a.scales, blockIdx.x * 32, a.B, [=](int b) { return x + (size_t)b * K; },
+                 [=](int b) { return y + (size_t)b * M; });
+}
+
+template <bool TER>
+__global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
+    __shared__ int g[6][kFusedPairs];
+    __shared__ int4 gjob;
+    const int job = blockIdx.x / a.row_blocks, rb = blockIdx.x - job * a.row_blocks;
+    int4 jd;
+    const int* pids;
+    if (a.route) {
+        if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
+        moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, 16, g);
+        for (int qq = threadIdx.x; qq < a.n_pairs; qq += blockDim.x)
+            if (g[4][qq] >= 0 && g[1][qq] == job) gjob = make_int4(g[4][qq] >> 5, qq, g[4][qq] & 31, 0);
+        __syncthreads();
+        jd = gjob;
+        if (jd.x < 0) return;
+        pids = g[5] + jd.y;
+    } else {
+        if (job >= *a.n_jobs) return;
+        jd = a.jobs[job];
+        pids = a.pair_ids + jd.y;
+    }
+    const int e = jd.x, nb = jd.z;
+    const uint16_t* x = a.x;
+    float* y = a.y;
+    const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
+    const size_t per_codes = (size_t)M * K / (TER ? 4 : 2), per_scales = (size_t)M * (K / 128);
+    mq_core<TER>(
+        a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * 32, nb,
+        [=](int b) {
+            const int p = pids[b];
+            return x + (size_t)(xpp ? p : p / topk) * K;
+        },
+        [=](int b) { return y + (size_t)pids[b] * M; });
+}
+
 // Dense dequant of ternary / INT4: one thread per 16-byte chunk.  Element t of a
 // word sits at bit (bits * (t / 2)) + (t odd ? 16 : 0).
 template <bool TER>
@@ -792,14 +957,8 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks, int pre
     if (p.wide) {
         p.RPW = MBD_WIDE_RPW; p.PF = 1;
     } else {
-        switch (bmax) {
-            case 1: p.RPW = ter ? Shape<true, 1>::RPW : Shape<false, 1>::RPW;
-                    p.PF = ter ? Shape<true, 1>::PF : Shape<false, 1>::PF; break;
-            case 2: p.RPW = Shape<false, 2>::RPW; p.PF = Shape<false, 2>::PF; break;
-            case 4: p.RPW = Shape<false, 4>::RPW; p.PF = Shape<false, 4>::PF; break;
-            case 8: p.RPW = Shape<false, 8>::RPW; p.PF = Shape<false, 8>::PF; break;
-            default: p.RPW = Shape<false, 16>::RPW; p.PF = Shape<false, 16>::PF; break;
-        }
+        p.RPW = ter ? Shape<true, 1>::RPW : Shape<false, 1>::RPW;
+        p.PF = ter ? Shape<true, 1>::PF : Shape<false, 1>::PF;
     }
     p.nw = bmax == 1 ? prefer_nw : MBD_BN_WAVES;
     // batch 1: grow the workgroup (up to 16 waves) when that lets every staging
@@ -841,7 +1000,7 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks, int pre
     return p;
 }
 
-// Kernel variants: batch bucket x (rows per wave, ring depth) x single/multi slab.
+// Batch-1 kernel variants: (rows per wave, ring depth) x single/multi slab.
 #define MBD_BQ_DISPATCH(KERNEL, TER, pl, bmax, grid, st, a, what)                                        \
     do {                                                                                                  \
         dim3 blk_(64 * (pl).nw);                                                                          \
@@ -853,19 +1012,9 @@ BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks, int pre
         if ((pl).wide) {                                                                                  \
             constexpr int WR = WideShape<TER, 1>::RPW;                                                    \
             return os_ ? go_(KERNEL<TER, 1, WR, 1, true>) : go_(KERNEL<TER, 1, WR, 1, false>);             \
-        } else {                                                                                          \
+        } else if (bmax == 1) {                                                                           \
             constexpr int R1 = Shape<TER, 1>::RPW, P1 = Shape<TER, 1>::PF;                                \
-            constexpr int R2 = Shape<TER, 2>::RPW, P2 = Shape<TER, 2>::PF;                                \
-            constexpr int R4 = Shape<TER, 4>::RPW, P4 = Shape<TER, 4>::PF;                                \
-            constexpr int R8 = Shape<TER, 8>::RPW, P8 = Shape<TER, 8>::PF;                                \
-            constexpr int R16 = Shape<TER, 16>::RPW, P16 = Shape<TER, 16>::PF;                            \
-            switch (bmax) {                                                                               \
-                case 1: return os_ ? go_(KERNEL<TER, 1, R1, P1, true>) : go_(KERNEL<TER, 1, R1, P1, false>); \
-                case 2: return os_ ? go_(KERNEL<TER, 2, R2, P2, true>) : go_(KERNEL<TER, 2, R2, P2, false>); \
-                case 4: return os_ ? go_(KERNEL<TER, 4, R4, P4, true>) : go_(KERNEL<TER, 4, R4, P4, false>); \
-                case 8: return os_ ? go_(KERNEL<TER, 8, R8, P8, true>) : go_(KERNEL<TER, 8, R8, P8, false>); \
-                case 16: return os_ ? go_(KERNEL<TER, 16, R16, P16, true>) : go_(KERNEL<TER, 16, R16, P16, false>); \
-            }                                                                                             \
+            return os_ ? go_(KERNEL<TER, 1, R1, P1, true>) : go_(KERNEL<TER, 1, R1, P1, false>);           \
         }                                                                                                 \
         return fail(MBD_EINVAL, "no kernel variant for batch %d", bmax);                                  \
     } while (0)
@@ -910,6 +1059,18 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2)) return fail(MBD_EALIGN, "codes must be 16-byte aligned");
     if (w->M == 0) return MBD_OK;
     const bool ter = w->fmt == MBD_TERNARY_B128;
+    if (B >= 2) {
+        // skinny GEMM on the matrix cores
+        MqArgs m{};
+        m.codes = static_cast<const uint8_t*>(w->sec[0]);
+        m.scales = static_cast<const uint16_t*>(w->sec[1]);
+        m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
+        const int nw = mq_waves(w->K);
+        const unsigned blocks = unsigned((w->M + 31) / 32);
+        if (ter) hipLaunchKernelGGL(gemv_mq_kernel<true>, dim3(blocks), dim3(64 * nw), 0, st, m);
+        else hipLaunchKernelGGL(gemv_mq_kernel<false>, dim3(blocks), dim3(64 * nw), 0, st, m);
+        return hip_check("batched gemv launch");
+    }
     const int bmax = round_batch(B);
     BqPlan pl = plan_bq(ter, w->M, w->K, bmax, 512);
     if (pl.lds > kMaxLds) return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
@@ -976,9 +1137,9 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int E = int(w->n_mats), P = T * k;
-    // jobs of at most 4 pairs (the batch-4 kernel); an expert routed more than 4
-    // tokens is read once per group of 4
-    const int bmax = std::min(4, round_batch(T));
+    // one token: the batch-1 kernel; more: jobs of up to 16 pairs on the matrix cores
+    const bool mq = T >= 2;
+    const int bmax = mq ? 16 : 1;
     // sum over experts of ceil(pairs / bmax) <= D + (P - D) / bmax, D = distinct experts
     const int64_t D = std::min<int64_t>(E, P), max_jobs = D + (P - D) / bmax;
     const bool fused = P <= kFusedPairs;
@@ -991,6 +1152,24 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
         else
             hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, st, route, P, E, bmax, pair_ids, jobs, n_jobs);
         if ((s = hip_check("expert grouping launch")) != MBD_OK) return s;
+    }
+    if (mq) {
+        MqArgs m{};
+        m.codes = static_cast<const uint8_t*>(w->sec[0]);
+        m.scales = static_cast<const uint16_t*>(w->sec[1]);
+        m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K);
+        m.jobs = jobs; m.n_jobs = n_jobs; m.pair_ids = pair_ids;
+        m.route = fused ? route : nullptr;
+        m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
+        m.row_blocks = int((w->M + 31) / 32);
+        const int nw = mq_waves(w->K);
+        const int64_t grid = max_jobs * m.row_blocks;
+        if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
+        if (w->fmt == MBD_TERNARY_B128)
+            hipLaunchKernelGGL(moe_mq_kernel<true>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
+        else
+            hipLaunchKernelGGL(moe_mq_kernel<false>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
+        return hip_check("expert gemv launch");
     }
     const bool ter = w->fmt == MBD_TERNARY_B128;
     // about MBD_MOE_BLOCKS workgroups over the whole call
