@@ -354,16 +354,28 @@ def main():
     ap.add_argument("--all", default=None, help="append one JSON line per workload to this file")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of one HIP graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain elementwise copy (y = -x, fp32) reading and writing BYTES per "
+                         "launch, --steps times: the reference kernel for scaling the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the hot path is a single-GPU kernel and "
-              "multi-GPU runs are not part of this build (got --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the hot path is a single-GPU kernel; a sharded run "
+              "over several GPUs is not implemented (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": args.steps}), flush=True)
+        return
     if args.all:
         for name in ALL:
             if name == args.workload:
