@@ -180,7 +180,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
  * token to a subset of experts).  route [T][k] int32 expert ids in [0, n_mats) with
  * distinct ids per token.  x bf16: [T][K] (x_per_pair = 0) or [T][k][K]
  * (x_per_pair = 1).  y fp32 [T][k][M]: y[t][j] = W[route[t][j]] @ x_row.  An
- * expert's weights are read once per group of up to 4 tokens routed to it.  At
+ * expert's weights are read once per group of up to 16 tokens routed to it.  At
  * most 4096 experts (MBD_ESHAPE beyond).  Ids outside [0, n_mats) leave their y
  * rows unwritten.  ws: device workspace of at least
  * mbd_moe_workspace_bytes(n_mats, T, k) bytes, 16-byte aligned, contents
