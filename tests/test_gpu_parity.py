@@ -79,6 +79,28 @@ def test_gemv_ragged(dev, kind, M, K, B):
     assert gemv.rel_l2(y, ref) <= TOL
 
 
+# Batch-1 kernel variants the ragged shapes do not reach: activations staged in
+# several LDS slabs (more than 1024 chunks per row), and the many-rows-per-wave
+# shape for short rows over many rows.
+B1_PATHS = [("int4", 3, 32768 + 256), ("ternary", 2, 65536 + 128), ("int4", 16384, 1024), ("ternary", 40000, 1024)]
+
+
+@pytest.mark.parametrize("kind,M,K", B1_PATHS)
+def test_gemv_b1_paths(dev, kind, M, K):
+    """Full-size launch; the oracle checks sampled rows (rows quantize independently)."""
+    print("case gemv b1 path", kind, M, K, flush=True)
+    w = _rand_w(M + K, M, K)
+    x = _rand_x(K, 1, K)
+    dw = _mbd().to_device(_mbd().mbd_pack(_fmt(kind), w), dev)
+    y = _run_gemv(dw, x, dev)
+    assert np.all(np.isfinite(y))
+    rows = np.unique(np.concatenate([np.arange(min(M, 24)), np.arange(max(0, M - 8), M),
+                                     np.random.default_rng(M).integers(0, M, 32)]))
+    q, s = QUANT[kind].quantize(w[rows])
+    ref = gemv.gemv(QUANT[kind].dequant(q, s), x)
+    assert gemv.rel_l2(y[:, rows], ref) <= TOL
+
+
 @pytest.mark.parametrize("kind", ["ternary", "int4"])
 def test_dequant_exact(dev, kind):
     mbd = _mbd()
