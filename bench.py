@@ -63,7 +63,7 @@ class BlockQuantGemv(Workload):
         import memory_bound_decode_amd as mbd
         import synth
         self.name, self.kind, self.M, self.K, self.B = name, kind, M, K, B
-        self.kernel = "gemv_bq_kernel"
+        self.kernel = "gemv_b1_kernel" if B == 1 else "gemv_mq_kernel"
         self.fmt_name = {"int4": "int4_g128", "ternary": "ternary_b128"}[kind]
         wl = synth.WORKLOADS[seed_name]
         if (wl.M, wl.K) == (M, K):
@@ -116,12 +116,13 @@ class MoeGemv(Workload):
         import memory_bound_decode_amd as mbd
         import synth
         wl = synth.WORKLOADS["ternary_moe"]
-        self.name, self.T, self.kernel, self.fmt_name = "ternary_moe_t%d" % T, T, "moe_bq_kernel", "ternary_b128"
+        self.name, self.T, self.kernel, self.fmt_name = "ternary_moe_t%d" % T, T, (
+            "moe_b1_kernel" if T == 1 else "moe_mq_kernel"), "ternary_b128"
         self.routes = synth.gen_routes(wl, T)
         ups = np.concatenate([synth.gen_expert(wl, e, "up") for e in range(wl.experts)])
         dns = np.concatenate([synth.gen_expert(wl, e, "down") for e in range(wl.experts)])
-        pu = mbd.mbd_pack(mbd.MBD_TERNARY_B128, ups)
-        pd = mbd.mbd_pack(mbd.MBD_TERNARY_B128, dns)
+        pu = mbd.mbd_pack(mbd.MBD_TERNARY_B128, ups, n_mats=wl.experts)
+        pd = mbd.mbd_pack(mbd.MBD_TERNARY_B128, dns, n_mats=wl.experts)
         per_expert = (sum(b for _, b in pu.sections().values()) + sum(b for _, b in pd.sections().values())) // wl.experts
         self.distinct = len(set(self.routes.reshape(-1).tolist()))
         self.weight_bytes = per_expert * self.distinct

@@ -61,21 +61,36 @@ typedef enum {
 /* ------------------------------------------------------------------ packing
  * Offline, CPU only.  Section layouts (all little-endian, rows contiguous):
  *
- * MBD_TERNARY_B128  (sec 0) "codes"  uint32 [M][K/16]: word w holds elements
- *                                    16w..16w+15, the even ones in the low half and
- *                                    the odd ones in the high half: code q+1 of
- *                                    element 16w+t at bit 2*(t/2) (+16 if t is odd);
- *                                    code 3 is never written
+ * MBD_TERNARY_B128  (sec 0) "codes"  uint32 [M*K/16]: a word holds 16 consecutive
+ *                                    elements of a row, the even ones in the low half
+ *                                    and the odd ones in the high half: code q+1 of
+ *                                    element t of the word at bit 2*(t/2) (+16 if t
+ *                                    is odd); code 3 is never written.  Word order is
+ *                                    tile-interleaved (below), blocks taken in pairs
+ *                                    (2h, 2h+1): unit (m, kq) of a pair is 16 bytes,
+ *                                    2 words of block 2h then 2 of block 2h+1 (columns
+ *                                    32kq..+32 of each); an odd last block is stored
+ *                                    alone in 8-byte units.
  *                   (sec 1) "scales" fp16 [M][K/128]: fp16(mean|w| of the block),
  *                                    round to nearest even; 1.0 for an all-zero
  *                                    block (whose codes are all q = 0).
  *                   q = clamp(round_half_even(w / scale), -1, 1).
- * MBD_INT4_G128     (sec 0) "codes"  uint32 [M][K/8]: word w holds elements
- *                                    8w..8w+7, evens in the low half, odds in the high
- *                                    half: code q+8 of element 8w+t at bit 4*(t/2)
- *                                    (+16 if t is odd); code 0 is never written
+ * MBD_INT4_G128     (sec 0) "codes"  uint32 [M*K/8]: a word holds 8 consecutive
+ *                                    elements of a row, evens in the low half, odds
+ *                                    in the high half: code q+8 of element t of the
+ *                                    word at bit 4*(t/2) (+16 if t is odd); code 0 is
+ *                                    never written.  Word order is tile-interleaved
+ *                                    (below); unit (m, kq) of group g is 16 bytes,
+ *                                    the 4 words of columns 128g + 32kq .. +32.
  *                   (sec 1) "scales" fp16 [M][K/128]: fp16(max|w| / 7); 1.0 for
  *                                    an all-zero group.  q = clamp(rne(w/s), -7, 7).
+ *                   Tile-interleaved order: rows in tiles of 16 (the last tile of a
+ *                   matrix holds the R <= 16 rows left).  A tile holds its groups
+ *                   (ternary: group pairs) in order; each is R*4 units, unit (row m
+ *                   of the tile, quarter kq) at index kq*R + m, so that the 64 lanes
+ *                   of a wave, lane = 16*kq + m, read one contiguous run.  A stack of
+ *                   n_mats matrices (mbd_pack_params.n_mats) is tiled matrix by
+ *                   matrix: its sections are the concatenation of each matrix's.
  * MBD_CASSANDRA     Wanda keep count floor(K*keep_num/keep_den) per row, score
  *                   |w| * act_norm[k], ties to the lower k; 3 high mantissa bits
  *                   kept; 4096-element flat tiles.  f = m*K + k is the flat index.
@@ -104,6 +119,8 @@ typedef enum {
 typedef struct {
     int32_t keep_num;   /* Cassandra keep fraction numerator   (default 3)  */
     int32_t keep_den;   /* Cassandra keep fraction denominator (default 10) */
+    int64_t n_mats;     /* TERNARY / INT4: the M rows are n_mats stacked matrices
+                           of M / n_mats rows each (default 1; 0 means 1)   */
 } mbd_pack_params;
 
 typedef struct mbd_packed mbd_packed;   /* opaque, owns the host section buffers */

@@ -29,9 +29,9 @@ SPEC_SECTIONS = ("bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix")
 class Packed:
     """Owns an mbd_packed handle (host sections written by the C++ packer)."""
 
-    def __init__(self, handle: ctypes.c_void_p, fmt: int, M: int, K: int):
+    def __init__(self, handle: ctypes.c_void_p, fmt: int, M: int, K: int, n_mats: int = 1):
         self._h = handle
-        self.fmt, self.M, self.K = fmt, M, K
+        self.fmt, self.M, self.K, self.n_mats = fmt, M, K, n_mats
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -67,8 +67,9 @@ class Packed:
 
 
 def mbd_pack(fmt: int, w_bits: np.ndarray, act_norm: np.ndarray | None = None,
-             keep_num: int = 3, keep_den: int = 10) -> Packed:
-    """Pack bf16 bits [M][K] (numpy uint16) on the CPU."""
+             keep_num: int = 3, keep_den: int = 10, n_mats: int = 1) -> Packed:
+    """Pack bf16 bits [M][K] (numpy uint16) on the CPU; n_mats > 1 packs the rows as
+    that many stacked matrices (ternary / INT4, for the expert GEMV)."""
     w = np.ascontiguousarray(w_bits, dtype=np.uint16)
     if w.ndim != 2:
         raise ValueError("w_bits must be 2-D [M][K]")
@@ -76,12 +77,12 @@ def mbd_pack(fmt: int, w_bits: np.ndarray, act_norm: np.ndarray | None = None,
     nrm = None
     if act_norm is not None:
         nrm = np.ascontiguousarray(act_norm, dtype=np.float32)
-    params = MbdPackParams(keep_num, keep_den)
+    params = MbdPackParams(keep_num, keep_den, n_mats)
     h = ctypes.c_void_p()
     st = lib().mbd_pack(fmt, w.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), M, K,
                         None if nrm is None else nrm.ctypes.data, ctypes.byref(params), ctypes.byref(h))
     check(st, "mbd_pack")
-    return Packed(h, fmt, M, K)
+    return Packed(h, fmt, M, K, n_mats)
 
 
 class DeviceWeights:
@@ -99,6 +100,9 @@ class DeviceWeights:
         self.desc.n_sym = st.n_sym
         if packed.M % n_mats:
             raise ValueError("rows not divisible by n_mats")
+        if n_mats != packed.n_mats and packed.fmt in (MBD_TERNARY_B128, MBD_INT4_G128):
+            raise ValueError("packed as %d matrices, described as %d: pack with mbd_pack(..., n_mats=%d)"
+                             % (packed.n_mats, n_mats, n_mats))
         self.desc.M = packed.M // n_mats
         self.desc.K = packed.K
         self.desc.n_kept = st.n_kept

@@ -13,7 +13,7 @@ MBD_MAX_SECTIONS = 8
 
 
 class MbdPackParams(Structure):
-    _fields_ = [("keep_num", c_int32), ("keep_den", c_int32)]
+    _fields_ = [("keep_num", c_int32), ("keep_den", c_int32), ("n_mats", c_int64)]
 
 
 class MbdSection(Structure):

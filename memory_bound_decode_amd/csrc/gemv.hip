@@ -1,32 +1,25 @@
 // Fused dequant-GEMV / skinny GEMM for block-ternary ([Bonsai2] 1.2) and INT4
 // group-128 ([GPT54-INT4] 3.2) weights on gfx950, the grouped expert GEMV, and
-// the dense dequant kernels.
+// the dense dequant kernel.
 //
-// Decode time is set by the weight bytes ([Bolt], background), so the kernel is
-// built around one coalesced 16-byte load per lane per "chunk" of packed codes
-// (64 ternary or 32 INT4 weights), decoded in registers into bf16 pairs and
-// consumed by v_dot2c_f32_bf16.
+// Decode time is set by the weight bytes ([Bolt], background), and every batch
+// size runs on v_mfma_f32_16x16x32_bf16.  Code -> bf16: OR-ing a small field c
+// into the mantissa of 0x4300 (bf16 128.0) gives the exact bf16 value
+// 128 + c * 2^p for a field at mantissa bit p.  A word keeps its even elements in
+// the low half and the odd ones in the high half, so one v_and_or_b32 (after a
+// shift) yields an element pair, and four pairs are one lane's MFMA A operand.
+// The constant part of the code values ("bias": K0 sum x over a scale group) is
+// removed once per group, and the group's fp16 scale applied once per group.
+// On a 16-lane SIMD a wave64 VALU op takes 4 clocks: a dot2 formulation (one op
+// per weight pair on top of the unpack) costs about as many SIMD clocks as HBM
+// needs to deliver the bytes it consumes, so even batch 1 uses the matrix cores
+// and leaves only the unpack on the VALU.
 //
-// Code -> bf16: OR-ing a small field c into the mantissa of 0x4300 (bf16 128.0)
-// gives the exact bf16 value 128 + c * 2^p for a field at mantissa bit p.  The
-// packed layout keeps the even elements of a word in its low half and the odd
-// ones in its high half, so one v_and_or_b32 (after a shift) yields the pair
-// (w[2t], w[2t+1]) that lines up with the natural activation pair
-// (x[2t], x[2t+1]).  A dot2 then accumulates sum (128 + c) x; the per-chunk
-// constant sum_k base_k x_k ("bias", shared by every row) is subtracted once
-// per chunk and the group scale applied once per chunk.  Ternary fields sit at
-// mantissa bits 0, 2 and 4 after a shift by 0, 6 or 12, giving three position
-// classes that are accumulated separately and combined with weights 1, 1/4,
-// 1/16, so three fields come out of every shift.
-//
-// Work split: lanes of a wave are grouped G to a row (G = largest power of two
-// <= 64 dividing the chunks per row); each lane walks its row's chunks with
-// stride G and every wave covers RPW such row-steps.  A ring of PF chunks of
-// 16-byte code loads stays in flight per lane.  The activations are staged once
-// per workgroup in LDS (raw bf16, quad-interleaved so that neighbouring lanes
-// read neighbouring 16-byte words, plus the per-chunk bias), in K slabs when
-// they do not fit.  The workgroup barrier waits on LDS traffic only: a plain
-// __syncthreads() would also drain every weight load in flight.
+// Codes are stored tile-interleaved (include/mbd.h): for each 16-row tile and
+// 128-column group (ternary: pair of groups), lane l = 16 kq + m of a wave finds
+// the 16 bytes of tile row m, columns 32kq .. +32, at l * 16.  One load
+// instruction then reads 1 KB contiguous and lands in A-operand order (lane l
+// holds row l % 16, k slots 8 (l / 16) .. +8 of each MFMA step).
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -38,6 +31,9 @@
 namespace mbd {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -49,52 +45,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_fl
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return __half2float(__ushort_as_half(h));
-}
-
-// Workgroup barrier that waits for this wave's LDS operations only (not for
-// vector-memory loads still in flight, unlike __syncthreads()).
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <bool TER>
-struct Fmt {
-    static constexpr int WPC = TER ? 64 : 32;     // weights per 16-byte chunk
-    static constexpr int XQ = WPC / 8;            // 16-byte words of activations per chunk
-    static constexpr int CPG = 128 / WPC;         // chunks per scale group
-};
-
-// Stage the activations of one chunk: stage_load issues the 16-byte loads (ahead
-// of the weight stream: vector-memory counters retire in issue order),
-// stage_store writes them to LDS and the chunk's bias.
-template <bool TER>
-__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ xs, uint4 (&raw)[Fmt<TER>::XQ]) {
-    const uint4* src = reinterpret_cast<const uint4*>(xs);
-#pragma unroll
-    for (int i = 0; i < Fmt<TER>::XQ; ++i) raw[i] = src[i];
-}
-
-template <bool TER>
-__device__ __forceinline__ void stage_store(const uint4 (&raw)[Fmt<TER>::XQ], uint4* __restrict__ dst,
-                                            int stride_q, float* __restrict__ bias) {
-    float b = 0.f;
-#pragma unroll
-    for (int q = 0; q < Fmt<TER>::XQ; ++q) {
-        dst[q * stride_q] = raw[q];
-        const uint32_t v[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float pair = bf16_to_f32(v[j] & 0xFFFFu) + bf16_to_f32(v[j] >> 16);
-            if constexpr (TER) {
-                // pair p = 4 * (q & 1) + j of the 16-element word q >> 1: class p % 3
-                const int cls = (4 * (q & 1) + j) % 3;
-                b += (cls == 0 ? 129.f : (cls == 1 ? 33.f : 9.f)) * pair;
-            } else {
-                b += pair;
-            }
-        }
-    }
-    *bias = TER ? b : 136.f * b;
 }
 
 // (a & m) | o in one VALU op.  gfx9 VOP3 encodings cannot take a literal, so
@@ -118,376 +68,49 @@ struct UnpackConsts {
     }
 };
 
-// One 32-bit word of codes -> bf16 pairs.  INT4: pair j = (w[2j], w[2j+1]).
-// Ternary: pair p = (w[2p], w[2p+1]) scaled by 1, 4 or 16 for p % 3 = 0, 1, 2.
+// A operand of MFMA step s (0..3) from the words of one scale group: INT4 words
+// x, y, z, w (step s = word s, 8 codes), ternary words x, y (step s = half s % 2
+// of word s / 2).  Ternary pair p of a word is read at mantissa bits 2 (p % 3)
+// after a shift by 6 (p / 3): value 128 + c 4^(p % 3), matched by activations
+// divided by 4^(p % 3).
 template <bool TER>
-__device__ __forceinline__ void unpack_word(const uint32_t v, uint32_t (&p)[TER ? 8 : 4], const UnpackConsts& k) {
+__device__ __forceinline__ bf16x8_t code_operand(const uint4 c, int s, const UnpackConsts& k) {
+    uint32_t o[4];
     if constexpr (TER) {
+        const uint32_t v = (s < 2) ? c.x : c.y;
         const uint32_t s6 = v >> 6, s12 = v >> 12;
-        p[0] = and_or(v, k.m2a, k.magic);
-        p[1] = and_or(v, k.m2b, k.magic);
-        p[2] = and_or(v, k.m2c, k.magic);
-        p[3] = and_or(s6, k.m2a, k.magic);
-        p[4] = and_or(s6, k.m2b, k.magic);
-        p[5] = and_or(s6, k.m2c, k.magic);
-        p[6] = and_or(s12, k.m2a, k.magic);
-        p[7] = and_or(s12, k.m2b, k.magic);
-    } else {
-        p[0] = and_or(v, k.m4, k.magic);
-        p[1] = and_or(v >> 4, k.m4, k.magic);
-        p[2] = and_or(v >> 8, k.m4, k.magic);
-        p[3] = and_or(v >> 12, k.m4, k.magic);
-    }
-}
-
-// Dot of one word's pairs with the matching activations (INT4: 4 pairs from one
-// 16-byte word; ternary: 8 pairs from two), into class accumulators.
-struct Acc3 {
-    float a, b, c, d;   // INT4: a, b chains; ternary: a/d class 1, b class 4, c class 16
-};
-
-template <bool TER>
-__device__ __forceinline__ void dot_word(const uint32_t (&pw)[TER ? 8 : 4], uint4 x0, uint4 x1, Acc3& t) {
-    if constexpr (TER) {
-        t.a = dot2(pw[0], x0.x, t.a);
-        t.b = dot2(pw[1], x0.y, t.b);
-        t.c = dot2(pw[2], x0.z, t.c);
-        t.d = dot2(pw[3], x0.w, t.d);
-        t.b = dot2(pw[4], x1.x, t.b);
-        t.c = dot2(pw[5], x1.y, t.c);
-        t.a = dot2(pw[6], x1.z, t.a);
-        t.b = dot2(pw[7], x1.w, t.b);
-    } else {
-        (void)x1;
-        t.a = dot2(pw[0], x0.x, t.a);
-        t.b = dot2(pw[1], x0.y, t.b);
-        t.a = dot2(pw[2], x0.z, t.a);
-        t.b = dot2(pw[3], x0.w, t.b);
-    }
-}
-
-template <bool TER>
-__device__ __forceinline__ float finish(const Acc3& t) {
-    if constexpr (TER) return (t.a + t.d) + 0.25f * t.b + 0.0625f * t.c;
-    else return t.a + t.b;
-}
-
-// Full chunk (4 code words) against the staged activations of one batch row:
-// xq points at quad 0 of the chunk, successive quads are `sq` uint4 apart.
-template <bool TER>
-__device__ __forceinline__ float chunk_dot(const uint4 w, const uint4* __restrict__ xq, int sq, float bias,
-                                           const UnpackConsts& k) {
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    Acc3 t{-bias, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t pw[TER ? 8 : 4];
-        const uint4 x0 = xq[(TER ? 2 * i : i) * sq];
-        const uint4 x1 = TER ? xq[(2 * i + 1) * sq] : x0;
-        unpack_word<TER>(wv[i], pw, k);
-        dot_word<TER>(pw, x0, x1, t);
-#if MBD_WORD_FENCE
-        __builtin_amdgcn_sched_barrier(0);   // keep one word's pairs live at a time
-#endif
-    }
-    return finish<TER>(t);
-}
-
-// Chunk against activations held in registers (one x chunk reused across rows).
-template <bool TER>
-__device__ __forceinline__ float chunk_dot_xreg(const uint4 w, const uint4 (&xr)[Fmt<TER>::XQ], float bias,
-                                                const UnpackConsts& k) {
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    Acc3 t{-bias, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t pw[TER ? 8 : 4];
-        unpack_word<TER>(wv[i], pw, k);
-        dot_word<TER>(pw, xr[TER ? 2 * i : i], xr[TER ? 2 * i + 1 : i], t);
-    }
-    return finish<TER>(t);
-}
-
-struct BqArgs {
-    const uint4* codes;      // [n_mats][M][C] chunks
-    const uint16_t* scales;  // [n_mats][M][K/128]
-    const uint16_t* x;       // bf16 activations
-    float* y;                // fp32 outputs
-    int M, K, C, G, SC, B;
-    int gshift;              // log2(G)
-    float inv_c;             // 1 / C (division-free staging job split)
-    int rows_per_block;      // n_iter * tile_rows
-    int tile_rows, n_iter;   // one-slab: the block walks n_iter tiles of tile_rows rows
-    // expert (grouped) mode
-    const int4* jobs;        // {expert, pair_start, n_pairs, 0}
-    const int* n_jobs;
-    const int* pair_ids;     // pairs sorted by expert: pair id = t*k + slot
-    int topk, x_per_pair, row_blocks;
-    const int* route;        // set: group the routes inside the kernel (n_pairs <= kFusedPairs)
-    int n_pairs, n_experts;
-};
-
-// Scale loads per thread in the one-slab path (rows_per_block * K/128 <= this * threads).
-template <int BMAX> struct ScaleLoads { static constexpr int N = BMAX == 1 ? 4 : 16; };
-
-// Load-ring depth and rows per wave-step for each batch bucket.
-#ifndef MBD_WORD_FENCE
-#define MBD_WORD_FENCE 1
-#endif
-#ifndef MBD_CODES_NT
-#define MBD_CODES_NT 1     // stream the packed codes with non-temporal loads
-#endif
-#ifndef MBD_B1_RPW
-#define MBD_B1_RPW 1
-#endif
-#ifndef MBD_B1_PF
-#define MBD_B1_PF 2
-#endif
-#ifndef MBD_MAX_WAVES
-#define MBD_MAX_WAVES 8       // waves per workgroup (upper bound) for batch 1
-#endif
-#ifndef MBD_WPE
-#define MBD_WPE 4             // INT4 batch-1 target waves per SIMD (caps VGPRs at 512 / MBD_WPE)
-#endif
-#ifndef MBD_TWPE
-#define MBD_TWPE 4            // ternary batch-1 target waves per SIMD
-#endif
-#ifndef MBD_T1_RPW
-#define MBD_T1_RPW 1
-#endif
-#ifndef MBD_T1_PF
-#define MBD_T1_PF 2
-#endif
-template <bool TER, int BMAX> struct Shape;
-template <> struct Shape<false, 1> { static constexpr int RPW = MBD_B1_RPW, PF = MBD_B1_PF; };
-template <> struct Shape<true, 1> { static constexpr int RPW = MBD_T1_RPW, PF = MBD_T1_PF; };
-#ifndef MBD_BN_WAVES
-#define MBD_BN_WAVES 4        // waves per workgroup for batch > 1
-#endif
-// Batch 1, short rows (one or two chunks per lane): more rows per wave, one load
-// each in flight per row, so that a lane still has several loads outstanding and
-// the block's staged activations serve more rows.
-#ifndef MBD_WIDE_RPW
-#define MBD_WIDE_RPW 4
-#endif
-template <bool TER, int BMAX> struct WideShape { static constexpr int RPW = MBD_WIDE_RPW, PF = 1; };
-
-// Core: rows [row_base, row_base + rows_per_block) of one matrix, nb <= BMAX batch
-// rows whose activations / outputs are given by xrow(b) / yrow(b).
-template <bool TER, int BMAX, int RPW, int PF, bool ONE_SLAB, class XRow, class YRow>
-__device__ __forceinline__ void bq_core(const BqArgs& a, const uint4* __restrict__ codes,
-                                        const uint16_t* __restrict__ scales, int row_base, int nb,
-                                        XRow xrow, YRow yrow) {
-    using F = Fmt<TER>;
-    extern __shared__ uint4 lds4[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // G is a power of two: all per-lane index math is shifts and masks (integer
-    // division would sit in front of the first load of every wave)
-    const int G = a.G, gs = a.gshift, RS = 64 >> gs, C = a.C, K = a.K, M = a.M, SC = a.SC;
-    const int sub = lane & (G - 1), rg = lane >> gs;
-    const int row0 = row_base + wave * (RS * RPW) + rg;
-    const int ngroups = K >> 7;
-    const int nj = C >> gs;              // chunks per lane per row
-    const int SJ = SC >> gs;             // chunks per lane per LDS slab (multiple of PF unless one slab)
-    uint4* xl = lds4;                                        // [BMAX][XQ][SC]
-    float* bl = reinterpret_cast<float*>(lds4 + BMAX * F::XQ * SC);   // [BMAX][SC]
-    uint16_t* sl = reinterpret_cast<uint16_t*>(bl + BMAX * SC);       // one-slab: [rows_per_block][ngroups]
-
-    const u32x4_t* rowp[RPW];
-    const uint16_t* srow[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int row = min(row0 + r * RS, M - 1);
-        rowp[r] = reinterpret_cast<const u32x4_t*>(codes) + (size_t)row * C + sub;
-        srow[r] = scales + (size_t)row * ngroups;
-    }
-    const int TR = a.tile_rows, NI = ONE_SLAB ? a.n_iter : 1;
-
-    float acc[RPW][BMAX];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) acc[r][b] = 0.f;
-    UnpackConsts kc;
-    kc.init();
-
-    uint4 w[PF][RPW];
-    uint32_t s[PF][RPW];     // raw fp16 scale bits: converting at issue time would make the
-                             // compiler wait for the load (and, in order, every load before it)
-    // Slots past the row's last chunk load a hot, in-bounds dummy (the first
-    // activation row) instead of branching: every issue is unconditional, so the
-    // count of loads in flight is static and the waits stay exact.
-    const u32x4_t* xdummy = reinterpret_cast<const u32x4_t*>(xrow(0)) + (lane & 15);
-    auto issue = [&](int j, int p) {
-        const bool real = j < nj;
-        const int c = sub + G * j;
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const u32x4_t* pc = real ? rowp[r] + G * j : xdummy;
-#if MBD_CODES_NT
-            const u32x4_t v = __builtin_nontemporal_load(pc);
-#else
-            const u32x4_t v = *pc;
-#endif
-            w[p][r] = make_uint4(v.x, v.y, v.z, v.w);
-            if constexpr (!ONE_SLAB) s[p][r] = real ? srow[r][c / F::CPG] : srow[r][0];
-        }
-        __builtin_amdgcn_sched_barrier(0);   // each slot's loads stay adjacent, in slot order
-    };
-    // One-slab walk: items (tile it, chunk j) in order, the ring PF items ahead.
-    int iss_it = 0, iss_j = 0;
-    auto issue_next = [&](int p) {
-        const bool real = iss_it < NI;
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int row = min(row0 + iss_it * TR + r * RS, M - 1);
-            const u32x4_t* pc = real ? reinterpret_cast<const u32x4_t*>(codes) + (size_t)row * C + sub + G * iss_j
-                                     : xdummy;
-#if MBD_CODES_NT
-            const u32x4_t v = __builtin_nontemporal_load(pc);
-#else
-            const u32x4_t v = *pc;
-#endif
-            w[p][r] = make_uint4(v.x, v.y, v.z, v.w);
-        }
-        if (++iss_j == nj) {
-            iss_j = 0;
-            ++iss_it;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Activation loads first, then the first PF chunks of codes, so that waiting
-    // for the activations does not wait for the weight stream.
-    const int scn0 = min(SC, C);
-    const bool one_pass = nb * scn0 <= (int)blockDim.x;
-    const int myjob = threadIdx.x;
-
-    const int rloc0 = row0 - row_base;   // this lane's first row inside the block
-    int cur_it = 0;   // one-slab: tile being computed
-    auto scale = [&](int p, int r, int cc) {
-        if constexpr (ONE_SLAB) return half_bits_to_f32(sl[(rloc0 + cur_it * TR + r * RS) * ngroups + (cc / F::CPG)]);
-        else return half_bits_to_f32(uint16_t(s[p][r]));
-    };
-    // reduce across the G lanes of each row group; lane sub == 0 stores
-    auto flush = [&](int it) {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-#pragma unroll
-            for (int b = 0; b < BMAX; ++b) {
-                float v = acc[r][b];
-                for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-                const int row = row0 + it * TR + r * RS;
-                if (sub == 0 && b < nb && row < M) yrow(b)[row] = v;
-                acc[r][b] = 0.f;
-            }
-        }
-    };
-    auto compute = [&](int p, int cc) {
-        if constexpr (BMAX == 1 && RPW == 1) {
-            acc[0][0] = fmaf(scale(p, 0, cc), chunk_dot<TER>(w[p][0], xl + cc, SC, bl[cc], kc), acc[0][0]);
-        } else if constexpr (BMAX == 1) {
-            // one read of the chunk's activations from LDS serves all RPW rows
-            uint4 xr[F::XQ];
-#pragma unroll
-            for (int q = 0; q < F::XQ; ++q) xr[q] = xl[q * SC + cc];
-            const float bias = bl[cc];
-#pragma unroll
-            for (int r = 0; r < RPW; ++r)
-                acc[r][0] = fmaf(scale(p, r, cc), chunk_dot_xreg<TER>(w[p][r], xr, bias, kc), acc[r][0]);
+        if ((s & 1) == 0) {
+            o[0] = and_or(v, k.m2a, k.magic);
+            o[1] = and_or(v, k.m2b, k.magic);
+            o[2] = and_or(v, k.m2c, k.magic);
+            o[3] = and_or(s6, k.m2a, k.magic);
         } else {
-            static_assert(BMAX == 1, "batches above 1 run on the matrix-core kernel");
-        }
-    };
-
-    if constexpr (ONE_SLAB) {
-        // every staging job fits in one pass (the launcher guarantees it)
-        // job -> (batch row, chunk) without integer division: (job + 1/2) / C is
-        // never within float rounding of an integer for C <= 2^12
-        const bool has = myjob < nb * C;
-        const int jb = BMAX == 1 ? 0 : int((float(myjob) + 0.5f) * a.inv_c);
-        const int jc = myjob - jb * C;
-        uint4 xraw[F::XQ];
-        // threads without a job load the first chunk again (unconditional issue)
-        stage_load<TER>(xrow(has ? jb : 0) + (size_t)(has ? jc : 0) * F::WPC, xraw);
-        // the block's fp16 scales: rows_per_block * ngroups contiguous values
-        const int nsc = a.rows_per_block * ngroups;
-        const int sc_lim = min(M - row_base, a.rows_per_block) * ngroups;   // rows past M are not read
-        constexpr int NSL = ScaleLoads<BMAX>::N;
-        uint16_t sraw[NSL];
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) {
-            const int e = myjob + i * (int)blockDim.x;
-            sraw[i] = scales[(size_t)row_base * ngroups + ((e < nsc && e < sc_lim) ? e : 0)];
-        }
-#pragma unroll
-        for (int p = 0; p < PF; ++p) issue_next(p);
-        __builtin_amdgcn_sched_barrier(0);          // keep the weight loads ahead of the staging waits
-        if (has) stage_store<TER>(xraw, xl + (size_t)jb * F::XQ * SC + jc, SC, bl + jb * SC + jc);
-#pragma unroll
-        for (int i = 0; i < NSL; ++i) {
-            const int e = myjob + i * (int)blockDim.x;
-            if (e < nsc) sl[e] = sraw[i];
-        }
-        barrier_lds();
-        const int total = NI * nj;
-        int cj = 0;
-        for (int f = 0; f < total; f += PF) {
-#pragma unroll
-            for (int p = 0; p < PF; ++p) {
-                if (f + p < total) {
-                    compute(p, sub + G * cj);
-                    if (++cj == nj) {
-                        flush(cur_it);
-                        cj = 0;
-                        ++cur_it;
-                    }
-                }
-                issue_next(p);
-            }
+            o[0] = and_or(s6, k.m2b, k.magic);
+            o[1] = and_or(s6, k.m2c, k.magic);
+            o[2] = and_or(s12, k.m2a, k.magic);
+            o[3] = and_or(s12, k.m2b, k.magic);
         }
     } else {
-        (void)one_pass;
-#pragma unroll
-        for (int p = 0; p < PF; ++p) issue(p, p);
-        for (int js = 0; js < nj; js += SJ) {
-            const int c0 = js * G;
-            const int scn = min(SC, C - c0);
-            for (int job = threadIdx.x; job < nb * scn; job += blockDim.x) {
-                const int b = job / scn, cc = job - b * scn;
-                uint4 raw[F::XQ];
-                stage_load<TER>(xrow(b) + (size_t)(c0 + cc) * F::WPC, raw);
-                stage_store<TER>(raw, xl + (size_t)b * F::XQ * SC + cc, SC, bl + b * SC + cc);
-            }
-            barrier_lds();
-            const int je = min(nj, js + SJ);
-            for (int j = js; j < je; j += PF) {
-#pragma unroll
-                for (int p = 0; p < PF; ++p) {
-                    const int jj = j + p;
-                    if (jj < je) compute(p, sub + G * (jj - js));
-                    issue(jj + PF, p);
-                }
-            }
-            barrier_lds();
-        }
+        const uint32_t v = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+        o[0] = and_or(v, k.m4, k.magic);
+        o[1] = and_or(v >> 4, k.m4, k.magic);
+        o[2] = and_or(v >> 8, k.m4, k.magic);
+        o[3] = and_or(v >> 12, k.m4, k.magic);
     }
-
-    if constexpr (!ONE_SLAB) flush(0);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-#define MBD_BQ_ATTRS(TER, BMAX)                                                     \
-    __launch_bounds__(BMAX == 1 ? 1024 : 64 * MBD_BN_WAVES)                         \
-    __attribute__((amdgpu_waves_per_eu(BMAX == 1 ? (TER ? MBD_TWPE : MBD_WPE) : 1, 8)))
+// Tile-interleaved addressing.  Tile t of a matrix holds rows [16t, 16t + R),
+// R = min(16, M - 16t), and starts at byte 16t * row_bytes.  Item i of a tile
+// (INT4: group i; ternary: group pair i) starts at i * 64 R, and unit (m, kq) of a
+// full item at (kq R + m) * 16; the odd last ternary group is an item of 8-byte
+// units at (kq R + m) * 8.
+__device__ __forceinline__ uint32_t tile_unit(int m, int kq, int R) { return uint32_t(kq * R + min(m, R - 1)); }
 
-template <bool TER, int BMAX, int RPW, int PF, bool ONE_SLAB>
-__global__ MBD_BQ_ATTRS(TER, BMAX) void gemv_bq_kernel(BqArgs a) {
-    const uint16_t* x = a.x;
-    float* y = a.y;
-    const int K = a.K, M = a.M;
-    bq_core<TER, BMAX, RPW, PF, ONE_SLAB>(
-        a, a.codes, a.scales, blockIdx.x * a.rows_per_block, a.B,
-        [=](int b) { return x + (size_t)b * K; }, [=](int b) { return y + (size_t)b * M; });
+__device__ __forceinline__ float dpp_quad_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    return v;
 }
 
 // Routes of up to kFusedPairs (token, slot) pairs are grouped inside the expert
@@ -571,40 +194,6 @@ __global__ __launch_bounds__(1024) void moe_group_sort_kernel(const int* __restr
     if (threadIdx.x == 0) *n_jobs = total;
 }
 
-template <bool TER, int BMAX, int RPW, int PF, bool ONE_SLAB>
-__global__ MBD_BQ_ATTRS(TER, BMAX) void moe_bq_kernel(BqArgs a) {
-    __shared__ int g[6][kFusedPairs];
-    __shared__ int4 gjob;
-    const int job = blockIdx.x / a.row_blocks, rb = blockIdx.x - job * a.row_blocks;
-    int4 jd;
-    const int* pids;
-    if (a.route) {
-        if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
-        moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, BMAX, g);
-        for (int q = threadIdx.x; q < a.n_pairs; q += blockDim.x)
-            if (g[4][q] >= 0 && g[1][q] == job) gjob = make_int4(g[4][q] >> 5, q, g[4][q] & 31, 0);
-        __syncthreads();
-        jd = gjob;
-        if (jd.x < 0) return;
-        pids = g[5] + jd.y;
-    } else {
-        if (job >= *a.n_jobs) return;
-        jd = a.jobs[job];
-        pids = a.pair_ids + jd.y;
-    }
-    const int e = jd.x, nb = jd.z;
-    const uint16_t* x = a.x;
-    float* y = a.y;
-    const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
-    const size_t per_codes = (size_t)a.M * a.C, per_scales = (size_t)a.M * (a.K / 128);
-    bq_core<TER, BMAX, RPW, PF, ONE_SLAB>(
-        a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * a.rows_per_block, nb,
-        [=](int b) {
-            const int p = pids[b];
-            return x + (size_t)(xpp ? p : p / topk) * K;
-        },
-        [=](int b) { return y + (size_t)pids[b] * M; });
-}
 
 // Group (token, slot) pairs by expert: a wave per expert counts its pairs with
 // ballots, one wave scans the counts into pair and job offsets, and the pairs
@@ -659,6 +248,226 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
     }
 }
 
+// ------------------------------------------------------------------ batch 1
+//
+// One activation row: only one of the MFMA's 16 output columns is used (B holds
+// the activations broadcast to every column), but the multiply-adds leave the
+// VALU.  A block owns one 16-row tile; its waves take contiguous runs of items
+// (INT4: groups; ternary: group pairs), in rounds when K is long.  Each wave
+// stages what its own items need in its own LDS area, so no wave waits for
+// another before computing:
+//   rec[g][kq]  80 bytes: activations of columns [128g + 32kq, +32) (ternary:
+//               divided by 4^class, exact, so that one accumulator covers the
+//               three position classes of the unpack) and the group's -bias
+//               four times, the initial C of the group's MFMA chain;
+//   sct[g][16]  the tile's fp16 scales of group g.
+// bias = sum over the group of (code value - q) x: 136 sum x for INT4 (code value
+// q + 136), sum (1 + 128 / 4^class) x for ternary (code value 128 + (q + 1) 4^class
+// against x / 4^class).  The waves' partial rows meet in LDS at the end.
+constexpr int B1_REC = 80;
+constexpr int B1_GROUP_LDS = 4 * B1_REC + 32;   // LDS bytes per staged group
+constexpr int B1_MAXG = 16;                     // groups one wave stages per round (4 jobs each)
+
+struct B1Args {
+    const uint8_t* codes;   // tile-interleaved codes of n_mats matrices
+    const uint16_t* scales; // [n_mats][M][K / 128]
+    const uint16_t* x;
+    float* y;
+    int M, K;
+    int ipw;                // items per wave per round
+    int tiles;              // 16-row tiles per matrix
+    // expert mode
+    const int4* jobs;       // {expert, pair_start, n_pairs, 0}
+    const int* n_jobs;
+    const int* pair_ids;    // pairs sorted by expert: pair id = t*k + slot
+    const int* route;       // set: group the routes inside the kernel (n_pairs <= kFusedPairs)
+    int n_pairs, n_experts, topk, x_per_pair;
+};
+
+// Rows of tile `tile` of one matrix against one activation row x; y is that
+// matrix's output row.
+template <bool TER, int PF>
+__device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restrict__ codes,
+                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ x,
+                                        float* __restrict__ y, int tile) {
+    constexpr int IG = TER ? 2 : 1;                  // groups per item
+    extern __shared__ uint4 lds4[];
+    char* lds = reinterpret_cast<char*>(lds4);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int M = a.M, K = a.K, ngroups = K >> 7;
+    const int n_items = TER ? (ngroups + 1) >> 1 : ngroups;
+    const int n_full = TER ? ngroups >> 1 : ngroups;          // items of 16-byte units
+    const int m = lane & 15, kq = lane >> 4;
+    const int row0 = tile * 16, R = min(16, M - row0);
+    const uint8_t* tcodes = codes + size_t(row0) * (size_t(K) / (TER ? 4 : 2));
+    const uint32_t unit = tile_unit(m, kq, R);
+    const int wg = a.ipw * IG;                                // groups a wave stages per round
+    char* rec = lds + wave * wg * B1_GROUP_LDS;               // [wg][4][B1_REC]
+    uint16_t* sct = reinterpret_cast<uint16_t*>(rec + wg * 4 * B1_REC);     // [wg][16]
+    float* red = reinterpret_cast<float*>(lds + nw * wg * B1_GROUP_LDS);    // [nw][16]
+    UnpackConsts kc;
+    kc.init();
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+
+    for (int rb = 0; rb < n_items; rb += nw * a.ipw) {
+        const int it0 = rb + wave * a.ipw;
+        const int n = min(a.ipw, n_items - it0);
+        if (n <= 0) continue;
+        const int g0 = it0 * IG, ng = min(n * IG, ngroups - g0);
+
+        // Staging loads first (vector-memory counters retire in issue order, so the
+        // staging waits do not wait for the code stream).  Job j = (local group
+        // j / 4, quarter j % 4); lanes past the last job redo the last group's jobs
+        // (the same values into the same slots).
+        const int j = min(lane, 4 * ng - 4 + (lane & 3));
+        const int sgl = j >> 2, skq = j & 3;
+        uint4 xv[4];
+        {
+            const uint4* xs = reinterpret_cast<const uint4*>(x + (g0 + sgl) * 128 + skq * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = xs[i];
+        }
+        // scale entry e = (local group e / 16, tile row e % 16), four per lane
+        uint32_t sv[4];
+        int se[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            se[u] = min(lane + 64 * u, 16 * ng - 1);
+            sv[u] = scales[size_t(row0 + min(se[u] & 15, R - 1)) * ngroups + g0 + (se[u] >> 4)];
+        }
+
+        // The odd last ternary group has 8-byte units: its 16-byte load takes the
+        // unit in the low half and 8 bytes past it, which lie inside the codes
+        // section or its padding (a load of one width keeps the waits exact).
+        uint4 w[PF];
+        auto issue = [&](int p, int i) __attribute__((always_inline)) {
+            const int it = it0 + i;
+            const uint32_t off = (TER && it >= n_full) ? unit * 8 : unit * 16;
+            const u32x4_t v = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(tcodes + size_t(it) * 64 * R + off));
+            w[p] = make_uint4(v.x, v.y, v.z, v.w);
+        };
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(p, min(p, n - 1));
+        __builtin_amdgcn_sched_barrier(0);
+
+        {
+            float part = 0.f;
+            uint32_t xo[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t v4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float lo = bf16_to_f32(v4[jj] & 0xFFFFu), hi = bf16_to_f32(v4[jj] >> 16);
+                    if constexpr (TER) {
+                        // columns 8i + 2jj, +1 of the 32 (a multiple of 16 from a word
+                        // start): pair (4i + jj) % 8 of the word, class pair % 3
+                        const int cls = ((4 * i + jj) & 7) % 3;
+                        const float f = cls == 0 ? 1.f : (cls == 1 ? 0.25f : 0.0625f);
+                        part += (1.f + 128.f * f) * (lo + hi);
+                        xo[4 * i + jj] = (__float_as_uint(lo * f) >> 16) | (__float_as_uint(hi * f) & 0xFFFF0000u);
+                    } else {
+                        part += lo + hi;
+                        xo[4 * i + jj] = v4[jj];
+                    }
+                }
+            }
+            part = dpp_quad_sum(part);      // the 4 jobs of a group are one lane quad
+            const float nb = TER ? -part : -136.f * part;
+            uint4* r = reinterpret_cast<uint4*>(rec + (sgl * 4 + skq) * B1_REC);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = make_uint4(xo[4 * i], xo[4 * i + 1], xo[4 * i + 2], xo[4 * i + 3]);
+            r[4] = make_uint4(__float_as_uint(nb), __float_as_uint(nb), __float_as_uint(nb), __float_as_uint(nb));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sct[(se[u] >> 4) * 16 + (se[u] & 15)] = uint16_t(sv[u]);
+            // a wave's LDS operations complete in order: its own stores are visible
+            // to all its lanes once they have completed
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+
+        auto group = [&](const uint4 gw, int lg) __attribute__((always_inline)) {
+            const char* r = rec + (lg * 4 + kq) * B1_REC;
+            f32x4_t c = *reinterpret_cast<const f32x4_t*>(r + 64);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(code_operand<TER>(gw, s, kc),
+                                                            *reinterpret_cast<const bf16x8_t*>(r + 16 * s), c, 0, 0, 0);
+            const uint2 sc = *reinterpret_cast<const uint2*>(sct + lg * 16 + 4 * kq);
+            acc[0] = fmaf(half_bits_to_f32(uint16_t(sc.x)), c[0], acc[0]);
+            acc[1] = fmaf(half_bits_to_f32(uint16_t(sc.x >> 16)), c[1], acc[1]);
+            acc[2] = fmaf(half_bits_to_f32(uint16_t(sc.y)), c[2], acc[2]);
+            acc[3] = fmaf(half_bits_to_f32(uint16_t(sc.y >> 16)), c[3], acc[3]);
+        };
+        auto compute = [&](int p, int i) __attribute__((always_inline)) {
+            group(w[p], i * IG);
+            if (TER && it0 + i < n_full) group(make_uint4(w[p].z, w[p].w, 0u, 0u), i * IG + 1);
+        };
+        int i = 0;
+        for (; i + PF < n; i += PF) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                compute(p, i + p);
+                issue(p, min(i + p + PF, n - 1));
+                __builtin_amdgcn_sched_barrier(0);   // refill each slot as soon as it is consumed
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+            if (i + p < n) compute(p, i + p);
+    }
+
+    // C[row 4kq + jj][column m]: every column holds the same sums
+    if (m == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) red[wave * 16 + 4 * kq + jj] = acc[jj];
+    }
+    __syncthreads();
+    if (int(threadIdx.x) < R) {
+        float s = 0.f;
+        for (int v = 0; v < nw; ++v) s += red[v * 16 + threadIdx.x];
+        y[row0 + threadIdx.x] = s;
+    }
+}
+
+template <bool TER, int PF>
+__global__ __launch_bounds__(1024) void gemv_b1_kernel(B1Args a) {
+    b1_core<TER, PF>(a, a.codes, a.scales, a.x, a.y, blockIdx.x);
+}
+
+// One token per expert job: block (job, tile).  Routes of at most kFusedPairs
+// pairs are grouped inside the kernel (every block redoes it: cheap only while
+// the route is short), longer ones by the grouping kernels.
+template <bool TER, int PF>
+__global__ __launch_bounds__(1024) void moe_b1_kernel(B1Args a) {
+    __shared__ int g[6][kFusedPairs];
+    __shared__ int4 gjob;
+    const int job = blockIdx.x / a.tiles, tile = blockIdx.x - job * a.tiles;
+    int4 jd;
+    const int* pids;
+    if (a.route) {
+        if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
+        moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, 1, g);
+        for (int q = threadIdx.x; q < a.n_pairs; q += blockDim.x)
+            if (g[4][q] >= 0 && g[1][q] == job) gjob = make_int4(g[4][q] >> 5, q, g[4][q] & 31, 0);
+        __syncthreads();
+        jd = gjob;
+        if (jd.x < 0) return;
+        pids = g[5] + jd.y;
+    } else {
+        if (job >= *a.n_jobs) return;
+        jd = a.jobs[job];
+        pids = a.pair_ids + jd.y;
+    }
+    const int e = jd.x, p = pids[0];
+    const int K = a.K, M = a.M;
+    const size_t per_codes = size_t(M) * K / (TER ? 4 : 2), per_scales = size_t(M) * (K / 128);
+    b1_core<TER, PF>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales,
+                     a.x + size_t(a.x_per_pair ? p : p / a.topk) * K, a.y + size_t(p) * M, tile);
+}
+
 // ------------------------------------------------------------------ batch >= 2: MFMA
 
 // Batch 2..16 is a skinny GEMM: the codes become bf16 MFMA operands directly.
@@ -670,11 +479,11 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
 // 16-row tiles) by all of K; its waves take the 128-column groups round robin,
 // with the next group's loads in flight while one is computed, and the waves'
 // partial tiles are summed at the end.  Lane (n, q) = (lane % 16, lane / 16)
-// holds columns [32q, 32q + 32) of the group for weight row n of each tile and
-// for batch row n; MFMA sub-step s uses columns 32q + 8s .. + 8 on both operands,
-// so every k slot sees the same column on A and B.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// holds columns [32q, 32q + 32) of the group for weight row n of each tile (the
+// tile-interleaved unit (n, q)) and for batch row n; MFMA sub-step s uses columns
+// 32q + 8s .. + 8 on both operands, so every k slot sees the same column on A and
+// B.  Ternary waves take group pairs, so that the two 8-byte halves of each
+// 16-byte unit are loaded back to back.
 
 constexpr int MQ_TILES = 2;
 constexpr int MQ_MAXW = 16;
@@ -706,8 +515,10 @@ struct MqArgs {
     int n_pairs, n_experts, topk, x_per_pair, row_blocks, B;
 };
 
+// A operand of MFMA step s from the lane's codes of one group, every pair shifted
+// to mantissa bits 0.. (value q + K0): the activations here are the raw rows.
 template <bool TER>
-__device__ __forceinline__ uint4 mq_unpack(const uint4 c, int s) {
+__device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s) {
     uint32_t o[4];
     if constexpr (TER) {
         const uint32_t w = (s < 2) ? c.x : c.y;        // 16 codes per word
@@ -719,7 +530,7 @@ __device__ __forceinline__ uint4 mq_unpack(const uint4 c, int s) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) o[p] = ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
     }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 // Rows [row_base, row_base + 32) of one matrix; nb <= 16 batch rows whose
@@ -736,11 +547,17 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     const int n = lane & 15, q = lane >> 4;
     const int K = a.K, M = a.M, ngroups = K >> 7;
     const size_t row_bytes = size_t(K) / BPR;
-    int rowc[MQ_TILES];                                    // weight rows this lane loads (clamped)
+    const int npairs = ngroups >> 1;                       // ternary: full group pairs
+    const uint8_t* tcode[MQ_TILES];                        // tile base (a tile past M: the last tile)
+    uint32_t unit[MQ_TILES];
+    int tR[MQ_TILES];
     int orow[MQ_TILES];                                    // first output row of this lane in each tile
 #pragma unroll
     for (int t = 0; t < MQ_TILES; ++t) {
-        rowc[t] = min(row_base + 16 * t + n, M - 1);
+        const int r0 = min(row_base + 16 * t, (M - 1) & ~15);
+        tR[t] = min(16, M - r0);
+        tcode[t] = codes + size_t(r0) * row_bytes;
+        unit[t] = tile_unit(n, q, tR[t]);
         orow[t] = row_base + 16 * t + 4 * q;
     }
     const bool xlive = n < nb;
@@ -748,12 +565,15 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     auto load = [&](int g, MqGroup& d) {
 #pragma unroll
         for (int t = 0; t < MQ_TILES; ++t) {
-            const uint8_t* cp = codes + size_t(rowc[t]) * row_bytes + size_t(g) * (128 / BPR) + q * (32 / BPR);
+            const size_t item = 64 * size_t(tR[t]);
             if constexpr (TER) {
+                const int h = g >> 1;
+                const uint8_t* cp = h < npairs ? tcode[t] + h * item + unit[t] * 16 + (g & 1) * 8
+                                               : tcode[t] + npairs * item + unit[t] * 8;
                 const uint2 v = *reinterpret_cast<const uint2*>(cp);
                 d.code[t] = make_uint4(v.x, v.y, 0u, 0u);
             } else {
-                d.code[t] = *reinterpret_cast<const uint4*>(cp);
+                d.code[t] = *reinterpret_cast<const uint4*>(tcode[t] + g * item + unit[t] * 16);
             }
             uint32_t sv[4];
 #pragma unroll
@@ -788,7 +608,7 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             f32x4_t cg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, mq_unpack<TER>(d.code[t], s)),
+                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(d.code[t], s),
                                                              __builtin_bit_cast(bf16x8_t, xb[s]), cg, 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -797,16 +617,21 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             }
         }
     };
+    // This wave's groups, in order: INT4 wave, wave + nw, ...; ternary the pairs
+    // (2h, 2h + 1) for h = wave, wave + nw, ... (the odd last group alone).
+    const int nitems = TER ? (ngroups + 1) >> 1 : ngroups;
+    const int mine = wave < nitems ? (nitems - 1 - wave) / nw + 1 : 0;
+    const bool odd_tail = TER && (ngroups & 1) && mine > 0 && wave + nw * (mine - 1) == npairs;
+    const int cnt = TER ? 2 * mine - (odd_tail ? 1 : 0) : mine;
+    auto gidx = [&](int i) { return TER ? 2 * (wave + nw * (i >> 1)) + (i & 1) : wave + nw * i; };
     // two group buffers, so a buffer is never copied while its loads are in flight
     MqGroup g0, g1;
-    int g = wave;
-    if (g < ngroups) load(g, g0);
-    for (; g < ngroups; g += 2 * nw) {
-        const int gn = g + nw;
-        load(min(gn, ngroups - 1), g1);
+    if (cnt > 0) load(gidx(0), g0);
+    for (int i = 0; i < cnt; i += 2) {
+        load(gidx(min(i + 1, cnt - 1)), g1);
         compute(g0);
-        load(min(gn + nw, ngroups - 1), g0);
-        if (gn < ngroups) compute(g1);
+        load(gidx(min(i + 2, cnt - 1)), g0);
+        if (i + 1 < cnt) compute(g1);
     }
 #pragma unroll
     for (int t = 0; t < MQ_TILES; ++t)
@@ -875,34 +700,48 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
         [=](int b) { return y + (size_t)pids[b] * M; });
 }
 
-// Dense dequant of ternary / INT4: one thread per 16-byte chunk.  Element t of a
-// word sits at bit (bits * (t / 2)) + (t odd ? 16 : 0).
+// Dense dequant of ternary / INT4: one thread per (row, group, quarter), 32
+// elements.  Element t of a word sits at bit (bits * (t / 2)) + (t odd ? 16 : 0).
 template <bool TER>
-__global__ __launch_bounds__(256) void dequant_bq_kernel(const uint4* __restrict__ codes,
+__global__ __launch_bounds__(256) void dequant_bq_kernel(const uint8_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales, float* __restrict__ out,
-                                                         int64_t n_chunks, int C, int K) {
-    using F = Fmt<TER>;
+                                                         int64_t n_units, int M, int K) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_chunks) return;
-    const int64_t row = i / C, c = i - row * C;
-    const float s = half_bits_to_f32(scales[row * (K / 128) + c / F::CPG]);
-    const uint4 w = codes[i];
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    float4* o = reinterpret_cast<float4*>(out + row * K + c * F::WPC);
-    constexpr int bits = TER ? 2 : 4, per = TER ? 16 : 8, off = TER ? 1 : 8;
+    if (i >= n_units) return;
+    const int ngroups = K >> 7;
+    const int kq = int(i & 3);
+    const int64_t rg = i >> 2, row = rg / ngroups;
+    const int g = int(rg - row * ngroups);
+    const int64_t r0 = row & ~int64_t(15);
+    const int R = int(M - r0 < 16 ? M - r0 : 16);
+    const uint32_t unit = tile_unit(int(row - r0), kq, R);
+    const uint8_t* tc = codes + size_t(r0) * (size_t(K) / (TER ? 4 : 2));
+    uint32_t wv[4];
+    if constexpr (TER) {
+        const int P = ngroups >> 1, h = g >> 1;
+        const uint2 v = h < P ? *reinterpret_cast<const uint2*>(tc + size_t(h) * 64 * R + unit * 16 + (g & 1) * 8)
+                              : *reinterpret_cast<const uint2*>(tc + size_t(P) * 64 * R + unit * 8);
+        wv[0] = v.x; wv[1] = v.y;
+    } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(tc + size_t(g) * 64 * R + unit * 16);
+        wv[0] = v.x; wv[1] = v.y; wv[2] = v.z; wv[3] = v.w;
+    }
+    const float s = half_bits_to_f32(scales[row * ngroups + g]);
+    float4* o = reinterpret_cast<float4*>(out + row * K + g * 128 + kq * 32);
+    constexpr int bits = TER ? 2 : 4, per = TER ? 16 : 8, off = TER ? 1 : 8, nwd = TER ? 2 : 4;
     constexpr uint32_t mask = (1u << bits) - 1;
 #pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
+    for (int wi = 0; wi < nwd; ++wi) {
 #pragma unroll
-        for (int j = 0; j < per; j += 4) {
+        for (int jj = 0; jj < per; jj += 4) {
             float e[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int t = j + u;
+                const int t = jj + u;
                 const int sh = bits * (t >> 1) + ((t & 1) ? 16 : 0);
                 e[u] = s * (float)((int)((wv[wi] >> sh) & mask) - off);
             }
-            o[(wi * per + j) / 4] = make_float4(e[0], e[1], e[2], e[3]);
+            o[(wi * per + jj) / 4] = make_float4(e[0], e[1], e[2], e[3]);
         }
     }
 }
@@ -923,116 +762,30 @@ mbd_status hip_check(const char* what) {
     return MBD_OK;
 }
 
-constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+#ifndef MBD_B1_IPW
+#define MBD_B1_IPW 4          // batch 1: items per wave at least (4 KB of codes)
+#endif
+#ifndef MBD_B1_PF
+#define MBD_B1_PF 2           // batch 1: items in flight per wave (1 KB each)
+#endif
 
-struct BqPlan {
-    int C, G, RS, RPW, PF, nw, rows_per_block, SC, blocks;
-    int tile_rows, n_iter;
+struct B1Plan {
+    int ipw, nw;
     size_t lds;
-    bool one_slab;   // all activations staged at once, one staging job per thread at most
-    bool wide;       // short rows: the many-rows-per-wave shape
 };
 
-#ifndef MBD_MAX_TILES
-#define MBD_MAX_TILES 2       // row tiles one workgroup walks at most
-#endif
-#ifndef MBD_MOE_BLOCKS
-#define MBD_MOE_BLOCKS 512
-#endif
-
-// min_blocks: shrink the workgroup until the grid has at least this many blocks.
-// n_mats: matrices the call covers (the grid is n_mats times the plan's blocks).
-// In the single-slab kernel a block then walks several row tiles when there are
-// more tiles than about one round of resident workgroups, so its staged
-// activations serve more rows.
-BqPlan plan_bq(bool ter, int64_t M, int64_t K, int bmax, int min_blocks, int prefer_nw = MBD_MAX_WAVES,
-               int64_t n_mats = 1) {
-    BqPlan p{};
-    const int wpc = ter ? 64 : 32, xq = ter ? 8 : 4;   // uint4 of activations per chunk
-    p.C = int(K / wpc);
-    p.G = 64;
-    while (p.C % p.G) p.G >>= 1;
-    p.RS = 64 / p.G;
-    p.wide = bmax == 1 && p.C / p.G <= 2 && M * n_mats * p.G >= int64_t(2048) * 64 * MBD_WIDE_RPW;
-    if (p.wide) {
-        p.RPW = MBD_WIDE_RPW; p.PF = 1;
-    } else {
-        p.RPW = ter ? Shape<true, 1>::RPW : Shape<false, 1>::RPW;
-        p.PF = ter ? Shape<true, 1>::PF : Shape<false, 1>::PF;
-    }
-    p.nw = bmax == 1 ? prefer_nw : MBD_BN_WAVES;
-    // batch 1: grow the workgroup (up to 16 waves) when that lets every staging
-    // job fit in one pass, i.e. the single-slab kernel
-    if (bmax == 1 && p.C > 64 * p.nw && p.C <= 64 * 16) p.nw = 16;
-    auto tiles_for = [&](int nw) {
-        const int64_t tr = int64_t(nw) * p.RS * p.RPW;
-        return (M + tr - 1) / tr;
-    };
-    while (p.nw > 1 && tiles_for(p.nw) < min_blocks) p.nw >>= 1;
-    p.tile_rows = p.nw * p.RS * p.RPW;
-    const int64_t tiles = tiles_for(p.nw);
-    const size_t per_chunk = size_t(bmax) * (xq * 16 + 4);
-    int sc = int(std::min<size_t>(p.C, (64 * 1024) / per_chunk));
-    if (sc < p.C) {
-        const int unit = p.G * p.PF;   // a partial slab must keep the load ring aligned
-        sc = std::max(unit, (sc / unit) * unit);
-    }
-    p.SC = sc;
-    p.lds = size_t(bmax) * sc * (xq * 16 + 4);   // <= 160 KiB: checked by the caller
-    const int64_t ngroups = K / 128;
-    const int64_t scale_cap = int64_t(bmax == 1 ? ScaleLoads<1>::N : ScaleLoads<2>::N) * 64 * p.nw;
-    p.one_slab = sc >= p.C && int64_t(bmax) * p.C <= int64_t(64) * p.nw && p.C <= 4096 &&
-                 int64_t(p.tile_rows) * ngroups <= scale_cap;
-    p.n_iter = 1;
-    if (p.one_slab) {
-        // about one round of resident workgroups (waves per CU: 8 per SIMD at
-        // batch 1, 4 above), at least min_blocks
-        const int64_t waves_per_cu = bmax == 1 ? 32 : 16;
-        const int64_t round = std::max<int64_t>(min_blocks, 256 * waves_per_cu / p.nw / std::max<int64_t>(1, n_mats));
-        int64_t it = std::max<int64_t>(1, tiles / round);
-        it = std::min<int64_t>(it, scale_cap / (int64_t(p.tile_rows) * ngroups));
-        it = std::min<int64_t>(it, MBD_MAX_TILES);
-        p.n_iter = int(std::max<int64_t>(1, it));
-    }
-    p.rows_per_block = p.n_iter * p.tile_rows;
-    p.blocks = int((M + p.rows_per_block - 1) / p.rows_per_block);
-    if (p.one_slab) p.lds += size_t(p.rows_per_block) * ngroups * 2;     // staged scales
+// Waves per 16-row tile and items per wave: at least MBD_B1_IPW items per wave,
+// up to 16 waves, and at most B1_MAXG groups staged per wave and round.
+B1Plan plan_b1(bool ter, int64_t K) {
+    B1Plan p{};
+    const int64_t ngroups = K / 128, n_items = ter ? (ngroups + 1) / 2 : ngroups;
+    const int64_t max_ipw = B1_MAXG / (ter ? 2 : 1);
+    int64_t ipw = std::max<int64_t>(MBD_B1_IPW, (n_items + 15) / 16);
+    ipw = std::min<int64_t>(std::min<int64_t>(ipw, max_ipw), n_items);
+    p.ipw = int(ipw);
+    p.nw = int(std::min<int64_t>(16, (n_items + ipw - 1) / ipw));
+    p.lds = size_t(p.nw) * size_t(ipw) * (ter ? 2 : 1) * B1_GROUP_LDS + size_t(p.nw) * 64;
     return p;
-}
-
-// Batch-1 kernel variants: (rows per wave, ring depth) x single/multi slab.
-#define MBD_BQ_DISPATCH(KERNEL, TER, pl, bmax, grid, st, a, what)                                        \
-    do {                                                                                                  \
-        dim3 blk_(64 * (pl).nw);                                                                          \
-        auto go_ = [&](auto kern) {                                                                       \
-            hipLaunchKernelGGL(kern, dim3(grid), blk_, (pl).lds, st, a);                                  \
-            return hip_check(what);                                                                       \
-        };                                                                                                \
-        const bool os_ = (pl).one_slab;                                                                   \
-        if ((pl).wide) {                                                                                  \
-            constexpr int WR = WideShape<TER, 1>::RPW;                                                    \
-            return os_ ? go_(KERNEL<TER, 1, WR, 1, true>) : go_(KERNEL<TER, 1, WR, 1, false>);             \
-        } else if (bmax == 1) {                                                                           \
-            constexpr int R1 = Shape<TER, 1>::RPW, P1 = Shape<TER, 1>::PF;                                \
-            return os_ ? go_(KERNEL<TER, 1, R1, P1, true>) : go_(KERNEL<TER, 1, R1, P1, false>);           \
-        }                                                                                                 \
-        return fail(MBD_EINVAL, "no kernel variant for batch %d", bmax);                                  \
-    } while (0)
-
-template <bool TER>
-mbd_status launch_gemv_bq(const BqPlan& pl, BqArgs a, int bmax, hipStream_t st) {
-    MBD_BQ_DISPATCH(gemv_bq_kernel, TER, pl, bmax, pl.blocks, st, a, "gemv launch");
-}
-
-template <bool TER>
-mbd_status launch_moe_bq(const BqPlan& pl, BqArgs a, int bmax, int grid_blocks, hipStream_t st) {
-    MBD_BQ_DISPATCH(moe_bq_kernel, TER, pl, bmax, grid_blocks, st, a, "expert gemv launch");
-}
-
-int round_batch(int B) {
-    int b = 1;
-    while (b < B) b <<= 1;
-    return b;
 }
 
 }  // namespace
@@ -1071,18 +824,15 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         else hipLaunchKernelGGL(gemv_mq_kernel<false>, dim3(blocks), dim3(64 * nw), 0, st, m);
         return hip_check("batched gemv launch");
     }
-    const int bmax = round_batch(B);
-    BqPlan pl = plan_bq(ter, w->M, w->K, bmax, 512);
-    if (pl.lds > kMaxLds) return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
-    BqArgs a{};
-    a.codes = static_cast<const uint4*>(w->sec[0]);
+    const B1Plan pl = plan_b1(ter, w->K);
+    B1Args a{};
+    a.codes = static_cast<const uint8_t*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
-    a.x = x;
-    a.y = y;
-    a.M = int(w->M); a.K = int(w->K); a.C = pl.C; a.G = pl.G; a.SC = pl.SC; a.B = B;
-    a.gshift = __builtin_ctz(unsigned(pl.G)); a.inv_c = 1.0f / float(pl.C);
-    a.rows_per_block = pl.rows_per_block; a.tile_rows = pl.tile_rows; a.n_iter = pl.n_iter;
-    return ter ? launch_gemv_bq<true>(pl, a, bmax, st) : launch_gemv_bq<false>(pl, a, bmax, st);
+    a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
+    a.tiles = int((w->M + 15) / 16);
+    if (ter) hipLaunchKernelGGL((gemv_b1_kernel<true, MBD_B1_PF>), dim3(a.tiles), dim3(64 * pl.nw), pl.lds, st, a);
+    else hipLaunchKernelGGL((gemv_b1_kernel<false, MBD_B1_PF>), dim3(a.tiles), dim3(64 * pl.nw), pl.lds, st, a);
+    return hip_check("gemv launch");
 }
 
 mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
@@ -1093,19 +843,21 @@ mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128)
         return fail(MBD_EINVAL, "dequant supports TERNARY, INT4 and MX32");
     if (w->M < 0 || w->K < 1 || w->K % 128) return fail(MBD_ESHAPE, "bad shape");
+    if (w->M > INT32_MAX || w->K > INT32_MAX) return fail(MBD_ESHAPE, "shape too large");
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2)) return fail(MBD_EALIGN, "codes must be 16-byte aligned");
     if (w->M == 0) return MBD_OK;
     const bool ter = w->fmt == MBD_TERNARY_B128;
-    const int C = int(w->K / (ter ? 64 : 32));
-    const int64_t n = w->M * C;
+    const int64_t n = w->M * (w->K / 128) * 4;
     const unsigned blocks = unsigned((n + 255) / 256);
     if (ter)
         hipLaunchKernelGGL((dequant_bq_kernel<true>), dim3(blocks), dim3(256), 0, st,
-                           static_cast<const uint4*>(w->sec[0]), static_cast<const uint16_t*>(w->sec[1]), out, n, C, int(w->K));
+                           static_cast<const uint8_t*>(w->sec[0]), static_cast<const uint16_t*>(w->sec[1]), out, n,
+                           int(w->M), int(w->K));
     else
         hipLaunchKernelGGL((dequant_bq_kernel<false>), dim3(blocks), dim3(256), 0, st,
-                           static_cast<const uint4*>(w->sec[0]), static_cast<const uint16_t*>(w->sec[1]), out, n, C, int(w->K));
+                           static_cast<const uint8_t*>(w->sec[0]), static_cast<const uint16_t*>(w->sec[1]), out, n,
+                           int(w->M), int(w->K));
     return hip_check("dequant launch");
 }
 
@@ -1172,25 +924,20 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
         return hip_check("expert gemv launch");
     }
     const bool ter = w->fmt == MBD_TERNARY_B128;
-    // about MBD_MOE_BLOCKS workgroups over the whole call
-    const int min_blocks = int(std::max<int64_t>(1, MBD_MOE_BLOCKS / std::max<int64_t>(1, D)));
-    BqPlan pl = plan_bq(ter, w->M, w->K, bmax, min_blocks, 16, D);
-    if (pl.lds + sizeof(int) * 6 * kFusedPairs + 16 > kMaxLds)
-        return fail(MBD_ESHAPE, "activation slab needs %zu bytes of LDS", pl.lds);
-    BqArgs a{};
-    a.codes = static_cast<const uint4*>(w->sec[0]);
+    const B1Plan pl = plan_b1(ter, w->K);
+    B1Args a{};
+    a.codes = static_cast<const uint8_t*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
-    a.x = x; a.y = y;
-    a.M = int(w->M); a.K = int(w->K); a.C = pl.C; a.G = pl.G; a.SC = pl.SC; a.B = 0;
-    a.gshift = __builtin_ctz(unsigned(pl.G)); a.inv_c = 1.0f / float(pl.C);
-    a.rows_per_block = pl.rows_per_block; a.tile_rows = pl.tile_rows; a.n_iter = pl.n_iter;
+    a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
+    a.tiles = int((w->M + 15) / 16);
     a.jobs = jobs; a.n_jobs = n_jobs; a.pair_ids = pair_ids;
-    a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0; a.row_blocks = pl.blocks;
     a.route = fused ? route : nullptr;
-    a.n_pairs = P; a.n_experts = E;
-    const int64_t grid = max_jobs * pl.blocks;
+    a.n_pairs = P; a.n_experts = E; a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0;
+    const int64_t grid = max_jobs * a.tiles;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-    return ter ? launch_moe_bq<true>(pl, a, bmax, int(grid), st) : launch_moe_bq<false>(pl, a, bmax, int(grid), st);
+    if (ter) hipLaunchKernelGGL((moe_b1_kernel<true, MBD_B1_PF>), dim3(unsigned(grid)), dim3(64 * pl.nw), pl.lds, st, a);
+    else hipLaunchKernelGGL((moe_b1_kernel<false, MBD_B1_PF>), dim3(unsigned(grid)), dim3(64 * pl.nw), pl.lds, st, a);
+    return hip_check("expert gemv launch");
 }
 
 }  // extern "C"

@@ -95,8 +95,22 @@ void parallel_rows(int64_t M, F&& f) {
 
 // ------------------------------------------------------------------ ternary / INT4
 
-mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary) {
-    const int64_t M = h->M, K = h->K, G = K / 128;
+// Word offset of word wd (0 .. 128/cpw - 1) of group g of row m in the
+// tile-interleaved code order, for a stack of matrices of Mm rows each.
+int64_t code_word_offset(bool ternary, int64_t m, int64_t g, int wd, int64_t Mm, int64_t K) {
+    const int64_t mat = m / Mm, r = m - mat * Mm, t0 = r & ~int64_t(15);
+    const int64_t R = std::min<int64_t>(16, Mm - t0), mi = r - t0;
+    const int64_t wpr = K / (ternary ? 16 : 8);                 // words per row
+    const int64_t base = (mat * Mm + t0) * wpr;
+    if (!ternary) return base + g * 16 * R + ((wd >> 2) * R + mi) * 4 + (wd & 3);
+    const int64_t P = (K / 128) / 2;                            // full block pairs
+    const int kq = wd >> 1, j = wd & 1;
+    if (g < 2 * P) return base + (g >> 1) * 16 * R + (kq * R + mi) * 4 + (g & 1) * 2 + j;
+    return base + P * 16 * R + (kq * R + mi) * 2 + j;
+}
+
+mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary, int64_t n_mats) {
+    const int64_t M = h->M, K = h->K, G = K / 128, Mm = M / n_mats;
     const int cpw = ternary ? 16 : 8, bits = ternary ? 2 : 4;
     h->sec.resize(2);
     h->sec[0].name = "codes";
@@ -127,7 +141,6 @@ mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary) {
                 scales[m * G + g] = s;
                 double sv = fp16_to_double(s);
                 const int qmax = ternary ? 1 : 7, off = ternary ? 1 : 8;
-                uint32_t* dst = codes + (m * K + g * 128) / cpw;
                 for (int wd = 0; wd < 128 / cpw; ++wd) {
                     uint32_t word = 0;
                     // element j of the word: evens in the low half, odds in the high half
@@ -140,7 +153,7 @@ mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary) {
                         zeros[m] += (q == 0);
                         word |= uint32_t(q + off) << (bits * (j >> 1) + ((j & 1) ? 16 : 0));
                     }
-                    dst[wd] = word;
+                    codes[code_word_offset(ternary, m, g, wd, Mm, K)] = word;
                 }
             }
         }
@@ -386,7 +399,10 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w, int64_t M, int64_t K, const 
     if (K % kmul) return fail(MBD_ESHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)kmul);
     if (fmt == MBD_CASSANDRA && !act_norm) return fail(MBD_EINVAL, "Cassandra packing needs act_norm_host");
     int32_t kn = 3, kd = 10;
-    if (params) { kn = params->keep_num; kd = params->keep_den; }
+    int64_t nm = 1;
+    if (params) { kn = params->keep_num; kd = params->keep_den; nm = params->n_mats ? params->n_mats : 1; }
+    if (nm < 1 || M % nm) return fail(MBD_EINVAL, "n_mats=%lld does not divide M=%lld", (long long)nm, (long long)M);
+    if (nm > 1 && fmt != MBD_TERNARY_B128 && fmt != MBD_INT4_G128) return fail(MBD_EINVAL, "n_mats > 1 needs TERNARY or INT4");
     if (fmt == MBD_CASSANDRA && (kd < 1 || kn < 0 || kn > kd)) return fail(MBD_EINVAL, "keep fraction %d/%d", kn, kd);
     if (fmt == MBD_CASSANDRA && M * K > int64_t(UINT32_MAX)) return fail(MBD_ESHAPE, "M*K exceeds the 32-bit kept prefix");
     mbd_packed* h = nullptr;
@@ -396,8 +412,8 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w, int64_t M, int64_t K, const 
         RoundNearest rn;
         mbd_status s;
         switch (fmt) {
-            case MBD_TERNARY_B128: s = pack_block_quant(h, w, true); break;
-            case MBD_INT4_G128: s = pack_block_quant(h, w, false); break;
+            case MBD_TERNARY_B128: s = pack_block_quant(h, w, true, nm); break;
+            case MBD_INT4_G128: s = pack_block_quant(h, w, false, nm); break;
             case MBD_CASSANDRA: s = pack_cassandra(h, w, act_norm); break;
             default: s = pack_mx32(h, w); break;
         }

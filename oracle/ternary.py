@@ -18,10 +18,16 @@ Readings where the page is silent (each listed in the design notes):
 * A block whose mean is 0, or whose fp16 scale underflows to 0, gets s = 1.0
   and q = 0 (the all-zero rule).  A scale that overflows fp16 is an error.
 * Packing (parity unpinned by the pages, fixed here): code c = q + 1 in
-  {0, 1, 2}; 32-bit word w of a row holds elements 16w .. 16w+15, the even ones
-  in the low half and the odd ones in the high half: element 16w + t sits at bit
-  2*(t // 2) when t is even and at bit 16 + 2*(t // 2) when t is odd.  The words
-  of a row are contiguous, rows follow each other.
+  {0, 1, 2}.  A 32-bit word holds 16 consecutive elements of a row, the even ones
+  in the low half and the odd ones in the high half: element t of the word sits at
+  bit 2*(t // 2) when t is even and at bit 16 + 2*(t // 2) when t is odd.  Words
+  are ordered tile-interleaved: rows are taken in tiles of 16 (the last tile of a
+  matrix holds the R <= 16 rows left); a tile stores its blocks in pairs (2h,
+  2h+1), each pair as R * 4 units of 16 bytes, unit (row m of the tile, quarter
+  kq) at index kq * R + m holding columns 32kq .. +32 of block 2h (2 words) then
+  of block 2h+1 (2 words).  With an odd block count the last block is stored
+  alone as R * 4 units of 8 bytes in the same order.  A stack of matrices is
+  tiled matrix by matrix.
 """
 from __future__ import annotations
 
@@ -57,18 +63,54 @@ def quantize(w_bits: np.ndarray):
 SHIFTS = np.array([2 * (t // 2) + (16 if t % 2 else 0) for t in range(16)], dtype=np.int64)
 
 
-def pack_codes(q: np.ndarray) -> np.ndarray:
-    """q int8 [M][K] in {-1,0,1} -> uint32 [M][K/16], code q+1 at SHIFTS[k % 16]."""
+TILE = 16
+
+
+def _tiles(M: int, n_mats: int):
+    """(first row, rows) of each 16-row tile, matrix by matrix."""
+    if M % n_mats:
+        raise ValueError("rows not divisible by n_mats")
+    Mm = M // n_mats
+    for mat in range(n_mats):
+        for t0 in range(0, Mm, TILE):
+            yield mat * Mm + t0, min(TILE, Mm - t0)
+
+
+def pack_codes(q: np.ndarray, n_mats: int = 1) -> np.ndarray:
+    """q int8 [M][K] in {-1,0,1} -> uint32 [M*K/16] in tile-interleaved order."""
     M, K = q.shape
     c = (q.astype(np.int64) + 1).reshape(M, K // 16, 16)
-    return (c << SHIFTS).sum(axis=-1).astype(np.uint32)
+    words = (c << SHIFTS).sum(axis=-1).astype(np.uint32)    # [M][K/16], word w = columns 16w .. 16w+15
+    G = K // BLOCK
+    P = G // 2
+    out = []
+    for r0, R in _tiles(M, n_mats):
+        blk = words[r0:r0 + R].reshape(R, G, 4, 2)                      # [row][block][quarter][word]
+        pairs = blk[:, :2 * P].reshape(R, P, 2, 4, 2)                   # [row][pair][half][quarter][word]
+        out.append(pairs.transpose(1, 3, 0, 2, 4).reshape(-1))          # [pair][quarter][row][half][word]
+        if G % 2:
+            out.append(blk[:, 2 * P].transpose(1, 0, 2).reshape(-1))    # [quarter][row][word]
+    return np.concatenate(out)
 
 
-def unpack_codes(words: np.ndarray, K: int) -> np.ndarray:
-    """uint32 [M][K/16] -> q int8 [M][K]; raises on the unused code 3."""
-    M = words.shape[0]
+def unpack_codes(words: np.ndarray, K: int, n_mats: int = 1) -> np.ndarray:
+    """Tile-interleaved uint32 words (any shape, M*K/16 of them) -> q int8 [M][K];
+    raises on the unused code 3."""
+    flat = np.asarray(words, dtype=np.uint32).reshape(-1)
+    M = flat.size * 16 // K
+    G = K // BLOCK
+    P = G // 2
+    rows = np.empty((M, G, 4, 2), np.uint32)
+    pos = 0
+    for r0, R in _tiles(M, n_mats):
+        n = P * R * 16
+        rows[r0:r0 + R, :2 * P] = flat[pos:pos + n].reshape(P, 4, R, 2, 2).transpose(2, 0, 3, 1, 4).reshape(R, 2 * P, 4, 2)
+        pos += n
+        if G % 2:
+            rows[r0:r0 + R, 2 * P] = flat[pos:pos + 8 * R].reshape(4, R, 2).transpose(1, 0, 2)
+            pos += 8 * R
     shifts = SHIFTS.astype(np.uint32)
-    c = (words.astype(np.uint32)[..., None] >> shifts) & 3
+    c = (rows.reshape(M, K // 16)[..., None] >> shifts) & 3
     if np.any(c == 3):
         raise ValueError("invalid ternary code 3")
     return (c.astype(np.int8) - 1).reshape(M, K)
@@ -81,15 +123,16 @@ def dequant(q: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
     return (q.reshape(M, K // BLOCK, BLOCK).astype(np.float64) * s[..., None]).reshape(M, K)
 
 
-def pack(w_bits: np.ndarray) -> dict:
-    """Packed sections {'codes', 'scales'} of a bf16 weight."""
+def pack(w_bits: np.ndarray, n_mats: int = 1) -> dict:
+    """Packed sections {'codes', 'scales'} of a bf16 weight (n_mats stacked matrices)."""
     q, s = quantize(w_bits)
-    return {"codes": pack_codes(q), "scales": s}
+    return {"codes": pack_codes(q, n_mats), "scales": s}
 
 
-def unpack_dequant(codes: np.ndarray, scales: np.ndarray, K: int) -> np.ndarray:
+def unpack_dequant(codes: np.ndarray, scales: np.ndarray, K: int, n_mats: int = 1) -> np.ndarray:
     """Dense fp64 weight from the packed sections."""
-    return dequant(unpack_codes(codes, K), scales)
+    M = np.asarray(codes).size * 16 // K
+    return dequant(unpack_codes(codes, K, n_mats), np.asarray(scales).reshape(M, K // BLOCK))
 
 
 def zero_fraction(q: np.ndarray) -> float:

@@ -174,7 +174,7 @@ def _moe_setup(dev, T, which):
     mats = {e: synth.gen_expert(wl, e, which) for e in used}
     filler = mats[used[0]]
     stack = np.concatenate([mats.get(e, filler) for e in range(wl.experts)])
-    dw = mbd.to_device(mbd.mbd_pack(mbd.MBD_TERNARY_B128, stack), dev, n_mats=wl.experts)
+    dw = mbd.to_device(mbd.mbd_pack(mbd.MBD_TERNARY_B128, stack, n_mats=wl.experts), dev, n_mats=wl.experts)
     return wl, routes, mats, dw
 
 
@@ -232,7 +232,7 @@ def test_moe_ragged(dev, case):
     routes = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
     routes[T // 2, k - 1] = E                          # an id out of range: its row stays unwritten
     mats = [_rand_w(100 + e, M, K) for e in range(E)]
-    dw = mbd.to_device(mbd.mbd_pack(_fmt(kind), np.concatenate(mats)), dev, n_mats=E)
+    dw = mbd.to_device(mbd.mbd_pack(_fmt(kind), np.concatenate(mats), n_mats=E), dev, n_mats=E)
     xb = _rand_x(7, T * k if per_pair else T, K)
     ws = torch.empty(mbd.mbd_moe_workspace_bytes(E, T, k), dtype=torch.uint8, device=dev)
     y = torch.full((T, k, M), float("nan"), dtype=torch.float32, device=dev)

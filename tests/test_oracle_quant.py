@@ -52,8 +52,8 @@ def test_ternary_crafted_blocks():
     assert s[0, 2] == 0x3C00 and np.all(q[0, 256:384] == 0)
     assert sv[3] == 0.5
     assert np.all(q[0, 384:448] == 0) and np.all(q[0, 448:512] == -1)
-    codes = ternary.pack_codes(q)
-    assert np.all(codes[0, 256 // 16:384 // 16] == 0x55555555)
+    codes = ternary.pack_codes(q[:, 256:384])
+    assert np.all(codes == 0x55555555)
 
 
 def test_ternary_idempotent_codes():
@@ -86,22 +86,45 @@ def test_ternary_bruteforce_fraction():
                     assert q[m, g * 128 + i] == r
 
 
+def _tile_of(m, M):
+    """(first row, rows) of the 16-row tile that holds row m."""
+    t0 = (m // 16) * 16
+    return t0, min(16, M - t0)
+
+
+def ternary_word_index(m, k, M, K):
+    """Word holding element (m, k) in the tile-interleaved ternary layout."""
+    t0, R = _tile_of(m, M)
+    g, kq, j = k // 128, (k % 128) // 32, (k % 32) // 16
+    P = (K // 128) // 2
+    base = t0 * (K // 16)
+    if g < 2 * P:
+        return base + (g // 2) * 16 * R + (kq * R + (m - t0)) * 4 + (g % 2) * 2 + j
+    return base + P * 16 * R + (kq * R + (m - t0)) * 2 + j
+
+
 def test_ternary_pack_layout_and_sizes():
-    M, K = 3, 256
+    M, K = 19, 384                                     # a partial second tile, an odd block count
     q = np.random.default_rng(4).integers(-1, 2, (M, K)).astype(np.int8)
     words = ternary.pack_codes(q)
-    assert words.shape == (M, K // 16) and words.nbytes == M * K // 4
-    # element 16w + t at bit 2*(t//2) (t even) or 16 + 2*(t//2) (t odd) of word w
-    for (m, k) in [(0, 0), (1, 17), (2, 255), (0, 100), (1, 6), (2, 9)]:
-        t = k % 16
-        bit = 2 * (t // 2) + (16 if t % 2 else 0)
-        assert (int(words[m, k // 16]) >> bit) & 3 == q[m, k] + 1
+    assert words.shape == (M * K // 16,) and words.nbytes == M * K // 4
+    # element t of a word (t = k % 16) at bit 2*(t//2) (t even) or 16 + 2*(t//2) (t odd)
+    for m in range(M):
+        for k in range(K):
+            t = k % 16
+            bit = 2 * (t // 2) + (16 if t % 2 else 0)
+            assert (int(words[ternary_word_index(m, k, M, K)]) >> bit) & 3 == q[m, k] + 1
     one = np.zeros((1, 128), np.int8)
     one[0, 1] = 1                                      # element 1: code 2 at bit 16
-    assert ternary.pack_codes(one)[0, 0] == 0x55555555 + (1 << 16)
+    assert ternary.pack_codes(one)[0] == 0x55555555 + (1 << 16)
     np.testing.assert_array_equal(ternary.unpack_codes(words, K), q)
     with pytest.raises(ValueError):
         ternary.unpack_codes(np.full((1, 8), 0xFFFFFFFF, np.uint32), 128)
+    # a stack is tiled matrix by matrix
+    q2 = np.random.default_rng(5).integers(-1, 2, (2 * 21, 256)).astype(np.int8)
+    np.testing.assert_array_equal(ternary.pack_codes(q2, 2),
+                                  np.concatenate([ternary.pack_codes(q2[:21]), ternary.pack_codes(q2[21:])]))
+    np.testing.assert_array_equal(ternary.unpack_codes(ternary.pack_codes(q2, 2), 256, 2), q2)
 
 
 def test_ternary_scale_overflow_rejected():
@@ -163,18 +186,29 @@ def test_int4_bruteforce_fraction():
                     assert q[m, g * 128 + i] == max(-7, min(7, round_half_even(v / sf)))
 
 
+def int4_word_index(m, k, M, K):
+    """Word holding element (m, k) in the tile-interleaved INT4 layout."""
+    t0, R = _tile_of(m, M)
+    g, kq, i = k // 128, (k % 128) // 32, (k % 32) // 8
+    return t0 * (K // 8) + g * 16 * R + (kq * R + (m - t0)) * 4 + i
+
+
 def test_int4_pack_layout_and_sizes():
-    M, K = 2, 384
+    M, K = 19, 384
     q = np.random.default_rng(6).integers(-7, 8, (M, K)).astype(np.int8)
     words = int4.pack_codes(q)
     assert words.nbytes == M * K // 2
-    for (m, k) in [(0, 0), (1, 9), (1, 383), (0, 2), (1, 7)]:
-        t = k % 8
-        bit = 4 * (t // 2) + (16 if t % 2 else 0)
-        assert (int(words[m, k // 8]) >> bit) & 15 == q[m, k] + 8
+    for m in range(M):
+        for k in range(K):
+            t = k % 8
+            bit = 4 * (t // 2) + (16 if t % 2 else 0)
+            assert (int(words[int4_word_index(m, k, M, K)]) >> bit) & 15 == q[m, k] + 8
     one = np.zeros((1, 128), np.int8)
     one[0, 3] = 7                                      # element 3: code 15 at bit 20
-    assert int4.pack_codes(one)[0, 0] == 0x88888888 + (7 << 20)
+    assert int4.pack_codes(one)[0] == 0x88888888 + (7 << 20)
     np.testing.assert_array_equal(int4.unpack_codes(words, K), q)
     scales = int4.quantize(_tiny(7, M, K))[1]
     assert scales.nbytes == 2 * M * K // 128
+    q2 = np.random.default_rng(8).integers(-7, 8, (2 * 33, 128)).astype(np.int8)
+    np.testing.assert_array_equal(int4.pack_codes(q2, 2),
+                                  np.concatenate([int4.pack_codes(q2[:33]), int4.pack_codes(q2[33:])]))

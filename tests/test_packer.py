@@ -46,12 +46,29 @@ def test_moe_experts_stacked():
             w = synth.gen_expert(wl, e, which)
             p = mbd.mbd_pack(mbd.MBD_TERNARY_B128, w)
             _check_sections(p, ternary.pack(w), ["codes", "scales"])
-    # stacking expert matrices row-wise packs to the concatenation of the packings
-    a, b = synth.gen_expert(wl, 3, "up")[:64], synth.gen_expert(wl, 4, "up")[:64]
+    # a stack packed with n_mats is the concatenation of the matrices' packings, also
+    # when the rows per matrix are not a multiple of the 16-row tile
+    a, b = synth.gen_expert(wl, 3, "up")[:33], synth.gen_expert(wl, 4, "up")[:33]
     pa, pb = mbd.mbd_pack(mbd.MBD_TERNARY_B128, a), mbd.mbd_pack(mbd.MBD_TERNARY_B128, b)
-    pab = mbd.mbd_pack(mbd.MBD_TERNARY_B128, np.concatenate([a, b]))
+    pab = mbd.mbd_pack(mbd.MBD_TERNARY_B128, np.concatenate([a, b]), n_mats=2)
     np.testing.assert_array_equal(pab.section("codes", np.uint32),
                                   np.concatenate([pa.section("codes", np.uint32), pb.section("codes", np.uint32)]))
+    _check_sections(pab, ternary.pack(np.concatenate([a, b]), 2), ["codes", "scales"])
+    with pytest.raises(ValueError):
+        mbd.to_device(pab, "cpu", n_mats=1)
+    with pytest.raises(mbd.MbdError):
+        mbd.mbd_pack(mbd.MBD_TERNARY_B128, np.concatenate([a, b]), n_mats=4)
+
+
+@pytest.mark.parametrize("M,K", [(19, 384), (33, 640), (5, 128), (16, 256), (50, 1152)])
+@pytest.mark.parametrize("kind", ["ternary", "int4"])
+def test_block_quant_ragged_tiles(kind, M, K):
+    """Partial last tiles and odd block counts match the oracle's packing."""
+    w = np.ascontiguousarray(synth.gen_weights(synth.WORKLOADS["int4_8k"], 0, M)[:, :K])
+    fmt, mod = (mbd.MBD_INT4_G128, int4) if kind == "int4" else (mbd.MBD_TERNARY_B128, ternary)
+    p = mbd.mbd_pack(fmt, w)
+    _check_sections(p, mod.pack(w), ["codes", "scales"])
+    p.validate()
 
 
 CAS_NAMES = ["bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix", "lo_nib", "pruned"]
