@@ -266,7 +266,9 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
 // against x / 4^class).  The waves' partial rows meet in LDS at the end.
 constexpr int B1_REC = 80;
 constexpr int B1_GROUP_LDS = 4 * B1_REC + 32;   // LDS bytes per staged group
-constexpr int B1_MAXG = 16;                     // groups one wave stages per round (4 jobs each)
+// Groups one wave stages per round (16 staging jobs each, so at most two passes
+// of 64 lanes): more would hold enough staging registers to cost occupancy.
+constexpr int B1_MAXG = 8;
 
 struct B1Args {
     const uint8_t* codes;   // tile-interleaved codes of n_mats matrices
@@ -286,7 +288,7 @@ struct B1Args {
 
 // Rows of tile `tile` of one matrix against one activation row x; y is that
 // matrix's output row.
-template <bool TER, int PF>
+template <bool TER, int PF, int SU>
 __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, const uint16_t* __restrict__ x,
                                         float* __restrict__ y, int tile) {
@@ -319,21 +321,19 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
 
         // Staging loads first (vector-memory counters retire in issue order, so the
         // staging waits do not wait for the code stream).  Job j = (local group
-        // j / 4, quarter j % 4); lanes past the last job redo the last group's jobs
-        // (the same values into the same slots).
-        const int j = min(lane, 4 * ng - 4 + (lane & 3));
-        const int sgl = j >> 2, skq = j & 3;
-        uint4 xv[4];
-        {
-            const uint4* xs = reinterpret_cast<const uint4*>(x + (g0 + sgl) * 128 + skq * 32);
+        // j / 16, quarter j / 4 % 4, slice j % 4): 8 activations, columns
+        // 32 quarter + 8 slice .. +8 of the group.  SU passes of 64 jobs; lanes past
+        // the last job redo jobs of the last group (the same values into the same
+        // slots).  The same passes load the scale entries e = (local group e / 16,
+        // tile row e % 16).
+        uint4 xv[SU];
+        int jx[SU];
+        uint32_t sv[SU];
+        int se[SU];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = xs[i];
-        }
-        // scale entry e = (local group e / 16, tile row e % 16), four per lane
-        uint32_t sv[4];
-        int se[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < SU; ++u) {
+            jx[u] = min(lane + 64 * u, 16 * ng - 16 + (lane & 15));
+            xv[u] = *reinterpret_cast<const uint4*>(x + (g0 + (jx[u] >> 4)) * 128 + (jx[u] & 15) * 8);
             se[u] = min(lane + 64 * u, 16 * ng - 1);
             sv[u] = scales[size_t(row0 + min(se[u] & 15, R - 1)) * ngroups + g0 + (se[u] >> 4)];
         }
@@ -353,40 +353,44 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
         for (int p = 0; p < PF; ++p) issue(p, min(p, n - 1));
         __builtin_amdgcn_sched_barrier(0);
 
-        {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int sl = jx[u] & 3;                        // slice: columns 8 sl .. +8 of the quarter
+            const uint32_t v4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+            uint32_t xo[4];
             float part = 0.f;
-            uint32_t xo[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t v4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const float lo = bf16_to_f32(v4[jj] & 0xFFFFu), hi = bf16_to_f32(v4[jj] >> 16);
-                    if constexpr (TER) {
-                        // columns 8i + 2jj, +1 of the 32 (a multiple of 16 from a word
-                        // start): pair (4i + jj) % 8 of the word, class pair % 3
-                        const int cls = ((4 * i + jj) & 7) % 3;
-                        const float f = cls == 0 ? 1.f : (cls == 1 ? 0.25f : 0.0625f);
-                        part += (1.f + 128.f * f) * (lo + hi);
-                        xo[4 * i + jj] = (__float_as_uint(lo * f) >> 16) | (__float_as_uint(hi * f) & 0xFFFF0000u);
-                    } else {
-                        part += lo + hi;
-                        xo[4 * i + jj] = v4[jj];
-                    }
+            for (int jj = 0; jj < 4; ++jj) {
+                if constexpr (TER) {
+                    // columns 8 sl + 2jj, +1 (a quarter starts on a word boundary): pair
+                    // (4 sl + jj) % 8 of a 16-code word, class pair % 3, weight 1 + 128 / 4^class
+                    const int ce = jj % 3, co = (4 + jj) % 3;        // class for an even / odd slice
+                    const bool odd = sl & 1;
+                    const uint32_t wpair = odd ? (co == 0 ? 0x43014301u : co == 1 ? 0x42044204u : 0x41104110u)
+                                               : (ce == 0 ? 0x43014301u : ce == 1 ? 0x42044204u : 0x41104110u);
+                    const float f = odd ? (co == 0 ? 1.f : co == 1 ? 0.25f : 0.0625f)
+                                        : (ce == 0 ? 1.f : ce == 1 ? 0.25f : 0.0625f);
+                    part = dot2(v4[jj], wpair, part);        // 129, 33, 9 are exact in bf16
+                    const float lo = bf16_to_f32(v4[jj] & 0xFFFFu) * f, hi = bf16_to_f32(v4[jj] >> 16) * f;
+                    xo[jj] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+                } else {
+                    part = dot2(v4[jj], 0x3F803F80u, part);  // (1.0, 1.0)
+                    xo[jj] = v4[jj];
                 }
             }
-            part = dpp_quad_sum(part);      // the 4 jobs of a group are one lane quad
+            // the 16 jobs of a group are one DPP row: every lane gets the row sum
+            part = dpp_quad_sum(part);
+            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x141, 0xF, 0xF, true));  // row_half_mirror
+            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x140, 0xF, 0xF, true));  // row_mirror
             const float nb = TER ? -part : -136.f * part;
-            uint4* r = reinterpret_cast<uint4*>(rec + (sgl * 4 + skq) * B1_REC);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = make_uint4(xo[4 * i], xo[4 * i + 1], xo[4 * i + 2], xo[4 * i + 3]);
-            r[4] = make_uint4(__float_as_uint(nb), __float_as_uint(nb), __float_as_uint(nb), __float_as_uint(nb));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sct[(se[u] >> 4) * 16 + (se[u] & 15)] = uint16_t(sv[u]);
-            // a wave's LDS operations complete in order: its own stores are visible
-            // to all its lanes once they have completed
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            char* r = rec + (jx[u] >> 2) * B1_REC;              // (local group, quarter) record
+            *reinterpret_cast<uint4*>(r + 16 * sl) = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+            *reinterpret_cast<float*>(r + 64 + 4 * sl) = nb;    // the four slices write the four copies
+            sct[(se[u] >> 4) * 16 + (se[u] & 15)] = uint16_t(sv[u]);
         }
+        // a wave's LDS operations complete in order: its own stores are visible to
+        // all its lanes once they have completed
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
         auto group = [&](const uint4 gw, int lg) __attribute__((always_inline)) {
             const char* r = rec + (lg * 4 + kq) * B1_REC;
@@ -432,15 +436,15 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
     }
 }
 
-template <bool TER, int PF>
+template <bool TER, int PF, int SU>
 __global__ __launch_bounds__(1024) void gemv_b1_kernel(B1Args a) {
-    b1_core<TER, PF>(a, a.codes, a.scales, a.x, a.y, blockIdx.x);
+    b1_core<TER, PF, SU>(a, a.codes, a.scales, a.x, a.y, blockIdx.x);
 }
 
 // One token per expert job: block (job, tile).  Routes of at most kFusedPairs
 // pairs are grouped inside the kernel (every block redoes it: cheap only while
 // the route is short), longer ones by the grouping kernels.
-template <bool TER, int PF>
+template <bool TER, int PF, int SU>
 __global__ __launch_bounds__(1024) void moe_b1_kernel(B1Args a) {
     __shared__ int g[6][kFusedPairs];
     __shared__ int4 gjob;
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(1024) void moe_b1_kernel(B1Args a) {
     const int e = jd.x, p = pids[0];
     const int K = a.K, M = a.M;
     const size_t per_codes = size_t(M) * K / (TER ? 4 : 2), per_scales = size_t(M) * (K / 128);
-    b1_core<TER, PF>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales,
+    b1_core<TER, PF, SU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales,
                      a.x + size_t(a.x_per_pair ? p : p / a.topk) * K, a.y + size_t(p) * M, tile);
 }
 
@@ -765,27 +769,49 @@ mbd_status hip_check(const char* what) {
 #ifndef MBD_B1_IPW
 #define MBD_B1_IPW 4          // batch 1: items per wave at least (4 KB of codes)
 #endif
-#ifndef MBD_B1_PF
-#define MBD_B1_PF 2           // batch 1: items in flight per wave (1 KB each)
+#ifndef MBD_B1_PF_I4
+#define MBD_B1_PF_I4 4        // batch 1 INT4: items (groups, 1 KB) in flight per wave
+#endif
+#ifndef MBD_B1_PF_T
+#define MBD_B1_PF_T 2         // batch 1 ternary: items (group pairs, 1 KB) in flight per wave
 #endif
 
 struct B1Plan {
     int ipw, nw;
+    int su;          // staging passes: 16 jobs per staged group, over 64 lanes
     size_t lds;
 };
 
-// Waves per 16-row tile and items per wave: at least MBD_B1_IPW items per wave,
-// up to 16 waves, and at most B1_MAXG groups staged per wave and round.
-B1Plan plan_b1(bool ter, int64_t K) {
+// Waves per 16-row tile and items per wave.  Up to MBD_B1_IPW items per wave,
+// fewer while the call (tiles = 16-row tiles over all its matrices) would have
+// under about 8192 waves, more when a tile would need over 16 waves; a wave
+// stages at most B1_MAXG groups per round.
+B1Plan plan_b1(bool ter, int64_t K, int64_t tiles) {
     B1Plan p{};
     const int64_t ngroups = K / 128, n_items = ter ? (ngroups + 1) / 2 : ngroups;
     const int64_t max_ipw = B1_MAXG / (ter ? 2 : 1);
-    int64_t ipw = std::max<int64_t>(MBD_B1_IPW, (n_items + 15) / 16);
-    ipw = std::min<int64_t>(std::min<int64_t>(ipw, max_ipw), n_items);
+    const int64_t fill = (tiles * n_items + 8191) / 8192;      // items per wave for ~8192 waves
+    int64_t ipw = std::max<int64_t>((n_items + 15) / 16, std::min<int64_t>(MBD_B1_IPW, fill));
+    ipw = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ipw, max_ipw), n_items));
     p.ipw = int(ipw);
     p.nw = int(std::min<int64_t>(16, (n_items + ipw - 1) / ipw));
-    p.lds = size_t(p.nw) * size_t(ipw) * (ter ? 2 : 1) * B1_GROUP_LDS + size_t(p.nw) * 64;
+    const int64_t wg = ipw * (ter ? 2 : 1);
+    p.su = wg <= 4 ? 1 : 2;
+    p.lds = size_t(p.nw) * size_t(wg) * B1_GROUP_LDS + size_t(p.nw) * 64;
     return p;
+}
+
+// gemv_b1_kernel / moe_b1_kernel for the plan's scale-load count.
+template <bool TER, bool MOE>
+mbd_status launch_b1(const B1Plan& pl, const B1Args& a, unsigned grid, hipStream_t st) {
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * pl.nw), pl.lds, st, a);
+        return hip_check(MOE ? "expert gemv launch" : "gemv launch");
+    };
+    constexpr int PF = TER ? MBD_B1_PF_T : MBD_B1_PF_I4;
+    static_assert(B1_MAXG <= 8, "two staging passes at most");
+    if (pl.su == 1) return go(MOE ? moe_b1_kernel<TER, PF, 1> : gemv_b1_kernel<TER, PF, 1>);
+    return go(MOE ? moe_b1_kernel<TER, PF, 2> : gemv_b1_kernel<TER, PF, 2>);
 }
 
 }  // namespace
@@ -824,15 +850,14 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         else hipLaunchKernelGGL(gemv_mq_kernel<false>, dim3(blocks), dim3(64 * nw), 0, st, m);
         return hip_check("batched gemv launch");
     }
-    const B1Plan pl = plan_b1(ter, w->K);
+    const int tiles = int((w->M + 15) / 16);
+    const B1Plan pl = plan_b1(ter, w->K, tiles);
     B1Args a{};
     a.codes = static_cast<const uint8_t*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
     a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
-    a.tiles = int((w->M + 15) / 16);
-    if (ter) hipLaunchKernelGGL((gemv_b1_kernel<true, MBD_B1_PF>), dim3(a.tiles), dim3(64 * pl.nw), pl.lds, st, a);
-    else hipLaunchKernelGGL((gemv_b1_kernel<false, MBD_B1_PF>), dim3(a.tiles), dim3(64 * pl.nw), pl.lds, st, a);
-    return hip_check("gemv launch");
+    a.tiles = tiles;
+    return ter ? launch_b1<true, false>(pl, a, unsigned(a.tiles), st) : launch_b1<false, false>(pl, a, unsigned(a.tiles), st);
 }
 
 mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
@@ -924,20 +949,19 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
         return hip_check("expert gemv launch");
     }
     const bool ter = w->fmt == MBD_TERNARY_B128;
-    const B1Plan pl = plan_b1(ter, w->K);
+    const int tiles = int((w->M + 15) / 16);
+    const B1Plan pl = plan_b1(ter, w->K, int64_t(tiles) * D);
     B1Args a{};
     a.codes = static_cast<const uint8_t*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
     a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
-    a.tiles = int((w->M + 15) / 16);
+    a.tiles = tiles;
     a.jobs = jobs; a.n_jobs = n_jobs; a.pair_ids = pair_ids;
     a.route = fused ? route : nullptr;
     a.n_pairs = P; a.n_experts = E; a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0;
     const int64_t grid = max_jobs * a.tiles;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-    if (ter) hipLaunchKernelGGL((moe_b1_kernel<true, MBD_B1_PF>), dim3(unsigned(grid)), dim3(64 * pl.nw), pl.lds, st, a);
-    else hipLaunchKernelGGL((moe_b1_kernel<false, MBD_B1_PF>), dim3(unsigned(grid)), dim3(64 * pl.nw), pl.lds, st, a);
-    return hip_check("expert gemv launch");
+    return ter ? launch_b1<true, true>(pl, a, unsigned(grid), st) : launch_b1<false, true>(pl, a, unsigned(grid), st);
 }
 
 }  // extern "C"
