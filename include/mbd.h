@@ -59,7 +59,7 @@ typedef enum {
 } mbd_format;
 
 /* ------------------------------------------------------------------ packing
- * Offline, CPU only.  Section layouts (all little-endian, rows contiguous):
+ * Offline, CPU only.  Section layouts (all little-endian):
  *
  * MBD_TERNARY_B128  (sec 0) "codes"  uint32 [M*K/16]: a word holds 16 consecutive
  *                                    elements of a row, the even ones in the low half

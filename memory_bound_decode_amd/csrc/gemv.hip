@@ -278,12 +278,9 @@ struct B1Args {
     int M, K;
     int ipw;                // items per wave per round
     int tiles;              // 16-row tiles per matrix
-    // expert mode
-    const int4* jobs;       // {expert, pair_start, n_pairs, 0}
-    const int* n_jobs;
-    const int* pair_ids;    // pairs sorted by expert: pair id = t*k + slot
-    const int* route;       // set: group the routes inside the kernel (n_pairs <= kFusedPairs)
-    int n_pairs, n_experts, topk, x_per_pair;
+    // expert mode: pair p = slot p of the token, expert route[p]
+    const int* route;
+    int n_experts, topk, x_per_pair;
 };
 
 // Rows of tile `tile` of one matrix against one activation row x; y is that
@@ -441,35 +438,18 @@ __global__ __launch_bounds__(1024) void gemv_b1_kernel(B1Args a) {
     b1_core<TER, PF, SU>(a, a.codes, a.scales, a.x, a.y, blockIdx.x);
 }
 
-// One token per expert job: block (job, tile).  Routes of at most kFusedPairs
-// pairs are grouped inside the kernel (every block redoes it: cheap only while
-// the route is short), longer ones by the grouping kernels.
+// One (token, slot) pair per job: block (pair, tile).  With one activation row
+// per job there is nothing to group: the pair's expert is read from the route,
+// and pairs whose expert id is out of range write nothing.
 template <bool TER, int PF, int SU>
 __global__ __launch_bounds__(1024) void moe_b1_kernel(B1Args a) {
-    __shared__ int g[6][kFusedPairs];
-    __shared__ int4 gjob;
-    const int job = blockIdx.x / a.tiles, tile = blockIdx.x - job * a.tiles;
-    int4 jd;
-    const int* pids;
-    if (a.route) {
-        if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
-        moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, 1, g);
-        for (int q = threadIdx.x; q < a.n_pairs; q += blockDim.x)
-            if (g[4][q] >= 0 && g[1][q] == job) gjob = make_int4(g[4][q] >> 5, q, g[4][q] & 31, 0);
-        __syncthreads();
-        jd = gjob;
-        if (jd.x < 0) return;
-        pids = g[5] + jd.y;
-    } else {
-        if (job >= *a.n_jobs) return;
-        jd = a.jobs[job];
-        pids = a.pair_ids + jd.y;
-    }
-    const int e = jd.x, p = pids[0];
+    const int p = blockIdx.x / a.tiles, tile = blockIdx.x - p * a.tiles;
+    const int e = a.route[p];
+    if (e < 0 || e >= a.n_experts) return;
     const int K = a.K, M = a.M;
     const size_t per_codes = size_t(M) * K / (TER ? 4 : 2), per_scales = size_t(M) * (K / 128);
     b1_core<TER, PF, SU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales,
-                     a.x + size_t(a.x_per_pair ? p : p / a.topk) * K, a.y + size_t(p) * M, tile);
+                         a.x + size_t(a.x_per_pair ? p : p / a.topk) * K, a.y + size_t(p) * M, tile);
 }
 
 // ------------------------------------------------------------------ batch >= 2: MFMA
@@ -543,7 +523,6 @@ template <bool TER, class XRow, class YRow>
 __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int row_base, int nb, XRow xrow,
                                         YRow yrow) {
-    constexpr float K0 = TER ? 129.f : 136.f;
     constexpr int BPR = TER ? 4 : 2;                       // elements per byte
     __shared__ float red[MQ_MAXW][MQ_TILES][64][4];
     const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
@@ -594,22 +573,20 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     for (int t = 0; t < MQ_TILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // Lanes n >= nb carry batch row 0's activations: B column n only reaches
     // output column n, which is not stored.
+    // -K0 sum x per batch column, on the matrix cores: A = -K0 everywhere (exact in
+    // bf16) against the group's activations puts -K0 sum_k x[n][k] in every row of
+    // column n; each tile's chain starts from it.
+    const uint32_t nk0 = TER ? 0xC301C301u : 0xC308C308u;   // bf16 -129 / -136, twice
+    const bf16x8_t ak0 = __builtin_bit_cast(bf16x8_t, make_uint4(nk0, nk0, nk0, nk0));
     auto compute = [&](const MqGroup& d) {
         const uint4* xb = d.xv;
-        float sx = 0.f;
+        f32x4_t cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sx = dot2(xb[i].x, 0x3F803F80u, sx);
-            sx = dot2(xb[i].y, 0x3F803F80u, sx);
-            sx = dot2(xb[i].z, 0x3F803F80u, sx);
-            sx = dot2(xb[i].w, 0x3F803F80u, sx);
-        }
-        sx += __shfl_xor(sx, 16, 64);
-        sx += __shfl_xor(sx, 32, 64);
-        const float bias = K0 * sx;
+        for (int s = 0; s < 4; ++s)
+            cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak0, __builtin_bit_cast(bf16x8_t, xb[s]), cb, 0, 0, 0);
 #pragma unroll
         for (int t = 0; t < MQ_TILES; ++t) {
-            f32x4_t cg = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t cg = cb;
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(d.code[t], s),
@@ -617,7 +594,7 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float sc = half_bits_to_f32(uint16_t(d.sc[t][j >> 1] >> (16 * (j & 1))));
-                acc[t][j] = fmaf(sc, cg[j] - bias, acc[t][j]);
+                acc[t][j] = fmaf(sc, cg[j], acc[t][j]);
             }
         }
     };
@@ -914,9 +891,23 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int E = int(w->n_mats), P = T * k;
-    // one token: the batch-1 kernel; more: jobs of up to 16 pairs on the matrix cores
-    const bool mq = T >= 2;
-    const int bmax = mq ? 16 : 1;
+    if (T == 1) {
+        // one token: every (token, slot) pair is a batch-1 job, nothing to group
+        const bool ter = w->fmt == MBD_TERNARY_B128;
+        const int tiles = int((w->M + 15) / 16);
+        const B1Plan pl = plan_b1(ter, w->K, int64_t(tiles) * std::min(E, P));
+        B1Args a{};
+        a.codes = static_cast<const uint8_t*>(w->sec[0]);
+        a.scales = static_cast<const uint16_t*>(w->sec[1]);
+        a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
+        a.tiles = tiles;
+        a.route = route; a.n_experts = E; a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0;
+        const int64_t grid = int64_t(P) * tiles;
+        if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
+        return ter ? launch_b1<true, true>(pl, a, unsigned(grid), st) : launch_b1<false, true>(pl, a, unsigned(grid), st);
+    }
+    // more tokens: jobs of up to 16 pairs of one expert on the matrix cores
+    constexpr int bmax = 16;
     // sum over experts of ceil(pairs / bmax) <= D + (P - D) / bmax, D = distinct experts
     const int64_t D = std::min<int64_t>(E, P), max_jobs = D + (P - D) / bmax;
     const bool fused = P <= kFusedPairs;
@@ -930,38 +921,22 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
             hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(1024), 0, st, route, P, E, bmax, pair_ids, jobs, n_jobs);
         if ((s = hip_check("expert grouping launch")) != MBD_OK) return s;
     }
-    if (mq) {
-        MqArgs m{};
-        m.codes = static_cast<const uint8_t*>(w->sec[0]);
-        m.scales = static_cast<const uint16_t*>(w->sec[1]);
-        m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K);
-        m.jobs = jobs; m.n_jobs = n_jobs; m.pair_ids = pair_ids;
-        m.route = fused ? route : nullptr;
-        m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
-        m.row_blocks = int((w->M + 31) / 32);
-        const int nw = mq_waves(w->K);
-        const int64_t grid = max_jobs * m.row_blocks;
-        if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-        if (w->fmt == MBD_TERNARY_B128)
-            hipLaunchKernelGGL(moe_mq_kernel<true>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
-        else
-            hipLaunchKernelGGL(moe_mq_kernel<false>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
-        return hip_check("expert gemv launch");
-    }
-    const bool ter = w->fmt == MBD_TERNARY_B128;
-    const int tiles = int((w->M + 15) / 16);
-    const B1Plan pl = plan_b1(ter, w->K, int64_t(tiles) * D);
-    B1Args a{};
-    a.codes = static_cast<const uint8_t*>(w->sec[0]);
-    a.scales = static_cast<const uint16_t*>(w->sec[1]);
-    a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
-    a.tiles = tiles;
-    a.jobs = jobs; a.n_jobs = n_jobs; a.pair_ids = pair_ids;
-    a.route = fused ? route : nullptr;
-    a.n_pairs = P; a.n_experts = E; a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0;
-    const int64_t grid = max_jobs * a.tiles;
+    MqArgs m{};
+    m.codes = static_cast<const uint8_t*>(w->sec[0]);
+    m.scales = static_cast<const uint16_t*>(w->sec[1]);
+    m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K);
+    m.jobs = jobs; m.n_jobs = n_jobs; m.pair_ids = pair_ids;
+    m.route = fused ? route : nullptr;
+    m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
+    m.row_blocks = int((w->M + 31) / 32);
+    const int nw = mq_waves(w->K);
+    const int64_t grid = max_jobs * m.row_blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-    return ter ? launch_b1<true, true>(pl, a, unsigned(grid), st) : launch_b1<false, true>(pl, a, unsigned(grid), st);
+    if (w->fmt == MBD_TERNARY_B128)
+        hipLaunchKernelGGL(moe_mq_kernel<true>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
+    else
+        hipLaunchKernelGGL(moe_mq_kernel<false>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
+    return hip_check("expert gemv launch");
 }
 
 }  // extern "C"
