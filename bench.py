@@ -63,7 +63,7 @@ class BlockQuantGemv(Workload):
         import memory_bound_decode_amd as mbd
         import synth
         self.name, self.kind, self.M, self.K, self.B = name, kind, M, K, B
-        self.kernel = "gemv_b1_kernel" if B == 1 else "gemv_mq_kernel"
+        self.kernel = "gemv_bn_kernel" if B <= 4 else "gemv_mq_kernel"
         self.fmt_name = {"int4": "int4_g128", "ternary": "ternary_b128"}[kind]
         wl = synth.WORKLOADS[seed_name]
         if (wl.M, wl.K) == (M, K):
@@ -216,6 +216,10 @@ def make_workload(name, dev):
         return BlockQuantGemv("int4", 8192, 8192, 1, dev, "int4_g128_gemv_8192x8192_b1", "int4_8k")
     if name == "int4_8k_b4":
         return BlockQuantGemv("int4", 8192, 8192, 4, dev, "int4_g128_gemv_8192x8192_b4", "int4_8k")
+    if name == "int4_8k_b8":
+        return BlockQuantGemv("int4", 8192, 8192, 8, dev, "int4_g128_gemv_8192x8192_b8", "int4_8k")
+    if name == "int4_8k_b16":
+        return BlockQuantGemv("int4", 8192, 8192, 16, dev, "int4_g128_gemv_8192x8192_b16", "int4_8k")
     if name == "ternary_1k":
         return BlockQuantGemv("ternary", 1024, 1024, 1, dev, "ternary_b128_gemv_1024x1024_b1", "ternary_1k")
     for kind, tag in (("int4", "int4_8k"), ("ternary", "ternary_moe")):
@@ -233,7 +237,7 @@ def make_workload(name, dev):
     raise SystemExit("unknown workload %s" % name)
 
 
-ALL = ["int4_8k", "int4_8k_b4", "ternary_1k", "int4_4096x14336", "int4_14336x4096", "int4_8192x28672",
+ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4_4096x14336", "int4_14336x4096", "int4_8192x28672",
        "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
        "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify"]
 

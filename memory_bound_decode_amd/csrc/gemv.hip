@@ -248,29 +248,34 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
     }
 }
 
-// ------------------------------------------------------------------ batch 1
+// ------------------------------------------------------------------ batch 1..4
 //
-// One activation row: only one of the MFMA's 16 output columns is used (B holds
-// the activations broadcast to every column), but the multiply-adds leave the
-// VALU.  A block owns one 16-row tile; its waves take contiguous runs of items
-// (INT4: groups; ternary: group pairs), in rounds when K is long.  Each wave
-// stages what its own items need in its own LDS area, so no wave waits for
-// another before computing:
-//   rec[g][kq]  80 bytes: activations of columns [128g + 32kq, +32) (ternary:
-//               divided by 4^class, exact, so that one accumulator covers the
-//               three position classes of the unpack) and the group's -bias
-//               four times, the initial C of the group's MFMA chain;
-//   sct[g][16]  the tile's fp16 scales of group g.
+// Few activation rows (batch 1..4).  Column n
+// of B holds activation row n (columns past the rows in use repeat the last row
+// and are not stored), so one MFMA chain serves every row; with one row only
+// column 0 is used, but the multiply-adds still leave the VALU, and the unpack,
+// the MFMAs and the scale multiply-adds cost the same for one row as for four.
+// A block owns one 16-row tile; its waves take contiguous runs of items (INT4:
+// groups; ternary: group pairs), in rounds when K is long.  Each wave stages
+// what its own items need in its own LDS area, so no wave waits for another
+// before computing:
+//   rec[g][kq][t]  80 bytes: activations of row t, columns [128g + 32kq, +32)
+//                  (ternary: divided by 4^class, exact, so that one accumulator
+//                  covers the three position classes of the unpack) and the
+//                  group's -bias of row t four times, the initial C values of
+//                  the group's MFMA chain;
+//   sct[g][16]     the tile's fp16 scales of group g.
 // bias = sum over the group of (code value - q) x: 136 sum x for INT4 (code value
 // q + 136), sum (1 + 128 / 4^class) x for ternary (code value 128 + (q + 1) 4^class
 // against x / 4^class).  The waves' partial rows meet in LDS at the end.
-constexpr int B1_REC = 80;
-constexpr int B1_GROUP_LDS = 4 * B1_REC + 32;   // LDS bytes per staged group
-// Groups one wave stages per round (16 staging jobs each, so at most two passes
-// of 64 lanes): more would hold enough staging registers to cost occupancy.
-constexpr int B1_MAXG = 8;
+constexpr int BN_REC = 80;
 
-struct B1Args {
+// Groups one wave stages per round: at most 8, and at most 16 / NB so that the
+// staging jobs (16 per group and row) fit four passes of 64 lanes.
+constexpr int bn_max_groups(int NB) { return NB >= 4 ? 4 : 8; }
+constexpr int bn_group_lds(int NB) { return 4 * NB * BN_REC + 32; }
+
+struct BnArgs {
     const uint8_t* codes;   // tile-interleaved codes of n_mats matrices
     const uint16_t* scales; // [n_mats][M][K / 128]
     const uint16_t* x;
@@ -278,18 +283,20 @@ struct B1Args {
     int M, K;
     int ipw;                // items per wave per round
     int tiles;              // 16-row tiles per matrix
-    // expert mode: pair p = slot p of the token, expert route[p]
+    int B;                  // activation rows (plain GEMV)
+    // expert mode, one token: pair p = slot p, expert route[p]
     const int* route;
     int n_experts, topk, x_per_pair;
 };
 
-// Rows of tile `tile` of one matrix against one activation row x; y is that
-// matrix's output row.
-template <bool TER, int PF, int SU>
-__device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restrict__ codes,
-                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ x,
-                                        float* __restrict__ y, int tile) {
+// Tile `tile` of one matrix against nb <= NB activation rows xrow(t); output row
+// n of the tile goes to yrow(n).  XU: staging passes of 64 lanes.
+template <bool TER, int PF, int NB, int XU, class XRow, class YRow>
+__device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restrict__ codes,
+                                        const uint16_t* __restrict__ scales, int nb, XRow xrow, YRow yrow,
+                                        int tile) {
     constexpr int IG = TER ? 2 : 1;                  // groups per item
+    constexpr int GLDS = bn_group_lds(NB);
     extern __shared__ uint4 lds4[];
     char* lds = reinterpret_cast<char*>(lds4);
     const int lane = threadIdx.x & 63;
@@ -303,9 +310,10 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
     const uint8_t* tcodes = codes + size_t(row0) * (size_t(K) / (TER ? 4 : 2));
     const uint32_t unit = tile_unit(m, kq, R);
     const int wg = a.ipw * IG;                                // groups a wave stages per round
-    char* rec = lds + wave * wg * B1_GROUP_LDS;               // [wg][4][B1_REC]
-    uint16_t* sct = reinterpret_cast<uint16_t*>(rec + wg * 4 * B1_REC);     // [wg][16]
-    float* red = reinterpret_cast<float*>(lds + nw * wg * B1_GROUP_LDS);    // [nw][16]
+    char* rec = lds + wave * wg * GLDS;                       // [wg][4][NB][BN_REC]
+    uint16_t* sct = reinterpret_cast<uint16_t*>(rec + wg * 4 * NB * BN_REC);   // [wg][16]
+    float* red = reinterpret_cast<float*>(lds + nw * wg * GLDS);              // [nw][NB][16]
+    const int boff = (kq * NB + min(m, nb - 1)) * BN_REC;    // B column m reads row min(m, nb - 1)
     UnpackConsts kc;
     kc.init();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -315,24 +323,33 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
         const int n = min(a.ipw, n_items - it0);
         if (n <= 0) continue;
         const int g0 = it0 * IG, ng = min(n * IG, ngroups - g0);
+        const int njobs = 16 * ng * nb;
 
         // Staging loads first (vector-memory counters retire in issue order, so the
-        // staging waits do not wait for the code stream).  Job j = (local group
-        // j / 16, quarter j / 4 % 4, slice j % 4): 8 activations, columns
-        // 32 quarter + 8 slice .. +8 of the group.  SU passes of 64 jobs; lanes past
-        // the last job redo jobs of the last group (the same values into the same
-        // slots).  The same passes load the scale entries e = (local group e / 16,
-        // tile row e % 16).
-        uint4 xv[SU];
-        int jx[SU];
+        // staging waits do not wait for the code stream).  Job j = (row t, local
+        // group gl, quarter, slice), j = (t ng + gl) 16 + 4 quarter + slice: 8
+        // activations, columns 32 quarter + 8 slice .. +8 of the group.  Lanes past
+        // the last job redo jobs of the last (row, group), the same values into the
+        // same slots.  The same passes load the scale entries e = (local group
+        // e / 16, tile row e % 16).
+        // at most 8 groups x 16 rows of scales: two passes
+        constexpr int SU = XU < 2 ? XU : 2;
+        const float inv_ng = 1.f / float(ng);
+        uint4 xv[XU];
+        int jr[XU], se[SU];                  // jr: record byte offset * 4 + slice
         uint32_t sv[SU];
-        int se[SU];
 #pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            jx[u] = min(lane + 64 * u, 16 * ng - 16 + (lane & 15));
-            xv[u] = *reinterpret_cast<const uint4*>(x + (g0 + (jx[u] >> 4)) * 128 + (jx[u] & 15) * 8);
-            se[u] = min(lane + 64 * u, 16 * ng - 1);
-            sv[u] = scales[size_t(row0 + min(se[u] & 15, R - 1)) * ngroups + g0 + (se[u] >> 4)];
+        for (int u = 0; u < XU; ++u) {
+            const int j = min(lane + 64 * u, njobs - 16 + (lane & 15));
+            const int gt = j >> 4;
+            const int t = int((float(gt) + 0.5f) * inv_ng);   // gt / ng, exact for gt < 128
+            const int gl = gt - t * ng, q = (j >> 2) & 3, sl = j & 3;
+            jr[u] = (((gl * 4 + q) * NB + t) * BN_REC) * 4 + sl;
+            xv[u] = *reinterpret_cast<const uint4*>(xrow(t) + (g0 + gl) * 128 + q * 32 + sl * 8);
+            if (u < SU) {
+                se[u] = min(lane + 64 * u, 16 * ng - 1);
+                sv[u] = scales[size_t(row0 + min(se[u] & 15, R - 1)) * ngroups + g0 + (se[u] >> 4)];
+            }
         }
 
         // The odd last ternary group has 8-byte units: its 16-byte load takes the
@@ -351,46 +368,48 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
         __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
-        for (int u = 0; u < SU; ++u) {
-            const int sl = jx[u] & 3;                        // slice: columns 8 sl .. +8 of the quarter
-            const uint32_t v4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
-            uint32_t xo[4];
-            float part = 0.f;
+        for (int u = 0; u < XU; ++u) {
+            if (64 * u < njobs) {                            // uniform: passes of padding jobs only are skipped
+                const int sl = jr[u] & 3;                    // slice: columns 8 sl .. +8 of the quarter
+                const uint32_t v4[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+                uint32_t xo[4];
+                float part = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                if constexpr (TER) {
-                    // columns 8 sl + 2jj, +1 (a quarter starts on a word boundary): pair
-                    // (4 sl + jj) % 8 of a 16-code word, class pair % 3, weight 1 + 128 / 4^class
-                    const int ce = jj % 3, co = (4 + jj) % 3;        // class for an even / odd slice
-                    const bool odd = sl & 1;
-                    const uint32_t wpair = odd ? (co == 0 ? 0x43014301u : co == 1 ? 0x42044204u : 0x41104110u)
-                                               : (ce == 0 ? 0x43014301u : ce == 1 ? 0x42044204u : 0x41104110u);
-                    const float f = odd ? (co == 0 ? 1.f : co == 1 ? 0.25f : 0.0625f)
-                                        : (ce == 0 ? 1.f : ce == 1 ? 0.25f : 0.0625f);
-                    part = dot2(v4[jj], wpair, part);        // 129, 33, 9 are exact in bf16
-                    const float lo = bf16_to_f32(v4[jj] & 0xFFFFu) * f, hi = bf16_to_f32(v4[jj] >> 16) * f;
-                    xo[jj] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-                } else {
-                    part = dot2(v4[jj], 0x3F803F80u, part);  // (1.0, 1.0)
-                    xo[jj] = v4[jj];
+                for (int jj = 0; jj < 4; ++jj) {
+                    if constexpr (TER) {
+                        // columns 8 sl + 2jj, +1 (a quarter starts on a word boundary): pair
+                        // (4 sl + jj) % 8 of a 16-code word, class pair % 3, weight 1 + 128 / 4^class
+                        const int ce = jj % 3, co = (4 + jj) % 3;    // class for an even / odd slice
+                        const bool odd = sl & 1;
+                        const uint32_t wpair = odd ? (co == 0 ? 0x43014301u : co == 1 ? 0x42044204u : 0x41104110u)
+                                                   : (ce == 0 ? 0x43014301u : ce == 1 ? 0x42044204u : 0x41104110u);
+                        const float f = odd ? (co == 0 ? 1.f : co == 1 ? 0.25f : 0.0625f)
+                                            : (ce == 0 ? 1.f : ce == 1 ? 0.25f : 0.0625f);
+                        part = dot2(v4[jj], wpair, part);    // 129, 33, 9 are exact in bf16
+                        const float lo = bf16_to_f32(v4[jj] & 0xFFFFu) * f, hi = bf16_to_f32(v4[jj] >> 16) * f;
+                        xo[jj] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+                    } else {
+                        part = dot2(v4[jj], 0x3F803F80u, part);    // (1.0, 1.0)
+                        xo[jj] = v4[jj];
+                    }
                 }
+                // the 16 jobs of a (row, group) are one DPP row: every lane gets the row sum
+                part = dpp_quad_sum(part);
+                part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x141, 0xF, 0xF, true));
+                part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x140, 0xF, 0xF, true));
+                const float nbias = TER ? -part : -136.f * part;
+                char* r = rec + (jr[u] >> 2);
+                *reinterpret_cast<uint4*>(r + 16 * sl) = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+                *reinterpret_cast<float*>(r + 64 + 4 * sl) = nbias;   // the four slices write the four copies
             }
-            // the 16 jobs of a group are one DPP row: every lane gets the row sum
-            part = dpp_quad_sum(part);
-            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x141, 0xF, 0xF, true));  // row_half_mirror
-            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x140, 0xF, 0xF, true));  // row_mirror
-            const float nb = TER ? -part : -136.f * part;
-            char* r = rec + (jx[u] >> 2) * B1_REC;              // (local group, quarter) record
-            *reinterpret_cast<uint4*>(r + 16 * sl) = make_uint4(xo[0], xo[1], xo[2], xo[3]);
-            *reinterpret_cast<float*>(r + 64 + 4 * sl) = nb;    // the four slices write the four copies
-            sct[(se[u] >> 4) * 16 + (se[u] & 15)] = uint16_t(sv[u]);
+            if (u < SU && 64 * u < 16 * ng) sct[se[u]] = uint16_t(sv[u]);
         }
         // a wave's LDS operations complete in order: its own stores are visible to
         // all its lanes once they have completed
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
         auto group = [&](const uint4 gw, int lg) __attribute__((always_inline)) {
-            const char* r = rec + (lg * 4 + kq) * B1_REC;
+            const char* r = rec + lg * 4 * NB * BN_REC + boff;
             f32x4_t c = *reinterpret_cast<const f32x4_t*>(r + 64);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
@@ -420,41 +439,52 @@ __device__ __forceinline__ void b1_core(const B1Args& a, const uint8_t* __restri
             if (i + p < n) compute(p, i + p);
     }
 
-    // C[row 4kq + jj][column m]: every column holds the same sums
-    if (m == 0) {
+    // C[row 4kq + jj][column m]: column m < nb is activation row m
+    if (m < nb) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) red[wave * 16 + 4 * kq + jj] = acc[jj];
+        for (int jj = 0; jj < 4; ++jj) red[(wave * NB + m) * 16 + 4 * kq + jj] = acc[jj];
     }
     __syncthreads();
-    if (int(threadIdx.x) < R) {
-        float s = 0.f;
-        for (int v = 0; v < nw; ++v) s += red[v * 16 + threadIdx.x];
-        y[row0 + threadIdx.x] = s;
+    for (int t = threadIdx.x; t < 16 * nb; t += blockDim.x) {
+        const int on = t >> 4, orow = t & 15;
+        if (orow < R) {
+            float s = 0.f;
+            for (int v = 0; v < nw; ++v) s += red[(v * NB + on) * 16 + orow];
+            yrow(on)[row0 + orow] = s;
+        }
     }
 }
 
-template <bool TER, int PF, int SU>
-__global__ __launch_bounds__(1024) void gemv_b1_kernel(B1Args a) {
-    b1_core<TER, PF, SU>(a, a.codes, a.scales, a.x, a.y, blockIdx.x);
+template <bool TER, int PF, int NB, int XU>
+__global__ __launch_bounds__(1024) void gemv_bn_kernel(BnArgs a) {
+    const uint16_t* x = a.x;
+    float* y = a.y;
+    const int K = a.K, M = a.M;
+    bn_core<TER, PF, NB, XU>(a, a.codes, a.scales, a.B, [=](int t) { return x + size_t(t) * K; },
+                             [=](int n) { return y + size_t(n) * M; }, blockIdx.x);
 }
 
-// One (token, slot) pair per job: block (pair, tile).  With one activation row
-// per job there is nothing to group: the pair's expert is read from the route,
-// and pairs whose expert id is out of range write nothing.
-template <bool TER, int PF, int SU>
-__global__ __launch_bounds__(1024) void moe_b1_kernel(B1Args a) {
+// One token: every (token, slot) pair is a one-row job, block (pair, tile).  With
+// one activation row there is nothing to group: the pair's expert is read from the
+// route, and pairs whose expert id is out of range write nothing.
+template <bool TER, int PF, int XU>
+__global__ __launch_bounds__(1024) void moe_b1_kernel(BnArgs a) {
     const int p = blockIdx.x / a.tiles, tile = blockIdx.x - p * a.tiles;
     const int e = a.route[p];
     if (e < 0 || e >= a.n_experts) return;
     const int K = a.K, M = a.M;
     const size_t per_codes = size_t(M) * K / (TER ? 4 : 2), per_scales = size_t(M) * (K / 128);
-    b1_core<TER, PF, SU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales,
-                         a.x + size_t(a.x_per_pair ? p : p / a.topk) * K, a.y + size_t(p) * M, tile);
+    const uint16_t* xr = a.x + size_t(a.x_per_pair ? p : p / a.topk) * K;
+    float* yr = a.y + size_t(p) * M;
+    bn_core<TER, PF, 1, XU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales, 1,
+                            [=](int) { return xr; }, [=](int) { return yr; }, tile);
 }
 
-// ------------------------------------------------------------------ batch >= 2: MFMA
+// ------------------------------------------------------------------ batch 5..16: MFMA
 
-// Batch 2..16 is a skinny GEMM: the codes become bf16 MFMA operands directly.
+// Batch 5..16 (and expert jobs of several tokens) is a skinny GEMM: the codes
+// become bf16 MFMA operands directly, and the activations are read per group
+// straight from memory (no staging).
 // A code c of a pair-friendly word, OR'ed into the bf16 pattern of 128, is the
 // exact value 128 + c = q + K0 (K0 = 136 for INT4, 129 for ternary), so
 // v_mfma_f32_16x16x32_bf16 over one 128-column scale group gives
@@ -744,52 +774,71 @@ mbd_status hip_check(const char* what) {
 }
 
 #ifndef MBD_B1_IPW
-#define MBD_B1_IPW 4          // batch 1: items per wave at least (4 KB of codes)
+#define MBD_B1_IPW 4          // items per wave at least (4 KB of codes), few-row kernel
 #endif
 #ifndef MBD_B1_PF_I4
-#define MBD_B1_PF_I4 4        // batch 1 INT4: items (groups, 1 KB) in flight per wave
+#define MBD_B1_PF_I4 4        // INT4: items (groups, 1 KB) in flight per wave
 #endif
 #ifndef MBD_B1_PF_T
-#define MBD_B1_PF_T 2         // batch 1 ternary: items (group pairs, 1 KB) in flight per wave
+#define MBD_B1_PF_T 2         // ternary: items (group pairs, 1 KB) in flight per wave
 #endif
 
-struct B1Plan {
+struct BnPlan {
+    int nb_max;      // NB: activation rows per block
     int ipw, nw;
-    int su;          // staging passes: 16 jobs per staged group, over 64 lanes
+    int xu;          // staging passes: 16 jobs per staged group and row, over 64 lanes
     size_t lds;
 };
 
-// Waves per 16-row tile and items per wave.  Up to MBD_B1_IPW items per wave,
-// fewer while the call (tiles = 16-row tiles over all its matrices) would have
-// under about 8192 waves, more when a tile would need over 16 waves; a wave
-// stages at most B1_MAXG groups per round.
-B1Plan plan_b1(bool ter, int64_t K, int64_t tiles) {
-    B1Plan p{};
+// Waves per 16-row tile and items per wave for NB activation rows.  Up to
+// MBD_B1_IPW items per wave, fewer while the call (tiles = 16-row tiles over all
+// its matrices and jobs) would have under about 8192 waves, more when a tile
+// would need over 16 waves; a wave stages at most bn_max_groups(NB) groups per
+// round.
+BnPlan plan_bn(bool ter, int64_t K, int64_t tiles, int NB) {
+    BnPlan p{};
+    p.nb_max = NB;
+    const int64_t IG = ter ? 2 : 1;
     const int64_t ngroups = K / 128, n_items = ter ? (ngroups + 1) / 2 : ngroups;
-    const int64_t max_ipw = B1_MAXG / (ter ? 2 : 1);
+    const int64_t max_ipw = std::max<int64_t>(1, bn_max_groups(NB) / IG);
     const int64_t fill = (tiles * n_items + 8191) / 8192;      // items per wave for ~8192 waves
     int64_t ipw = std::max<int64_t>((n_items + 15) / 16, std::min<int64_t>(MBD_B1_IPW, fill));
     ipw = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ipw, max_ipw), n_items));
     p.ipw = int(ipw);
     p.nw = int(std::min<int64_t>(16, (n_items + ipw - 1) / ipw));
-    const int64_t wg = ipw * (ter ? 2 : 1);
-    p.su = wg <= 4 ? 1 : 2;
-    p.lds = size_t(p.nw) * size_t(wg) * B1_GROUP_LDS + size_t(p.nw) * 64;
+    const int64_t wg = ipw * IG, jobs = 16 * wg * NB;
+    p.xu = jobs <= 64 ? 1 : jobs <= 128 ? 2 : 4;
+    p.lds = size_t(p.nw) * size_t(wg) * bn_group_lds(NB) + size_t(p.nw) * NB * 64;
     return p;
 }
 
-// gemv_b1_kernel / moe_b1_kernel for the plan's scale-load count.
+// gemv_bn_kernel for the plan's row count and staging passes, or moe_b1_kernel.
 template <bool TER, bool MOE>
-mbd_status launch_b1(const B1Plan& pl, const B1Args& a, unsigned grid, hipStream_t st) {
+mbd_status launch_bn(const BnPlan& pl, const BnArgs& a, unsigned grid, hipStream_t st) {
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * pl.nw), pl.lds, st, a);
         return hip_check(MOE ? "expert gemv launch" : "gemv launch");
     };
-    constexpr int PF = TER ? MBD_B1_PF_T : MBD_B1_PF_I4;
-    static_assert(B1_MAXG <= 8, "two staging passes at most");
-    if (pl.su == 1) return go(MOE ? moe_b1_kernel<TER, PF, 1> : gemv_b1_kernel<TER, PF, 1>);
-    return go(MOE ? moe_b1_kernel<TER, PF, 2> : gemv_b1_kernel<TER, PF, 2>);
+    // ring depth: INT4 with one row MBD_B1_PF_I4; more rows (more staging
+    // registers) and ternary MBD_B1_PF_T
+    constexpr int PF1 = TER ? MBD_B1_PF_T : MBD_B1_PF_I4, PFN = MBD_B1_PF_T;
+    if constexpr (MOE) {
+        if (pl.nb_max == 1 && pl.xu == 1) return go(moe_b1_kernel<TER, PF1, 1>);
+        if (pl.nb_max == 1 && pl.xu == 2) return go(moe_b1_kernel<TER, PF1, 2>);
+    } else {
+        switch (pl.nb_max * 8 + pl.xu) {
+            case 1 * 8 + 1: return go(gemv_bn_kernel<TER, PF1, 1, 1>);
+            case 1 * 8 + 2: return go(gemv_bn_kernel<TER, PF1, 1, 2>);
+            case 4 * 8 + 1: return go(gemv_bn_kernel<TER, PFN, 4, 1>);
+            case 4 * 8 + 2: return go(gemv_bn_kernel<TER, PFN, 4, 2>);
+            case 4 * 8 + 4: return go(gemv_bn_kernel<TER, PFN, 4, 4>);
+            default: break;
+        }
+    }
+    return fail(MBD_EINVAL, "no kernel for %d rows and %d staging passes", pl.nb_max, pl.xu);
 }
+
+int bn_rows(int B) { return B <= 1 ? 1 : 4; }
 
 }  // namespace
 
@@ -815,8 +864,9 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2)) return fail(MBD_EALIGN, "codes must be 16-byte aligned");
     if (w->M == 0) return MBD_OK;
     const bool ter = w->fmt == MBD_TERNARY_B128;
-    if (B >= 2) {
-        // skinny GEMM on the matrix cores
+    if (B > 4) {
+        // 5..16 rows: the 32-row kernel with activations read per group (at 8 rows
+        // it measured even with the few-row kernel, above that faster)
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
         m.scales = static_cast<const uint16_t*>(w->sec[1]);
@@ -828,13 +878,13 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         return hip_check("batched gemv launch");
     }
     const int tiles = int((w->M + 15) / 16);
-    const B1Plan pl = plan_b1(ter, w->K, tiles);
-    B1Args a{};
+    const BnPlan pl = plan_bn(ter, w->K, tiles, bn_rows(B));
+    BnArgs a{};
     a.codes = static_cast<const uint8_t*>(w->sec[0]);
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
     a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
-    a.tiles = tiles;
-    return ter ? launch_b1<true, false>(pl, a, unsigned(a.tiles), st) : launch_b1<false, false>(pl, a, unsigned(a.tiles), st);
+    a.tiles = tiles; a.B = B;
+    return ter ? launch_bn<true, false>(pl, a, unsigned(tiles), st) : launch_bn<false, false>(pl, a, unsigned(tiles), st);
 }
 
 mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
@@ -891,12 +941,12 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int E = int(w->n_mats), P = T * k;
+    const bool ter = w->fmt == MBD_TERNARY_B128;
+    const int tiles = int((w->M + 15) / 16);
     if (T == 1) {
-        // one token: every (token, slot) pair is a batch-1 job, nothing to group
-        const bool ter = w->fmt == MBD_TERNARY_B128;
-        const int tiles = int((w->M + 15) / 16);
-        const B1Plan pl = plan_b1(ter, w->K, int64_t(tiles) * std::min(E, P));
-        B1Args a{};
+        // one token: every (token, slot) pair is a one-row job, nothing to group
+        const BnPlan pl = plan_bn(ter, w->K, int64_t(tiles) * std::min(E, P), 1);
+        BnArgs a{};
         a.codes = static_cast<const uint8_t*>(w->sec[0]);
         a.scales = static_cast<const uint16_t*>(w->sec[1]);
         a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
@@ -904,9 +954,11 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
         a.route = route; a.n_experts = E; a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0;
         const int64_t grid = int64_t(P) * tiles;
         if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-        return ter ? launch_b1<true, true>(pl, a, unsigned(grid), st) : launch_b1<false, true>(pl, a, unsigned(grid), st);
+        return ter ? launch_bn<true, true>(pl, a, unsigned(grid), st) : launch_bn<false, true>(pl, a, unsigned(grid), st);
     }
-    // more tokens: jobs of up to 16 pairs of one expert on the matrix cores
+    // more tokens: jobs of up to 16 pairs of one expert on the 32-row kernel, which
+    // reads the activations per group and needs no staging (jobs of one or two
+    // pairs, the common case, measured twice as slow on the few-row kernel)
     constexpr int bmax = 16;
     // sum over experts of ceil(pairs / bmax) <= D + (P - D) / bmax, D = distinct experts
     const int64_t D = std::min<int64_t>(E, P), max_jobs = D + (P - D) / bmax;
@@ -932,7 +984,7 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     const int nw = mq_waves(w->K);
     const int64_t grid = max_jobs * m.row_blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-    if (w->fmt == MBD_TERNARY_B128)
+    if (ter)
         hipLaunchKernelGGL(moe_mq_kernel<true>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
     else
         hipLaunchKernelGGL(moe_mq_kernel<false>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
