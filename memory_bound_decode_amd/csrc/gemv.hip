@@ -47,14 +47,12 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return __half2float(__ushort_as_half(h));
 }
 
-// (a & m) | o in one VALU op.  gfx9 VOP3 encodings cannot take a literal, so
-// left to itself the compiler splits this into v_and + v_or with literals; the
-// masks are kept in VGPRs instead (loaded once per kernel).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-    return r;
-}
+// (a & m) | o, one v_and_or_b32 when m and o sit in VGPRs (UnpackConsts): gfx9
+// VOP3 encodings cannot take a literal, so with constant masks the compiler
+// splits it into v_and + v_or.  Plain code, not inline asm: the compiler's
+// hazard tracking does not see an asm block as a VALU write, and an MFMA that
+// reads its result as an A operand too soon reads a stale register.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
 
 // Masks used by the unpackers, held in registers.
 struct UnpackConsts {
@@ -511,7 +509,8 @@ inline int mq_waves(int64_t K) {
 
 struct MqGroup {
     uint4 code[MQ_TILES];          // INT4: 4 words (32 codes); ternary: .x, .y (32 codes)
-    uint32_t sc[MQ_TILES][2];      // fp16 scales of the lane's 4 output rows, packed in pairs
+    uint32_t sc[MQ_TILES][4];      // raw fp16 scales of the lane's 4 output rows: packing them
+                                   // at issue would wait for the loads (and all before them)
     uint4 xv[4];                   // 32 activations of batch row n
 };
 
@@ -532,19 +531,17 @@ struct MqArgs {
 // A operand of MFMA step s from the lane's codes of one group, every pair shifted
 // to mantissa bits 0.. (value q + K0): the activations here are the raw rows.
 template <bool TER>
-__device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s) {
-    uint32_t o[4];
+__device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s, const UnpackConsts& k) {
     if constexpr (TER) {
         const uint32_t w = (s < 2) ? c.x : c.y;        // 16 codes per word
         const int p0 = 4 * (s & 1);
+        uint32_t o[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) o[p] = ((w >> (2 * (p0 + p))) & 0x00030003u) | 0x43004300u;
+        for (int p = 0; p < 4; ++p) o[p] = and_or(w >> (2 * (p0 + p)), k.m2a, k.magic);
+        return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
-        const uint32_t w = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;   // 8 codes per word
-#pragma unroll
-        for (int p = 0; p < 4; ++p) o[p] = ((w >> (4 * p)) & 0x000F000Fu) | 0x43004300u;
+        return code_operand<false>(c, s, k);           // INT4 fields already sit at bit 0 after the shift
     }
-    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 // Rows [row_base, row_base + 32) of one matrix; nb <= 16 batch rows whose
@@ -559,40 +556,43 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, q = lane >> 4;
     const int K = a.K, M = a.M, ngroups = K >> 7;
-    const size_t row_bytes = size_t(K) / BPR;
+    const uint32_t row_bytes = uint32_t(K) / BPR;
     const int npairs = ngroups >> 1;                       // ternary: full group pairs
-    const uint8_t* tcode[MQ_TILES];                        // tile base (a tile past M: the last tile)
-    uint32_t unit[MQ_TILES];
-    int tR[MQ_TILES];
+    // Per-lane 32-bit offsets (the group's part of every address is uniform):
+    // code bytes of the lane's unit in each tile (a tile past M: the last tile),
+    // scale bytes of its 4 output rows (clamped).
+    uint32_t coff[MQ_TILES], coff8[MQ_TILES], soff[MQ_TILES][4];
+    uint32_t item[MQ_TILES];
     int orow[MQ_TILES];                                    // first output row of this lane in each tile
 #pragma unroll
     for (int t = 0; t < MQ_TILES; ++t) {
         const int r0 = min(row_base + 16 * t, (M - 1) & ~15);
-        tR[t] = min(16, M - r0);
-        tcode[t] = codes + size_t(r0) * row_bytes;
-        unit[t] = tile_unit(n, q, tR[t]);
+        const int R = min(16, M - r0);
+        const uint32_t u = tile_unit(n, q, R);
+        item[t] = 64u * uint32_t(R);
+        coff[t] = uint32_t(r0) * row_bytes + u * 16;
+        coff8[t] = uint32_t(r0) * row_bytes + u * 8;
         orow[t] = row_base + 16 * t + 4 * q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) soff[t][j] = uint32_t(min(orow[t] + j, M - 1)) * uint32_t(2 * ngroups);   // bytes
     }
     const bool xlive = n < nb;
     const uint16_t* xr = xrow(xlive ? n : 0);
     auto load = [&](int g, MqGroup& d) {
 #pragma unroll
         for (int t = 0; t < MQ_TILES; ++t) {
-            const size_t item = 64 * size_t(tR[t]);
             if constexpr (TER) {
                 const int h = g >> 1;
-                const uint8_t* cp = h < npairs ? tcode[t] + h * item + unit[t] * 16 + (g & 1) * 8
-                                               : tcode[t] + npairs * item + unit[t] * 8;
-                const uint2 v = *reinterpret_cast<const uint2*>(cp);
+                const bool pair = h < npairs;
+                const uint8_t* base = codes + (pair ? size_t(h) * item[t] + (g & 1) * 8 : size_t(npairs) * item[t]);
+                const uint2 v = *reinterpret_cast<const uint2*>(base + (pair ? coff[t] : coff8[t]));
                 d.code[t] = make_uint4(v.x, v.y, 0u, 0u);
             } else {
-                d.code[t] = *reinterpret_cast<const uint4*>(tcode[t] + g * item + unit[t] * 16);
+                d.code[t] = *reinterpret_cast<const uint4*>(codes + size_t(g) * item[t] + coff[t]);
             }
-            uint32_t sv[4];
+            const char* sg = reinterpret_cast<const char*>(scales + g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sv[j] = scales[size_t(min(orow[t] + j, M - 1)) * ngroups + g];
-            d.sc[t][0] = sv[0] | (sv[1] << 16);
-            d.sc[t][1] = sv[2] | (sv[3] << 16);
+            for (int j = 0; j < 4; ++j) d.sc[t][j] = *reinterpret_cast<const uint16_t*>(sg + soff[t][j]);
         }
         const uint4* px = reinterpret_cast<const uint4*>(xr + size_t(g) * 128 + 32 * q);
 #pragma unroll
@@ -606,6 +606,8 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     // -K0 sum x per batch column, on the matrix cores: A = -K0 everywhere (exact in
     // bf16) against the group's activations puts -K0 sum_k x[n][k] in every row of
     // column n; each tile's chain starts from it.
+    UnpackConsts kc;
+    kc.init();
     const uint32_t nk0 = TER ? 0xC301C301u : 0xC308C308u;   // bf16 -129 / -136, twice
     const bf16x8_t ak0 = __builtin_bit_cast(bf16x8_t, make_uint4(nk0, nk0, nk0, nk0));
     auto compute = [&](const MqGroup& d) {
@@ -619,11 +621,11 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             f32x4_t cg = cb;
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(d.code[t], s),
+                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(d.code[t], s, kc),
                                                              __builtin_bit_cast(bf16x8_t, xb[s]), cg, 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sc = half_bits_to_f32(uint16_t(d.sc[t][j >> 1] >> (16 * (j & 1))));
+                const float sc = half_bits_to_f32(uint16_t(d.sc[t][j]));
                 acc[t][j] = fmaf(sc, cg[j], acc[t][j]);
             }
         }
