@@ -125,17 +125,45 @@ def test_gemv_ternary_1k_full(dev):
     assert gemv.rel_l2(_run_gemv(dw, x, dev), ref) <= TOL
 
 
-@pytest.mark.parametrize("B", [1, 4])
-def test_gemv_int4_8k_full(dev, B):
+@pytest.fixture(scope="module")
+def int4_8k_full(dev):
+    """The 8192 x 8192 INT4 workload packed once: (workload, device weights, fp64 dequant)."""
     wl = synth.WORKLOADS["int4_8k"]
     w = synth.gen_weights(wl)
-    x = synth.gen_x(wl, B)
     dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_INT4_G128, w), dev)
     q, s = int4.quantize(w)
-    ref = gemv.gemv(int4.dequant(q, s), x)
+    return wl, dw, int4.dequant(q, s)
+
+
+# batch 1..4 run on the staged few-row kernel, 5..16 on the 32-row kernel
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 16])
+def test_gemv_int4_8k_full(dev, int4_8k_full, B):
+    wl, dw, W = int4_8k_full
+    x = synth.gen_x(wl, B)
+    print("case int4_8k full B=%d" % B, flush=True)
     y = _run_gemv(dw, x, dev)
-    err = gemv.rel_l2(y, ref)
+    err = gemv.rel_l2(y, gemv.gemv(W, x))
     print("int4_8k B=%d rel_l2=%.3e" % (B, err), flush=True)
+    assert err <= TOL
+
+
+@pytest.fixture(scope="module")
+def ternary_ffn_full(dev):
+    """A 4096 x 14336 ternary matrix (t(4) weights, the MoE workload's distribution)."""
+    wl = synth.WORKLOADS["ternary_moe"]
+    w = synth.f32_to_bf16_bits(synth.gen_weight_rows(wl.seed + 77, 4096, 14336, wl.dist, wl.scale).astype(np.float32))
+    dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_TERNARY_B128, w), dev)
+    q, s = ternary.quantize(w)
+    return wl, dw, ternary.dequant(q, s)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_gemv_ternary_ffn_full(dev, ternary_ffn_full, B):
+    wl, dw, W = ternary_ffn_full
+    x = synth.gen_x(wl, B, 14336)
+    print("case ternary 4096x14336 full B=%d" % B, flush=True)
+    err = gemv.rel_l2(_run_gemv(dw, x, dev), gemv.gemv(W, x))
+    print("ternary 4096x14336 B=%d rel_l2=%.3e" % (B, err), flush=True)
     assert err <= TOL
 
 
