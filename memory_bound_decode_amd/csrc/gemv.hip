@@ -497,7 +497,11 @@ __global__ __launch_bounds__(1024) void moe_b1_kernel(BnArgs a) {
 // B.  Ternary waves take group pairs, so that the two 8-byte halves of each
 // 16-byte unit are loaded back to back.
 
-constexpr int MQ_TILES = 2;
+#ifndef MBD_MQ_TILES
+#define MBD_MQ_TILES 2        // 16-row tiles per block
+#endif
+constexpr int MQ_TILES = MBD_MQ_TILES;
+constexpr int MQ_ROWS = 16 * MQ_TILES;
 constexpr int MQ_MAXW = 16;
 #ifndef MBD_MQ_GPW
 #define MBD_MQ_GPW 4          // scale groups per wave (sets the waves per block)
@@ -544,7 +548,7 @@ __device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s, const Unpac
     }
 }
 
-// Rows [row_base, row_base + 32) of one matrix; nb <= 16 batch rows whose
+// Rows [row_base, row_base + MQ_ROWS) of one matrix; nb <= 16 batch rows whose
 // activations / outputs are xrow(b) / yrow(b).
 template <bool TER, class XRow, class YRow>
 __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restrict__ codes,
@@ -674,7 +678,7 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void gemv_mq_kernel(MqArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    mq_core<TER>(a, a.codes, a.scales, blockIdx.x * 32, a.B, [=](int b) { return x + (size_t)b * K; },
+    mq_core<TER>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return x + (size_t)b * K; },
                  [=](int b) { return y + (size_t)b * M; });
 }
 
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)M * K / (TER ? 4 : 2), per_scales = (size_t)M * (K / 128);
     mq_core<TER>(
-        a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * 32, nb,
+        a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * MQ_ROWS, nb,
         [=](int b) {
             const int p = pids[b];
             return x + (size_t)(xpp ? p : p / topk) * K;
@@ -874,7 +878,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         m.scales = static_cast<const uint16_t*>(w->sec[1]);
         m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
         const int nw = mq_waves(w->K);
-        const unsigned blocks = unsigned((w->M + 31) / 32);
+        const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
         if (ter) hipLaunchKernelGGL(gemv_mq_kernel<true>, dim3(blocks), dim3(64 * nw), 0, st, m);
         else hipLaunchKernelGGL(gemv_mq_kernel<false>, dim3(blocks), dim3(64 * nw), 0, st, m);
         return hip_check("batched gemv launch");
@@ -982,7 +986,7 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     m.jobs = jobs; m.n_jobs = n_jobs; m.pair_ids = pair_ids;
     m.route = fused ? route : nullptr;
     m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
-    m.row_blocks = int((w->M + 31) / 32);
+    m.row_blocks = int((w->M + MQ_ROWS - 1) / MQ_ROWS);
     const int nw = mq_waves(w->K);
     const int64_t grid = max_jobs * m.row_blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
