@@ -211,6 +211,75 @@ class CassandraWl(Workload):
         return d
 
 
+class CassandraStep(Workload):
+    """Draft/verify step of speculative decoding over a stack of layer-shaped
+    Cassandra matrices (Cassandra review, speculative decoding and the ideal-speedup
+    figure): N draft tokens, each through every layer as a GEMV over the speculation
+    data only, then every layer's batch-(N+1) fused restore + verify GEMM.  The
+    activations are synthetic (no trained weights), drawn per call.  Acceptance is a
+    parameter: with per-token acceptance a, a step yields (1 - a^(N+1)) / (1 - a)
+    tokens on average; the weight bytes per token against bf16 give the byte side of
+    the ideal speedup."""
+
+    def __init__(self, dev, n_draft=4, layers=2, alpha=0.8):
+        import torch
+        import memory_bound_decode_amd as mbd
+        import synth
+        wl = synth.WORKLOADS["cassandra_verify"]
+        self.M, self.K, self.N, self.L, self.alpha = wl.M, wl.K, n_draft, layers, alpha
+        self.name, self.kernel, self.fmt_name = "cassandra_draft_verify_step", "verify_gemm_kernel", "cassandra"
+        norms = synth.gen_act_norms(wl)
+        packs = []
+        for l in range(layers):
+            w = synth.f32_to_bf16_bits(synth.gen_weight_rows(wl.seed + 101 * (l + 1), wl.M, wl.K, wl.dist,
+                                                             wl.scale).astype(np.float32))
+            packs.append(mbd.mbd_pack(mbd.MBD_CASSANDRA, w, norms))
+        secs = packs[0].sections()
+        self.spec_bytes = sum(secs[k][1] for k in mbd.SPEC_SECTIONS)
+        self.full_bytes = sum(b for _, b in secs.values())
+        weight_step = sum(self._layer_bytes(p, mbd) for p in packs)
+        self.n = _pool_copies(weight_step)
+        self.copies = [[mbd.to_device(p, dev) for p in packs] for _ in range(self.n)]
+        self.weight_step = weight_step
+        xs = synth.gen_x(wl, n_draft * layers)              # one activation row per draft call
+        self.xd = [[_x_dev(xs[l * n_draft + t:l * n_draft + t + 1], dev) for t in range(n_draft)]
+                   for l in range(layers)]
+        self.X = [_x_dev(synth.gen_x(wl, n_draft + 1), dev) for _ in range(layers)]
+        self.yd = torch.empty((layers, n_draft, 1, wl.M), dtype=torch.float32, device=dev)
+        self.Y = torch.empty((layers, n_draft + 1, wl.M), dtype=torch.float32, device=dev)
+        self.mbd = mbd
+
+    def _layer_bytes(self, p, mbd):
+        secs = p.sections()
+        return self.N * sum(secs[k][1] for k in mbd.SPEC_SECTIONS) + sum(b for _, b in secs.values())
+
+    def bytes_per_step(self):
+        M, K, N, L = self.M, self.K, self.N, self.L
+        act = L * (N * (2 * K + 4 * M) + (N + 1) * (2 * K + 4 * M))
+        return self.weight_step + act
+
+    def launch(self, i):
+        m, layers = self.mbd, self.copies[i % self.n]
+        for t in range(self.N):                      # draft: token by token through the stack
+            for l, dw in enumerate(layers):
+                m.mbd_spec_gemv(dw, self.xd[l][t], self.yd[l, t])
+        for l, dw in enumerate(layers):              # verify: all N + 1 positions at once
+            m.mbd_gemv(dw, self.X[l], self.Y[l])
+
+    def config(self):
+        a, N = self.alpha, self.N
+        tokens = (1 - a ** (N + 1)) / (1 - a)
+        bf16_per_token = self.L * self.M * self.K * 2
+        return {"workload": self.name, "layers": self.L, "layer": [self.M, self.K], "n_draft": N,
+                "verify_batch": N + 1, "weight_format": "cassandra", "rotation_copies": self.n,
+                "spec_bytes_per_layer": self.spec_bytes, "full_bytes_per_layer": self.full_bytes,
+                "weight_bytes_per_step": self.weight_step, "bytes_per_step": self.bytes_per_step(),
+                "acceptance": a, "tokens_per_step": round(tokens, 4),
+                "bf16_weight_bytes_per_token": bf16_per_token,
+                "weight_bytes_per_token": round(self.weight_step / tokens),
+                "byte_speedup_vs_bf16": round(bf16_per_token / (self.weight_step / tokens), 4)}
+
+
 def make_workload(name, dev):
     if name == "int4_8k":
         return BlockQuantGemv("int4", 8192, 8192, 1, dev, "int4_g128_gemv_8192x8192_b1", "int4_8k")
@@ -231,6 +300,8 @@ def make_workload(name, dev):
         return MoeGemv(1, dev)
     if name == "moe_t8":
         return MoeGemv(8, dev)
+    if name == "cassandra_step":
+        return CassandraStep(dev)
     if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify"):
         return CassandraWl({"cassandra_spec": "spec", "cassandra_restore": "restore",
                             "cassandra_verify": "verify", "mx_verify": "mx"}[name], dev)
@@ -239,7 +310,7 @@ def make_workload(name, dev):
 
 ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4_4096x14336", "int4_14336x4096", "int4_8192x28672",
        "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
-       "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify"]
+       "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_step"]
 
 
 def time_workload(wl, steps, warmup, use_graph=True):

@@ -442,6 +442,38 @@ def test_cassandra_verify_full(dev, verify_full):
     assert err <= TOL
 
 
+def test_cassandra_draft_verify_step(dev):
+    """One speculative step over a two-layer stack: N draft GEMVs per layer over the
+    speculation data (token by token through the stack), then each layer's
+    batch-(N+1) verify GEMM; every output against its own reference."""
+    mbd = _mbd()
+    N, L, M, K = 3, 2, 48, 8192
+    wl = synth.WORKLOADS["cassandra_verify"]
+    norms = synth.gen_act_norms(wl)[:K]
+    ws = [synth.f32_to_bf16_bits(synth.gen_weight_rows(wl.seed + 7 * (l + 1), M, K, wl.dist, wl.scale)
+                                 .astype(np.float32)) for l in range(L)]
+    dws = [_cas(dev, w, norms)[1] for w in ws]
+    xs = synth.gen_x(wl, N * L, K)
+    X = synth.gen_x(wl, N + 1, K)
+    yd = torch.empty((L, N, 1, M), dtype=torch.float32, device=dev)
+    Y = torch.empty((L, N + 1, M), dtype=torch.float32, device=dev)
+    xd = [[_x_dev(xs[l * N + t:l * N + t + 1], dev) for t in range(N)] for l in range(L)]
+    Xd = _x_dev(X, dev)
+    print("case draft/verify step N=%d L=%d %dx%d" % (N, L, M, K), flush=True)
+    for t in range(N):
+        for l in range(L):
+            mbd.mbd_spec_gemv(dws[l], xd[l][t], yd[l, t])
+    for l in range(L):
+        mbd.mbd_gemv(dws[l], Xd, Y[l])
+    torch.cuda.synchronize()
+    for l, w in enumerate(ws):
+        spec = np.where(cassandra.keep_mask(w, norms), w & 0xFFF0, 0).astype(np.uint16)
+        for t in range(N):
+            x = xs[l * N + t:l * N + t + 1]
+            assert gemv.rel_l2(yd[l, t].cpu().numpy(), gemv.gemv(bits.bf16_value(spec), x)) <= TOL
+        assert gemv.rel_l2(Y[l].cpu().numpy(), gemv.gemv(bits.bf16_value(w), X)) <= TOL
+
+
 def test_mx_full(dev, verify_full):
     mbd = _mbd()
     wl, w, norms, x = verify_full
