@@ -17,4 +17,7 @@ from .workloads import (  # noqa: F401
     gen_down_inputs,
     gen_expert,
     stream,
+    gen_zero_blocks,
+    zero_out_blocks,
+    ZERO_BLOCK_FRAC,
 )

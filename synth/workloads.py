@@ -17,6 +17,10 @@ distributions follow the five workloads the hot path is measured on:
                       8 of 64 experts per token, 1 and 8 tokens
 * ``cassandra_spec``  4096 x 14336, t(4) * 0.02, act norms LogNormal(0, 1), batch 1
 * ``cassandra_verify`` 8192 x 28672, same distributions, batch 16
+
+Block-sparse ternary weights (the skip format) take a dense draw and set whole
+128-value blocks to zero, each block independently with probability
+``ZERO_BLOCK_FRAC`` (its own stream, one key per row block).
 """
 from __future__ import annotations
 
@@ -27,7 +31,12 @@ import numpy as np
 ROW_BLOCK = 512
 
 # Stream identifiers (first element of the spawn key).
-S_W, S_OUTLIER, S_X, S_NORM, S_ROUTE, S_DOWN_X = 0, 1, 2, 3, 4, 5
+S_W, S_OUTLIER, S_X, S_NORM, S_ROUTE, S_DOWN_X, S_ZERO = 0, 1, 2, 3, 4, 5, 6
+
+# Fraction of all-zero 128-blocks in block-sparse ternary weights: 2 (1 - z) code
+# bits plus 0.14 bits of scales and tables gives 1.74 bits per weight, under the
+# 1.78 a 27B ternary package averages with its higher-precision embedding.
+ZERO_BLOCK_FRAC = 0.2
 
 
 @dataclass(frozen=True)
@@ -149,3 +158,25 @@ def gen_down_inputs(wl: Workload, T: int) -> np.ndarray:
     """bf16 bits [T][topk][M_up]: an independent N(0, 1) input per (token, expert slot)."""
     a = stream(wl.seed, S_DOWN_X, T).standard_normal((T, wl.topk, wl.M))
     return f32_to_bf16_bits(a.astype(np.float32))
+
+
+def gen_zero_blocks(seed: int, M: int, K: int, frac: float = ZERO_BLOCK_FRAC,
+                    r0: int = 0, r1: int | None = None) -> np.ndarray:
+    """bool [rows][K/128] for rows [r0, r1): block (row, g) is zeroed."""
+    r1 = M if r1 is None else r1
+    G = K // 128
+    out = np.empty((r1 - r0, G), dtype=bool)
+    for b in range(r0 // ROW_BLOCK, (r1 - 1) // ROW_BLOCK + 1):
+        lo, hi = b * ROW_BLOCK, min(M, (b + 1) * ROW_BLOCK)
+        blk = stream(seed, S_ZERO, b).random((hi - lo, G)) < frac
+        s0, s1 = max(lo, r0), min(hi, r1)
+        out[s0 - r0:s1 - r0] = blk[s0 - lo:s1 - lo]
+    return out
+
+
+def zero_out_blocks(w_bits: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """Copy of bf16 bits [rows][K] with the flagged 128-blocks set to +0."""
+    rows, K = w_bits.shape
+    out = np.array(w_bits, dtype=np.uint16, copy=True).reshape(rows, K // 128, 128)
+    out[zero] = 0
+    return out.reshape(rows, K)
