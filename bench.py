@@ -53,6 +53,11 @@ class Workload:
     def launch(self, i: int) -> None: ...
 
 
+def synth_zero_frac():
+    import synth
+    return synth.ZERO_BLOCK_FRAC
+
+
 def _pool_copies(bytes_weights):
     return max(1, math.ceil(POOL_BYTES / max(1, bytes_weights)))
 
@@ -64,15 +69,19 @@ class BlockQuantGemv(Workload):
         import synth
         self.name, self.kind, self.M, self.K, self.B = name, kind, M, K, B
         self.kernel = "gemv_bn_kernel" if B <= 4 else "gemv_mq_kernel"
-        self.fmt_name = {"int4": "int4_g128", "ternary": "ternary_b128"}[kind]
+        self.fmt_name = {"int4": "int4_g128", "ternary": "ternary_b128", "ternary_skip": "ternary_b128_skip"}[kind]
         wl = synth.WORKLOADS[seed_name]
         if (wl.M, wl.K) == (M, K):
             self.w = synth.gen_weights(wl)
         else:
+            seed = wl.seed + 1000 * M + K
             self.w = synth.f32_to_bf16_bits(
-                synth.gen_weight_rows(wl.seed + 1000 * M + K, M, K, wl.dist, wl.scale).astype(np.float32))
+                synth.gen_weight_rows(seed, M, K, wl.dist, wl.scale).astype(np.float32))
+            if kind == "ternary_skip":         # block-sparse: whole 128-blocks zero
+                self.w = synth.zero_out_blocks(self.w, synth.gen_zero_blocks(seed, M, K))
         self.x = synth.gen_x(wl, B, K)
-        fmt = mbd.MBD_INT4_G128 if kind == "int4" else mbd.MBD_TERNARY_B128
+        fmt = {"int4": mbd.MBD_INT4_G128, "ternary": mbd.MBD_TERNARY_B128,
+               "ternary_skip": mbd.MBD_TERNARY_SKIP}[kind]
         self.packed = mbd.mbd_pack(fmt, self.w)
         st = self.packed.stats()
         self.bpw = st.bpw
@@ -91,13 +100,21 @@ class BlockQuantGemv(Workload):
         self.mbd.mbd_gemv(self.copies[i % self.n], self.xt, self.y)
 
     def config(self):
-        return {"workload": self.name, "M": self.M, "K": self.K, "batch": self.B,
-                "weight_format": self.fmt_name, "bits_per_weight": round(self.bpw, 4),
-                "rotation_copies": self.n, "bytes_per_step": self.bytes_per_step()}
+        c = {"workload": self.name, "M": self.M, "K": self.K, "batch": self.B,
+             "weight_format": self.fmt_name, "bits_per_weight": round(self.bpw, 4),
+             "rotation_copies": self.n, "bytes_per_step": self.bytes_per_step()}
+        if self.kind == "ternary_skip":
+            c["zero_block_fraction"] = synth_zero_frac()
+            c["dense_format_bytes"] = self.M * self.K // 4 + self.M * (self.K // 128) * 2
+        return c
 
     def oracle_call(self):
         """One oracle call: unpack + dequant from the packed sections + fp64 matvec."""
-        from oracle import gemv, int4, ternary
+        from oracle import gemv, int4, ternary, ternary_skip
+        if self.kind == "ternary_skip":
+            sec = {k: self.packed.section(k, dt) for k, dt in
+                   (("codes", np.uint32), ("scales", np.uint16), ("slabs", np.uint32), ("tile_base", np.uint32))}
+            return gemv.gemv(ternary_skip.unpack_dequant(sec, self.M, self.K), self.x)
         mod = int4 if self.kind == "int4" else ternary
         codes = self.packed.section("codes", np.uint32).reshape(self.M, -1)
         scales = self.packed.section("scales", np.uint16).reshape(self.M, -1)
@@ -296,6 +313,11 @@ def make_workload(name, dev):
             if name == "%s_%dx%d" % (kind, M, K):
                 return BlockQuantGemv(kind, M, K, 1, dev, "%s_gemv_%dx%d_b1" % (
                     "int4_g128" if kind == "int4" else "ternary_b128", M, K), tag)
+    for (M, K) in ((4096, 14336), (8192, 28672)):
+        for B in (1, 4, 8):
+            if name == "ternary_skip_%dx%d%s" % (M, K, "" if B == 1 else "_b%d" % B):
+                return BlockQuantGemv("ternary_skip", M, K, B, dev, "ternary_skip_gemv_%dx%d_b%d" % (M, K, B),
+                                      "ternary_moe")
     if name == "moe_t1":
         return MoeGemv(1, dev)
     if name == "moe_t8":
@@ -310,7 +332,9 @@ def make_workload(name, dev):
 
 ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4_4096x14336", "int4_14336x4096", "int4_8192x28672",
        "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
-       "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_step"]
+       "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_step",
+       "ternary_skip_8192x28672", "ternary_skip_4096x14336", "ternary_skip_8192x28672_b4",
+       "ternary_skip_8192x28672_b8"]
 
 
 def time_workload(wl, steps, warmup, use_graph=True):

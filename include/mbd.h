@@ -55,7 +55,9 @@ typedef enum {
     MBD_TERNARY_B128 = 1,   /* [Bonsai2] 1.2: 2-bit codes + fp16 scale per 128      */
     MBD_INT4_G128    = 2,   /* [GPT54-INT4] 3.2: 4-bit codes + fp16 scale per 128   */
     MBD_CASSANDRA    = 3,   /* [Cassandra] 3.2-3.3: bit-split speculation / verify  */
-    MBD_MX32         = 4    /* [Cassandra] 3.3: shared max exponent per 32 values   */
+    MBD_MX32         = 4,   /* [Cassandra] 3.3: shared max exponent per 32 values   */
+    MBD_TERNARY_SKIP = 5    /* [Bonsai2] 1.2 + 3.4 / 5.5: ternary, all-zero blocks
+                               flagged and not stored                              */
 } mbd_format;
 
 /* ------------------------------------------------------------------ packing
@@ -91,6 +93,21 @@ typedef enum {
  *                   of a wave, lane = 16*kq + m, read one contiguous run.  A stack of
  *                   n_mats matrices (mbd_pack_params.n_mats) is tiled matrix by
  *                   matrix: its sections are the concatenation of each matrix's.
+ * MBD_TERNARY_SKIP  The MBD_TERNARY_B128 quantizer and word encoding; a block whose
+ *                   codes are all q = 0 ([Bonsai2] 3.4 / 5.5: all-zero, scale 1) is
+ *                   flagged and its codes are not stored.  tiles = ceil(M / 16).
+ *                   (sec 0) "codes"  uint32: the stored blocks, 32 bytes each, tile
+ *                                    by tile, block column g by g; the nz stored
+ *                                    blocks of (tile, g), ranked r by tile row, as
+ *                                    4*nz units of 8 bytes, unit (r, kq) at index
+ *                                    kq*nz + r holding columns 32kq .. +32 (2 words).
+ *                   (sec 1) "scales" fp16 [M][K/128], as MBD_TERNARY_B128.
+ *                   (sec 2) "slabs"  uint32 [tiles][K/128]: bit m (m < R) set when
+ *                                    tile row m's block is stored (clear = the
+ *                                    all-zero flag); bits 16-31: blocks stored in
+ *                                    this tile before column g.  K <= 524288.
+ *                   (sec 3) "tile_base" uint32 [tiles+1]: blocks stored before
+ *                                    tile t; the last entry is the total.
  * MBD_CASSANDRA     Wanda keep count floor(K*keep_num/keep_den) per row, score
  *                   |w| * act_norm[k], ties to the lower k; 3 high mantissa bits
  *                   kept; 4096-element flat tiles.  f = m*K + k is the flat index.

@@ -13,7 +13,7 @@ import numpy as np
 
 from ._native import (  # noqa: F401
     MBD_CASSANDRA, MBD_EALIGN, MBD_EFORMAT, MBD_EHIP, MBD_EINVAL, MBD_ENOMEM, MBD_ERANGE,
-    MBD_ESHAPE, MBD_INT4_G128, MBD_MX32, MBD_OK, MBD_TERNARY_B128, MbdDWeights, MbdError,
+    MBD_ESHAPE, MBD_INT4_G128, MBD_MX32, MBD_OK, MBD_TERNARY_B128, MBD_TERNARY_SKIP, MbdDWeights, MbdError,
     MbdPackParams, MbdSection, MbdStats, check, lib,
 )
 
@@ -22,6 +22,7 @@ SECTION_NAMES = {
     MBD_INT4_G128: ["codes", "scales"],
     MBD_CASSANDRA: ["bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix", "lo_nib", "pruned"],
     MBD_MX32: ["mx_exp", "mx_sign", "mx_mag"],
+    MBD_TERNARY_SKIP: ["codes", "scales", "slabs", "tile_base"],
 }
 SPEC_SECTIONS = ("bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix")
 

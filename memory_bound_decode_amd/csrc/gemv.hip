@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "mbd_internal.h"
 
@@ -276,6 +277,8 @@ constexpr int bn_group_lds(int NB) { return 4 * NB * BN_REC + 32; }
 struct BnArgs {
     const uint8_t* codes;   // tile-interleaved codes of n_mats matrices
     const uint16_t* scales; // [n_mats][M][K / 128]
+    const uint32_t* slabs;  // skip format: [tiles][K / 128] stored-row mask | in-tile offset << 16
+    const uint32_t* tile_base;   // skip format: [tiles + 1] blocks stored before each tile
     const uint16_t* x;
     float* y;
     int M, K;
@@ -288,11 +291,15 @@ struct BnArgs {
 };
 
 // Tile `tile` of one matrix against nb <= NB activation rows xrow(t); output row
-// n of the tile goes to yrow(n).  XU: staging passes of 64 lanes.
-template <bool TER, int PF, int NB, int XU, class XRow, class YRow>
+// n of the tile goes to yrow(n).  XU: staging passes of 64 lanes.  SK (ternary
+// only): the skip format.  An item is still a pair of block columns; lane (m, kq)
+// finds its 8 bytes of each through the column's slab word, or, when tile row m's
+// block is all-zero and not stored, uses code 1 (q = 0) in every field.
+template <bool TER, bool SK, int PF, int NB, int XU, class XRow, class YRow>
 __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int nb, XRow xrow, YRow yrow,
                                         int tile) {
+    static_assert(TER || !SK, "the skip format is ternary");
     constexpr int IG = TER ? 2 : 1;                  // groups per item
     constexpr int GLDS = bn_group_lds(NB);
     extern __shared__ uint4 lds4[];
@@ -301,11 +308,17 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
     const int M = a.M, K = a.K, ngroups = K >> 7;
-    const int n_items = TER ? (ngroups + 1) >> 1 : ngroups;
+    const int n_items = IG == 2 ? (ngroups + 1) >> 1 : ngroups;
     const int n_full = TER ? ngroups >> 1 : ngroups;          // items of 16-byte units
     const int m = lane & 15, kq = lane >> 4;
     const int row0 = tile * 16, R = min(16, M - row0);
-    const uint8_t* tcodes = codes + size_t(row0) * (size_t(K) / (TER ? 4 : 2));
+    const uint8_t* tcodes = SK ? codes + size_t(a.tile_base[tile]) * 32
+                               : codes + size_t(row0) * (size_t(K) / (TER ? 4 : 2));
+    // skip format: lane l holds the slab word of the round's block column l (sw),
+    // the next round's loaded one round ahead (swn)
+    const uint32_t* tsl = SK ? a.slabs + size_t(tile) * ngroups : nullptr;
+    uint32_t swn = 0;
+    if constexpr (SK) swn = tsl[min(IG * wave * a.ipw + lane, ngroups - 1)];
     const uint32_t unit = tile_unit(m, kq, R);
     const int wg = a.ipw * IG;                                // groups a wave stages per round
     char* rec = lds + wave * wg * GLDS;                       // [wg][4][NB][BN_REC]
@@ -322,6 +335,8 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         if (n <= 0) continue;
         const int g0 = it0 * IG, ng = min(n * IG, ngroups - g0);
         const int njobs = 16 * ng * nb;
+        const uint32_t sw = swn;
+        if constexpr (SK) swn = tsl[min(IG * (rb + nw * a.ipw + wave * a.ipw) + lane, ngroups - 1)];
 
         // Staging loads first (vector-memory counters retire in issue order, so the
         // staging waits do not wait for the code stream).  Job j = (row t, local
@@ -353,13 +368,37 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         // The odd last ternary group has 8-byte units: its 16-byte load takes the
         // unit in the low half and 8 bytes past it, which lie inside the codes
         // section or its padding (a load of one width keeps the waits exact).
+        // skip format: bits 2p, 2p + 1 of stf = slot p's two blocks are stored
         uint4 w[PF];
+        uint32_t stf = 0;
         auto issue = [&](int p, int i) __attribute__((always_inline)) {
             const int it = it0 + i;
-            const uint32_t off = (TER && it >= n_full) ? unit * 8 : unit * 16;
-            const u32x4_t v = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(tcodes + size_t(it) * 64 * R + off));
-            w[p] = make_uint4(v.x, v.y, v.z, v.w);
+            if constexpr (SK) {
+                // stored blocks of a column ranked by tile row, unit (rank, kq) at
+                // (kq nz + rank) * 8; a lane whose block is not stored reads the
+                // column's first unit (in bounds: codes are padded) and drops it.
+                // The odd last column's partner is the column itself (not computed).
+                uint32_t v[4], stb = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t ws = uint32_t(__builtin_amdgcn_readlane(int(sw), min(2 * i + h, ng - 1)));
+                    const uint32_t mask = ws & 0xFFFFu;
+                    const uint32_t nz = uint32_t(__builtin_popcount(mask));
+                    const uint32_t rank = uint32_t(__builtin_popcount(mask & ((1u << m) - 1u)));
+                    const bool st = (mask >> m) & 1u;
+                    const uint32_t off = (ws >> 16) * 32u + (st ? (uint32_t(kq) * nz + rank) * 8u : 0u);
+                    const u32x2_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(tcodes + off));
+                    v[2 * h] = u.x; v[2 * h + 1] = u.y;
+                    stb |= uint32_t(st) << h;
+                }
+                w[p] = make_uint4(v[0], v[1], v[2], v[3]);
+                stf = (stf & ~(3u << (2 * p))) | (stb << (2 * p));
+            } else {
+                const uint32_t off = (TER && it >= n_full) ? unit * 8 : unit * 16;
+                const u32x4_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(tcodes + size_t(it) * 64 * R + off));
+                w[p] = make_uint4(v.x, v.y, v.z, v.w);
+            }
         };
 #pragma unroll
         for (int p = 0; p < PF; ++p) issue(p, min(p, n - 1));
@@ -420,8 +459,15 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
             acc[3] = fmaf(half_bits_to_f32(uint16_t(sc.y >> 16)), c[3], acc[3]);
         };
         auto compute = [&](int p, int i) __attribute__((always_inline)) {
-            group(w[p], i * IG);
-            if (TER && it0 + i < n_full) group(make_uint4(w[p].z, w[p].w, 0u, 0u), i * IG + 1);
+            if constexpr (SK) {                          // not stored: code 1 (q = 0) everywhere
+                const bool s0 = (stf >> (2 * p)) & 1u, s1 = (stf >> (2 * p + 1)) & 1u;
+                group(make_uint4(s0 ? w[p].x : 0x55555555u, s0 ? w[p].y : 0x55555555u, 0u, 0u), i * IG);
+                if (it0 + i < n_full)
+                    group(make_uint4(s1 ? w[p].z : 0x55555555u, s1 ? w[p].w : 0x55555555u, 0u, 0u), i * IG + 1);
+            } else {
+                group(w[p], i * IG);
+                if (TER && it0 + i < n_full) group(make_uint4(w[p].z, w[p].w, 0u, 0u), i * IG + 1);
+            }
         };
         int i = 0;
         for (; i + PF < n; i += PF) {
@@ -453,12 +499,12 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
     }
 }
 
-template <bool TER, int PF, int NB, int XU>
+template <bool TER, bool SK, int PF, int NB, int XU>
 __global__ __launch_bounds__(1024) void gemv_bn_kernel(BnArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    bn_core<TER, PF, NB, XU>(a, a.codes, a.scales, a.B, [=](int t) { return x + size_t(t) * K; },
+    bn_core<TER, SK, PF, NB, XU>(a, a.codes, a.scales, a.B, [=](int t) { return x + size_t(t) * K; },
                              [=](int n) { return y + size_t(n) * M; }, blockIdx.x);
 }
 
@@ -474,7 +520,7 @@ __global__ __launch_bounds__(1024) void moe_b1_kernel(BnArgs a) {
     const size_t per_codes = size_t(M) * K / (TER ? 4 : 2), per_scales = size_t(M) * (K / 128);
     const uint16_t* xr = a.x + size_t(a.x_per_pair ? p : p / a.topk) * K;
     float* yr = a.y + size_t(p) * M;
-    bn_core<TER, PF, 1, XU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales, 1,
+    bn_core<TER, false, PF, 1, XU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales, 1,
                             [=](int) { return xr; }, [=](int) { return yr; }, tile);
 }
 
@@ -521,6 +567,8 @@ struct MqGroup {
 struct MqArgs {
     const uint8_t* codes;   // [n_mats][M][K * bits / 8]
     const uint16_t* scales; // [n_mats][M][K / 128]
+    const uint32_t* slabs;  // skip format (see BnArgs)
+    const uint32_t* tile_base;
     const uint16_t* x;
     float* y;
     int M, K;
@@ -549,11 +597,15 @@ __device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s, const Unpac
 }
 
 // Rows [row_base, row_base + MQ_ROWS) of one matrix; nb <= 16 batch rows whose
-// activations / outputs are xrow(b) / yrow(b).
-template <bool TER, class XRow, class YRow>
+// activations / outputs are xrow(b) / yrow(b).  SK: the ternary skip format; the
+// waves take single block columns, and lane j of sw holds the slab word of this
+// wave's column j / MQ_TILES in tile j % MQ_TILES (the launcher keeps a wave's
+// columns times MQ_TILES within 64).
+template <bool TER, bool SK, class XRow, class YRow>
 __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int row_base, int nb, XRow xrow,
                                         YRow yrow) {
+    static_assert(TER || !SK, "the skip format is ternary");
     constexpr int BPR = TER ? 4 : 2;                       // elements per byte
     __shared__ float red[MQ_MAXW][MQ_TILES][64][4];
     const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
@@ -582,10 +634,29 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     }
     const bool xlive = n < nb;
     const uint16_t* xr = xrow(xlive ? n : 0);
-    auto load = [&](int g, MqGroup& d) {
+    // skip format: byte offset of each tile's stored blocks, and the slab words
+    uint32_t tbase[MQ_TILES];
+    uint32_t sw = 0;
+    if constexpr (SK) {
+#pragma unroll
+        for (int t = 0; t < MQ_TILES; ++t) tbase[t] = a.tile_base[min(row_base + 16 * t, (M - 1) & ~15) >> 4] * 32u;
+        const int j = lane / MQ_TILES, tj = lane % MQ_TILES;
+        const int tix = min(row_base + 16 * tj, (M - 1) & ~15) >> 4;
+        sw = a.slabs[size_t(tix) * ngroups + min(wave + nw * j, ngroups - 1)];
+    }
+    auto load = [&](int li, int g, MqGroup& d) {
 #pragma unroll
         for (int t = 0; t < MQ_TILES; ++t) {
-            if constexpr (TER) {
+            if constexpr (SK) {
+                const uint32_t ws = uint32_t(__builtin_amdgcn_readlane(int(sw), li * MQ_TILES + t));
+                const uint32_t mask = ws & 0xFFFFu;
+                const uint32_t nz = uint32_t(__builtin_popcount(mask));
+                const uint32_t rank = uint32_t(__builtin_popcount(mask & ((1u << n) - 1u)));
+                const bool st = (mask >> n) & 1u;
+                const uint32_t off = tbase[t] + (ws >> 16) * 32u + (st ? (uint32_t(q) * nz + rank) * 8u : 0u);
+                const uint2 v = *reinterpret_cast<const uint2*>(codes + off);
+                d.code[t] = make_uint4(v.x, v.y, st ? 1u : 0u, 0u);
+            } else if constexpr (TER) {
                 const int h = g >> 1;
                 const bool pair = h < npairs;
                 const uint8_t* base = codes + (pair ? size_t(h) * item[t] + (g & 1) * 8 : size_t(npairs) * item[t]);
@@ -623,9 +694,13 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
 #pragma unroll
         for (int t = 0; t < MQ_TILES; ++t) {
             f32x4_t cg = cb;
+            uint4 cw = d.code[t];
+            if constexpr (SK) {                            // not stored: code 1 (q = 0) everywhere
+                if (cw.z == 0u) cw = make_uint4(0x55555555u, 0x55555555u, 0u, 0u);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(d.code[t], s, kc),
+                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(cw, s, kc),
                                                              __builtin_bit_cast(bf16x8_t, xb[s]), cg, 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -636,18 +711,20 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     };
     // This wave's groups, in order: INT4 wave, wave + nw, ...; ternary the pairs
     // (2h, 2h + 1) for h = wave, wave + nw, ... (the odd last group alone).
-    const int nitems = TER ? (ngroups + 1) >> 1 : ngroups;
+    constexpr bool PAIRS = TER && !SK;
+    const int nitems = PAIRS ? (ngroups + 1) >> 1 : ngroups;
     const int mine = wave < nitems ? (nitems - 1 - wave) / nw + 1 : 0;
-    const bool odd_tail = TER && (ngroups & 1) && mine > 0 && wave + nw * (mine - 1) == npairs;
-    const int cnt = TER ? 2 * mine - (odd_tail ? 1 : 0) : mine;
-    auto gidx = [&](int i) { return TER ? 2 * (wave + nw * (i >> 1)) + (i & 1) : wave + nw * i; };
+    const bool odd_tail = PAIRS && (ngroups & 1) && mine > 0 && wave + nw * (mine - 1) == npairs;
+    const int cnt = PAIRS ? 2 * mine - (odd_tail ? 1 : 0) : mine;
+    auto gidx = [&](int i) { return PAIRS ? 2 * (wave + nw * (i >> 1)) + (i & 1) : wave + nw * i; };
     // two group buffers, so a buffer is never copied while its loads are in flight
     MqGroup g0, g1;
-    if (cnt > 0) load(gidx(0), g0);
+    if (cnt > 0) load(0, gidx(0), g0);
     for (int i = 0; i < cnt; i += 2) {
-        load(gidx(min(i + 1, cnt - 1)), g1);
+        const int i1 = min(i + 1, cnt - 1), i2 = min(i + 2, cnt - 1);
+        load(i1, gidx(i1), g1);
         compute(g0);
-        load(gidx(min(i + 2, cnt - 1)), g0);
+        load(i2, gidx(i2), g0);
         if (i + 1 < cnt) compute(g1);
     }
 #pragma unroll
@@ -673,12 +750,12 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     }
 }
 
-template <bool TER>
+template <bool TER, bool SK>
 __global__ __launch_bounds__(64 * MQ_MAXW) void gemv_mq_kernel(MqArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    mq_core<TER>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return x + (size_t)b * K; },
+    mq_core<TER, SK>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return x + (size_t)b * K; },
                  [=](int b) { return y + (size_t)b * M; });
 }
 
@@ -708,7 +785,7 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
     float* y = a.y;
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)M * K / (TER ? 4 : 2), per_scales = (size_t)M * (K / 128);
-    mq_core<TER>(
+    mq_core<TER, false>(
         a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * MQ_ROWS, nb,
         [=](int b) {
             const int p = pids[b];
@@ -717,8 +794,30 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
         [=](int b) { return y + (size_t)pids[b] * M; });
 }
 
+// 32 dequantized values q * s of one quarter block from its words (ternary 2,
+// INT4 4).  Element t of a word sits at bit (bits * (t / 2)) + (t odd ? 16 : 0).
+template <bool TER>
+__device__ __forceinline__ void dequant_quarter(const uint32_t* wv, float s, float4* o) {
+    constexpr int bits = TER ? 2 : 4, per = TER ? 16 : 8, off = TER ? 1 : 8, nwd = TER ? 2 : 4;
+    constexpr uint32_t mask = (1u << bits) - 1;
+#pragma unroll
+    for (int wi = 0; wi < nwd; ++wi) {
+#pragma unroll
+        for (int jj = 0; jj < per; jj += 4) {
+            float e[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = jj + u;
+                const int sh = bits * (t >> 1) + ((t & 1) ? 16 : 0);
+                e[u] = s * (float)((int)((wv[wi] >> sh) & mask) - off);
+            }
+            o[(wi * per + jj) / 4] = make_float4(e[0], e[1], e[2], e[3]);
+        }
+    }
+}
+
 // Dense dequant of ternary / INT4: one thread per (row, group, quarter), 32
-// elements.  Element t of a word sits at bit (bits * (t / 2)) + (t odd ? 16 : 0).
+// elements.
 template <bool TER>
 __global__ __launch_bounds__(256) void dequant_bq_kernel(const uint8_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales, float* __restrict__ out,
@@ -743,24 +842,35 @@ __global__ __launch_bounds__(256) void dequant_bq_kernel(const uint8_t* __restri
         const uint4 v = *reinterpret_cast<const uint4*>(tc + size_t(g) * 64 * R + unit * 16);
         wv[0] = v.x; wv[1] = v.y; wv[2] = v.z; wv[3] = v.w;
     }
-    const float s = half_bits_to_f32(scales[row * ngroups + g]);
-    float4* o = reinterpret_cast<float4*>(out + row * K + g * 128 + kq * 32);
-    constexpr int bits = TER ? 2 : 4, per = TER ? 16 : 8, off = TER ? 1 : 8, nwd = TER ? 2 : 4;
-    constexpr uint32_t mask = (1u << bits) - 1;
-#pragma unroll
-    for (int wi = 0; wi < nwd; ++wi) {
-#pragma unroll
-        for (int jj = 0; jj < per; jj += 4) {
-            float e[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int t = jj + u;
-                const int sh = bits * (t >> 1) + ((t & 1) ? 16 : 0);
-                e[u] = s * (float)((int)((wv[wi] >> sh) & mask) - off);
-            }
-            o[(wi * per + jj) / 4] = make_float4(e[0], e[1], e[2], e[3]);
-        }
+    dequant_quarter<TER>(wv, half_bits_to_f32(scales[row * ngroups + g]),
+                         reinterpret_cast<float4*>(out + row * K + g * 128 + kq * 32));
+}
+
+// Skip format: as above, with the block found through its slab word; an all-zero
+// block (not stored) gives zeros.
+__global__ __launch_bounds__(256) void dequant_skip_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint32_t* __restrict__ slabs,
+                                                           const uint32_t* __restrict__ tile_base,
+                                                           float* __restrict__ out, int64_t n_units, int M, int K) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_units) return;
+    const int ngroups = K >> 7;
+    const int kq = int(i & 3);
+    const int64_t rg = i >> 2, row = rg / ngroups;
+    const int g = int(rg - row * ngroups);
+    const int64_t tile = row >> 4;
+    const int m = int(row & 15);
+    const uint32_t ws = slabs[tile * ngroups + g], mask = ws & 0xFFFFu;
+    uint32_t wv[2] = {0x55555555u, 0x55555555u};
+    if ((mask >> m) & 1u) {
+        const uint32_t nz = uint32_t(__builtin_popcount(mask)), rank = uint32_t(__builtin_popcount(mask & ((1u << m) - 1u)));
+        const uint2 v = *reinterpret_cast<const uint2*>(codes + (size_t(tile_base[tile]) + (ws >> 16)) * 32 +
+                                                        (uint32_t(kq) * nz + rank) * 8);
+        wv[0] = v.x; wv[1] = v.y;
     }
+    dequant_quarter<true>(wv, half_bits_to_f32(scales[row * ngroups + g]),
+                          reinterpret_cast<float4*>(out + row * K + g * 128 + kq * 32));
 }
 
 }  // namespace mbd
@@ -819,25 +929,26 @@ BnPlan plan_bn(bool ter, int64_t K, int64_t tiles, int NB) {
 }
 
 // gemv_bn_kernel for the plan's row count and staging passes, or moe_b1_kernel.
-template <bool TER, bool MOE>
+template <bool TER, bool SK, bool MOE>
 mbd_status launch_bn(const BnPlan& pl, const BnArgs& a, unsigned grid, hipStream_t st) {
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * pl.nw), pl.lds, st, a);
         return hip_check(MOE ? "expert gemv launch" : "gemv launch");
     };
     // ring depth: INT4 with one row MBD_B1_PF_I4; more rows (more staging
-    // registers) and ternary MBD_B1_PF_T
+    // registers) and ternary (both formats) MBD_B1_PF_T
     constexpr int PF1 = TER ? MBD_B1_PF_T : MBD_B1_PF_I4, PFN = MBD_B1_PF_T;
     if constexpr (MOE) {
+        static_assert(!SK, "the expert GEMV takes the dense formats");
         if (pl.nb_max == 1 && pl.xu == 1) return go(moe_b1_kernel<TER, PF1, 1>);
         if (pl.nb_max == 1 && pl.xu == 2) return go(moe_b1_kernel<TER, PF1, 2>);
     } else {
         switch (pl.nb_max * 8 + pl.xu) {
-            case 1 * 8 + 1: return go(gemv_bn_kernel<TER, PF1, 1, 1>);
-            case 1 * 8 + 2: return go(gemv_bn_kernel<TER, PF1, 1, 2>);
-            case 4 * 8 + 1: return go(gemv_bn_kernel<TER, PFN, 4, 1>);
-            case 4 * 8 + 2: return go(gemv_bn_kernel<TER, PFN, 4, 2>);
-            case 4 * 8 + 4: return go(gemv_bn_kernel<TER, PFN, 4, 4>);
+            case 1 * 8 + 1: return go(gemv_bn_kernel<TER, SK, PF1, 1, 1>);
+            case 1 * 8 + 2: return go(gemv_bn_kernel<TER, SK, PF1, 1, 2>);
+            case 4 * 8 + 1: return go(gemv_bn_kernel<TER, SK, PFN, 4, 1>);
+            case 4 * 8 + 2: return go(gemv_bn_kernel<TER, SK, PFN, 4, 2>);
+            case 4 * 8 + 4: return go(gemv_bn_kernel<TER, SK, PFN, 4, 4>);
             default: break;
         }
     }
@@ -845,6 +956,49 @@ mbd_status launch_bn(const BnPlan& pl, const BnArgs& a, unsigned grid, hipStream
 }
 
 int bn_rows(int B) { return B <= 1 ? 1 : 4; }
+
+// Ternary with all-zero blocks not stored ([Bonsai2] 3.4, 5.5).  Batch 1..4 on
+// the staged kernel; 5..16 on the 32-row kernel while a wave's block columns
+// times its tiles fit the 64 lanes that hold their slab words (K up to 65536),
+// else as several staged launches of up to 4 rows.
+mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y, hipStream_t st) {
+    if (w->K % 128) return fail(MBD_ESHAPE, "K=%lld is not a multiple of 128", (long long)w->K);
+    if (w->K > 524288 || w->M > INT32_MAX) return fail(MBD_ESHAPE, "shape too large for the skip format");
+    if (w->n_mats > 1) return fail(MBD_EINVAL, "the skip format holds one matrix");
+    if (!w->sec[0] || !w->sec[1] || !w->sec[2] || !w->sec[3]) return fail(MBD_EINVAL, "a section is NULL");
+    if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2) || !aligned(w->sec[2], 4) || !aligned(w->sec[3], 4))
+        return fail(MBD_EALIGN, "codes must be 16-byte, slabs and tile_base 4-byte aligned");
+    if (w->M * w->K / 4 >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "codes beyond 4 GiB");
+    if (w->M == 0) return MBD_OK;
+    const int tiles = int((w->M + 15) / 16);
+    const int ngroups = int(w->K / 128);
+    const int nw_mq = mq_waves(w->K);
+    if (B > 4 && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
+        MqArgs m{};
+        m.codes = static_cast<const uint8_t*>(w->sec[0]);
+        m.scales = static_cast<const uint16_t*>(w->sec[1]);
+        m.slabs = static_cast<const uint32_t*>(w->sec[2]);
+        m.tile_base = static_cast<const uint32_t*>(w->sec[3]);
+        m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
+        const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
+        hipLaunchKernelGGL((gemv_mq_kernel<true, true>), dim3(blocks), dim3(64 * nw_mq), 0, st, m);
+        return hip_check("batched gemv launch");
+    }
+    for (int b0 = 0; b0 < B; b0 += 4) {
+        const int nb = std::min(4, B - b0);
+        const BnPlan pl = plan_bn(true, w->K, tiles, bn_rows(nb));
+        BnArgs a{};
+        a.codes = static_cast<const uint8_t*>(w->sec[0]);
+        a.scales = static_cast<const uint16_t*>(w->sec[1]);
+        a.slabs = static_cast<const uint32_t*>(w->sec[2]);
+        a.tile_base = static_cast<const uint32_t*>(w->sec[3]);
+        a.x = x + size_t(b0) * w->K; a.y = y + size_t(b0) * w->M;
+        a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw; a.tiles = tiles; a.B = nb;
+        mbd_status s = launch_bn<true, true, false>(pl, a, unsigned(tiles), st);
+        if (s != MBD_OK) return s;
+    }
+    return MBD_OK;
+}
 
 }  // namespace
 
@@ -863,6 +1017,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (w->fmt == MBD_CASSANDRA) return mbd_gemv_cassandra(w, x, B, y, st);
     if (w->fmt == MBD_MX32) return mbd_gemv_mx32(w, x, B, y, st);
+    if (w->fmt == MBD_TERNARY_SKIP) return gemv_skip(w, x, B, y, st);
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128) return fail(MBD_EINVAL, "unknown format %d", w->fmt);
     if (w->K % 128) return fail(MBD_ESHAPE, "K=%lld is not a multiple of 128", (long long)w->K);
     if (w->M > INT32_MAX || w->K > INT32_MAX) return fail(MBD_ESHAPE, "shape too large");
@@ -879,8 +1034,8 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
         const int nw = mq_waves(w->K);
         const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
-        if (ter) hipLaunchKernelGGL(gemv_mq_kernel<true>, dim3(blocks), dim3(64 * nw), 0, st, m);
-        else hipLaunchKernelGGL(gemv_mq_kernel<false>, dim3(blocks), dim3(64 * nw), 0, st, m);
+        if (ter) hipLaunchKernelGGL((gemv_mq_kernel<true, false>), dim3(blocks), dim3(64 * nw), 0, st, m);
+        else hipLaunchKernelGGL((gemv_mq_kernel<false, false>), dim3(blocks), dim3(64 * nw), 0, st, m);
         return hip_check("batched gemv launch");
     }
     const int tiles = int((w->M + 15) / 16);
@@ -890,7 +1045,8 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     a.scales = static_cast<const uint16_t*>(w->sec[1]);
     a.x = x; a.y = y; a.M = int(w->M); a.K = int(w->K); a.ipw = pl.ipw;
     a.tiles = tiles; a.B = B;
-    return ter ? launch_bn<true, false>(pl, a, unsigned(tiles), st) : launch_bn<false, false>(pl, a, unsigned(tiles), st);
+    return ter ? launch_bn<true, false, false>(pl, a, unsigned(tiles), st)
+               : launch_bn<false, false, false>(pl, a, unsigned(tiles), st);
 }
 
 mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
@@ -898,8 +1054,22 @@ mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
     if (!aligned(out, 16)) return fail(MBD_EALIGN, "w_out must be 16-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (w->fmt == MBD_MX32) return mbd_dequant_mx32(w, out, st);
+    if (w->fmt == MBD_TERNARY_SKIP) {
+        if (w->M < 0 || w->K < 1 || w->K % 128 || w->K > 524288 || w->M > INT32_MAX) return fail(MBD_ESHAPE, "bad shape");
+        if (w->n_mats > 1) return fail(MBD_EINVAL, "the skip format holds one matrix");
+        if (!w->sec[0] || !w->sec[1] || !w->sec[2] || !w->sec[3]) return fail(MBD_EINVAL, "a section is NULL");
+        if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2) || !aligned(w->sec[2], 4) || !aligned(w->sec[3], 4))
+            return fail(MBD_EALIGN, "misaligned section");
+        if (w->M == 0) return MBD_OK;
+        const int64_t n = w->M * (w->K / 128) * 4;
+        hipLaunchKernelGGL(dequant_skip_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint8_t*>(w->sec[0]), static_cast<const uint16_t*>(w->sec[1]),
+                           static_cast<const uint32_t*>(w->sec[2]), static_cast<const uint32_t*>(w->sec[3]), out, n,
+                           int(w->M), int(w->K));
+        return hip_check("dequant launch");
+    }
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128)
-        return fail(MBD_EINVAL, "dequant supports TERNARY, INT4 and MX32");
+        return fail(MBD_EINVAL, "dequant supports TERNARY, TERNARY_SKIP, INT4 and MX32");
     if (w->M < 0 || w->K < 1 || w->K % 128) return fail(MBD_ESHAPE, "bad shape");
     if (w->M > INT32_MAX || w->K > INT32_MAX) return fail(MBD_ESHAPE, "shape too large");
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
@@ -960,7 +1130,8 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
         a.route = route; a.n_experts = E; a.topk = k; a.x_per_pair = x_per_pair ? 1 : 0;
         const int64_t grid = int64_t(P) * tiles;
         if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-        return ter ? launch_bn<true, true>(pl, a, unsigned(grid), st) : launch_bn<false, true>(pl, a, unsigned(grid), st);
+        return ter ? launch_bn<true, false, true>(pl, a, unsigned(grid), st)
+                   : launch_bn<false, false, true>(pl, a, unsigned(grid), st);
     }
     // more tokens: jobs of up to 16 pairs of one expert on the 32-row kernel, which
     // reads the activations per group and needs no staging (jobs of one or two

@@ -1,7 +1,9 @@
-// Offline CPU packer for the three compressed weight layouts and the MX-32
-// variant, plus the status / error plumbing of the C ABI.
+// Offline CPU packer for the three compressed weight layouts, the MX-32 variant
+// and ternary with all-zero blocks left out, plus the status / error plumbing of
+// the C ABI.
 //
-// Ternary: [Bonsai2] 1.2 (absmean block 128), 3.4 / 5.5 (all-zero block -> scale 1).
+// Ternary: [Bonsai2] 1.2 (absmean block 128), 3.4 / 5.5 (all-zero block -> scale 1,
+//          flagged, its codes not stored).
 // INT4:    [GPT54-INT4] 3.2 (group 128, scale max|w|/7, codes in [-7, 7]).
 // Cassandra: [Cassandra] 3.2 (Wanda pruning + bitmap, mantissa truncation,
 //          speculation + verification = original), 3.3 (unary exponent ranks, MX).
@@ -167,6 +169,65 @@ mbd_status pack_block_quant(mbd_packed* h, const uint16_t* w, bool ternary, int6
     return MBD_OK;
 }
 
+// Ternary with all-zero blocks left out ([Bonsai2] 3.4, 5.5): the dense packing
+// first, then every block whose 8 words are all code 1 (q = 0) is dropped and the
+// rest re-laid per (16-row tile, block column): its stored blocks ranked by tile
+// row, unit (rank, quarter) of 8 bytes at quarter * stored + rank.
+mbd_status pack_ternary_skip(mbd_packed* h, const uint16_t* w) {
+    const int64_t M = h->M, K = h->K, G = K / 128, tiles = (M + 15) / 16;
+    if (16 * G > 65536) return fail(MBD_ESHAPE, "K=%lld too large for the 16-bit in-tile block offset", (long long)K);
+    mbd_status s = pack_block_quant(h, w, true, 1);
+    if (s != MBD_OK) return s;
+    Section dense = std::move(h->sec[0]);
+    const uint32_t* dc = dense.as<uint32_t>();
+    h->sec.resize(4);
+    h->sec[2].name = "slabs";
+    h->sec[2].resize(uint64_t(tiles) * G * 4);
+    h->sec[3].name = "tile_base";
+    h->sec[3].resize(uint64_t(tiles + 1) * 4);
+    uint32_t* slabs = h->sec[2].as<uint32_t>();
+    uint32_t* base = h->sec[3].as<uint32_t>();
+    auto word = [&](int64_t m, int64_t g, int wd) { return dc[code_word_offset(true, m, g, wd, M, K)]; };
+    int64_t total = 0;
+    for (int64_t t = 0; t < tiles; ++t) {
+        const int64_t r0 = 16 * t, R = std::min<int64_t>(16, M - r0);
+        base[t] = uint32_t(total);
+        uint32_t in_tile = 0;
+        for (int64_t g = 0; g < G; ++g) {
+            uint32_t mask = 0;
+            for (int64_t mi = 0; mi < R; ++mi) {
+                bool zero = true;
+                for (int wd = 0; wd < 8; ++wd) zero = zero && word(r0 + mi, g, wd) == 0x55555555u;
+                if (!zero) mask |= 1u << mi;
+            }
+            slabs[t * G + g] = mask | (in_tile << 16);
+            in_tile += uint32_t(__builtin_popcount(mask));
+        }
+        total += in_tile;
+        if (total > int64_t(UINT32_MAX)) return fail(MBD_ESHAPE, "too many stored blocks");
+    }
+    base[tiles] = uint32_t(total);
+    h->sec[0].name = "codes";
+    h->sec[0].resize(uint64_t(total) * 32);
+    uint32_t* codes = h->sec[0].as<uint32_t>();
+    for (int64_t t = 0; t < tiles; ++t) {
+        const int64_t r0 = 16 * t, R = std::min<int64_t>(16, M - r0);
+        for (int64_t g = 0; g < G; ++g) {
+            const uint32_t sw = slabs[t * G + g], mask = sw & 0xFFFFu;
+            const int nz = __builtin_popcount(mask);
+            uint32_t* dst = codes + (int64_t(base[t]) + (sw >> 16)) * 8;
+            int r = 0;
+            for (int64_t mi = 0; mi < R; ++mi) {
+                if (!((mask >> mi) & 1)) continue;
+                for (int kq = 0; kq < 4; ++kq)
+                    for (int j = 0; j < 2; ++j) dst[(kq * nz + r) * 2 + j] = word(r0 + mi, g, 2 * kq + j);
+                ++r;
+            }
+        }
+    }
+    return MBD_OK;
+}
+
 // ------------------------------------------------------------------ Cassandra
 
 mbd_status pack_cassandra(mbd_packed* h, const uint16_t* w, const float* norm) {
@@ -324,6 +385,30 @@ mbd_status validate(const mbd_packed* h) {
             if ((s[i] & 0x7C00) == 0x7C00) return fail(MBD_EFORMAT, "non-finite scale %lld", (long long)i);
         return MBD_OK;
     }
+    if (h->fmt == MBD_TERNARY_SKIP) {
+        const int64_t G = K / 128, tiles = (M + 15) / 16;
+        const uint32_t* c = h->sec[0].as<uint32_t>();
+        const uint32_t* sl = h->sec[2].as<uint32_t>();
+        const uint32_t* base = h->sec[3].as<uint32_t>();
+        for (int64_t i = 0; i < int64_t(h->sec[0].bytes / 4); ++i)
+            if (c[i] & (c[i] >> 1) & 0x55555555u) return fail(MBD_EFORMAT, "ternary code 3 in word %lld", (long long)i);
+        if (base[0] != 0) return fail(MBD_EFORMAT, "tile_base[0] != 0");
+        for (int64_t t = 0; t < tiles; ++t) {
+            const int64_t R = std::min<int64_t>(16, M - 16 * t);
+            uint32_t in_tile = 0;
+            for (int64_t g = 0; g < G; ++g) {
+                const uint32_t sw = sl[t * G + g], mask = sw & 0xFFFFu;
+                if ((mask >> R) || (sw >> 16) != in_tile) return fail(MBD_EFORMAT, "bad slab word (tile %lld, block %lld)", (long long)t, (long long)g);
+                in_tile += uint32_t(__builtin_popcount(mask));
+            }
+            if (uint64_t(base[t + 1]) != uint64_t(base[t]) + in_tile) return fail(MBD_EFORMAT, "bad tile_base at tile %lld", (long long)t);
+        }
+        if (uint64_t(base[tiles]) * 32 != h->sec[0].bytes) return fail(MBD_EFORMAT, "codes size does not match the stored blocks");
+        const uint16_t* s = h->sec[1].as<uint16_t>();
+        for (int64_t i = 0; i < M * G; ++i)
+            if ((s[i] & 0x7C00) == 0x7C00) return fail(MBD_EFORMAT, "non-finite scale %lld", (long long)i);
+        return MBD_OK;
+    }
     if (h->fmt == MBD_MX32) {
         const uint8_t* xe = h->sec[0].as<uint8_t>();
         for (int64_t i = 0; i < M * (K / 32); ++i)
@@ -393,7 +478,7 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w, int64_t M, int64_t K, const 
     if (!out) return fail(MBD_EINVAL, "out is NULL");
     *out = nullptr;
     if (!w) return fail(MBD_EINVAL, "w_bf16_host is NULL");
-    if (fmt < MBD_TERNARY_B128 || fmt > MBD_MX32) return fail(MBD_EINVAL, "unknown format %d", fmt);
+    if (fmt < MBD_TERNARY_B128 || fmt > MBD_TERNARY_SKIP) return fail(MBD_EINVAL, "unknown format %d", fmt);
     if (M < 1 || K < 1) return fail(MBD_ESHAPE, "M and K must be positive");
     int64_t kmul = fmt == MBD_MX32 ? 32 : 128;
     if (K % kmul) return fail(MBD_ESHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)kmul);
@@ -415,6 +500,7 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w, int64_t M, int64_t K, const 
             case MBD_TERNARY_B128: s = pack_block_quant(h, w, true, nm); break;
             case MBD_INT4_G128: s = pack_block_quant(h, w, false, nm); break;
             case MBD_CASSANDRA: s = pack_cassandra(h, w, act_norm); break;
+            case MBD_TERNARY_SKIP: s = pack_ternary_skip(h, w); break;
             default: s = pack_mx32(h, w); break;
         }
         if (s != MBD_OK) { delete h; return s; }

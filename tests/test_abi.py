@@ -97,6 +97,20 @@ def test_validate_detects_corruption(L):
         pc.validate()
     assert e.value.status == mbd.MBD_EFORMAT
 
+    ws = synth.f32_to_bf16_bits((rng.standard_normal((20, 384)) * 0.02).astype(np.float32))
+    ws[3, 128:256] = 0                                                          # one all-zero block
+    ps = mbd.mbd_pack(mbd.MBD_TERNARY_SKIP, ws)
+    ps.validate()
+    secs = (mbd.MbdSection * 4)()
+    assert L.mbd_packed_sections(ps._h, secs, 4, ctypes.byref(n)) == mbd.MBD_OK
+    assert secs[0].bytes == 32 * (20 * 3 - 1)
+    slabs = (ctypes.c_uint32 * 6).from_address(secs[2].data)
+    assert slabs[1] & 0xFFFF == 0xFFFF & ~(1 << 3)
+    slabs[1] |= 1 << 3                                                          # flag says stored, table disagrees
+    with pytest.raises(mbd.MbdError) as e:
+        ps.validate()
+    assert e.value.status == mbd.MBD_EFORMAT
+
 
 def _desc(fmt, M, K, n_sym=0, ptr=0x1000, n_mats=1):
     d = mbd.MbdDWeights()
@@ -125,6 +139,26 @@ def test_gemv_argument_errors(L):
     assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EALIGN
     d = _desc(mbd.MBD_MX32, 16, 48)
     assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_ESHAPE
+
+
+def test_skip_format_argument_errors(L):
+    d = _desc(mbd.MBD_TERNARY_SKIP, 16, 256, ptr=0x10000)
+    d.n_mats = 2
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EINVAL    # one matrix only
+    d.n_mats = 1
+    d.sec[3] = None
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EINVAL    # tile_base missing
+    assert L.mbd_dequant(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL
+    d.sec[3] = 0x10000
+    d.sec[2] = 0x10002
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EALIGN    # slabs 4-byte aligned
+    d.sec[2] = 0x10000
+    d.K = 128 * 4097
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_ESHAPE    # 16-bit in-tile offset
+    d.K = 200
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_ESHAPE
+    e = _desc(mbd.MBD_TERNARY_SKIP, 64, 256)
+    assert L.mbd_moe_gemv(ctypes.byref(e), P16, 1, 1, P16, 0, P16, P16, 1 << 20, None) == mbd.MBD_EINVAL
 
 
 def test_cassandra_and_moe_argument_errors(L):

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import cassandra, int4, mx, ternary
+from oracle import cassandra, int4, mx, ternary, ternary_skip
 
 mbd = pytest.importorskip("memory_bound_decode_amd")
 
@@ -69,6 +69,37 @@ def test_block_quant_ragged_tiles(kind, M, K):
     p = mbd.mbd_pack(fmt, w)
     _check_sections(p, mod.pack(w), ["codes", "scales"])
     p.validate()
+
+
+SKIP_NAMES = ["codes", "scales", "slabs", "tile_base"]
+
+
+@pytest.mark.parametrize("M,K,frac", [(37, 384, 0.3), (16, 128, 0.5), (50, 1152, 0.2), (3, 256, 1.0), (20, 512, 0.0)])
+def test_ternary_skip_sections(M, K, frac):
+    """Block-skipping ternary: every section bit-exact against the oracle,
+    including all-zero and fully dense matrices and ragged last tiles."""
+    w = synth.f32_to_bf16_bits(synth.gen_weight_rows(40 + M, M, K, "t4", 0.02).astype(np.float32))
+    w = synth.zero_out_blocks(w, synth.gen_zero_blocks(40 + M, M, K, frac))
+    p = mbd.mbd_pack(mbd.MBD_TERNARY_SKIP, w)
+    _check_sections(p, ternary_skip.pack(w), SKIP_NAMES)
+    p.validate()
+    st = p.stats()
+    assert st.bpw * M * K == pytest.approx(8 * ternary_skip.stored_bytes(ternary_skip.pack(w)))
+
+
+def test_ternary_skip_workload_rows():
+    wl = synth.WORKLOADS["ternary_moe"]
+    M, K = 64, 28672
+    w = synth.f32_to_bf16_bits(synth.gen_weight_rows(wl.seed, M, K, wl.dist, wl.scale).astype(np.float32))
+    w = synth.zero_out_blocks(w, synth.gen_zero_blocks(wl.seed, M, K))
+    _check_sections(mbd.mbd_pack(mbd.MBD_TERNARY_SKIP, w), ternary_skip.pack(w), SKIP_NAMES)
+
+
+def test_ternary_skip_rejects():
+    with pytest.raises(mbd.MbdError):                 # 16-bit in-tile offset
+        mbd.mbd_pack(mbd.MBD_TERNARY_SKIP, np.zeros((1, 128 * 4097), np.uint16))
+    with pytest.raises(mbd.MbdError):
+        mbd.mbd_pack(mbd.MBD_TERNARY_SKIP, np.zeros((32, 256), np.uint16), n_mats=2)
 
 
 CAS_NAMES = ["bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix", "lo_nib", "pruned"]
