@@ -176,13 +176,16 @@ class CassandraWl(Workload):
         import torch
         import memory_bound_decode_amd as mbd
         import synth
-        wl = synth.WORKLOADS["cassandra_spec" if mode == "spec" else "cassandra_verify"]
+        wl = synth.WORKLOADS["cassandra_spec" if mode in ("spec", "spec_mx") else "cassandra_verify"]
         self.mode, self.M, self.K = mode, wl.M, wl.K
         self.w = synth.gen_weights(wl)
         norms = synth.gen_act_norms(wl)
-        self.fmt_name = "cassandra" if mode != "mx" else "mx32"
+        self.fmt_name = {"mx": "mx32", "spec_mx": "cassandra2_mx32_spec"}.get(mode, "cassandra")
         if mode == "mx":
             p = mbd.mbd_pack(mbd.MBD_MX32, self.w)
+            used = list(p.sections().keys())
+        elif mode == "spec_mx":
+            p = mbd.mbd_pack(mbd.MBD_CASSANDRA_MX, self.w, norms)
             used = list(p.sections().keys())
         else:
             p = mbd.mbd_pack(mbd.MBD_CASSANDRA, self.w, norms)
@@ -195,11 +198,12 @@ class CassandraWl(Workload):
         self.weight_bytes = sum(secs[k][1] for k in used)
         self.n = _pool_copies(self.weight_bytes)
         self.copies = [mbd.to_device(p, dev, only=used) for _ in range(self.n)]
-        self.B = {"spec": 1, "restore": 0, "verify": 16, "mx": 16}[mode]
+        self.B = {"spec": 1, "spec_mx": 1, "restore": 0, "verify": 16, "mx": 16}[mode]
         self.name = {"spec": "cassandra_spec_gemv_4096x14336_b1", "restore": "cassandra_restore_8192x28672",
-                     "verify": "cassandra_verify_gemm_8192x28672_b16", "mx": "mx32_gemm_8192x28672_b16"}[mode]
+                     "verify": "cassandra_verify_gemm_8192x28672_b16", "mx": "mx32_gemm_8192x28672_b16",
+                     "spec_mx": "cassandra2_mx_spec_gemv_4096x14336_b1"}[mode]
         self.kernel = {"spec": "spec_gemv_kernel", "restore": "decode_dense_kernel", "verify": "verify_gemm_kernel",
-                       "mx": "mx_gemm_kernel"}[mode]
+                       "mx": "mx_gemm_kernel", "spec_mx": "mx_spec_gemv_kernel"}[mode]
         if self.B:
             self.xt = _x_dev(synth.gen_x(wl, self.B), dev)
             self.y = torch.empty((self.B, self.M), dtype=torch.float32, device=dev)
@@ -214,7 +218,7 @@ class CassandraWl(Workload):
 
     def launch(self, i):
         m, c = self.mbd, self.copies[i % self.n]
-        if self.mode == "spec":
+        if self.mode in ("spec", "spec_mx"):
             m.mbd_spec_gemv(c, self.xt, self.y)
         elif self.mode == "restore":
             m.mbd_verify_restore(c, self.out)
@@ -324,8 +328,8 @@ def make_workload(name, dev):
         return MoeGemv(8, dev)
     if name == "cassandra_step":
         return CassandraStep(dev)
-    if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify"):
-        return CassandraWl({"cassandra_spec": "spec", "cassandra_restore": "restore",
+    if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_spec_mx"):
+        return CassandraWl({"cassandra_spec": "spec", "cassandra_restore": "restore", "cassandra_spec_mx": "spec_mx",
                             "cassandra_verify": "verify", "mx_verify": "mx"}[name], dev)
     raise SystemExit("unknown workload %s" % name)
 
@@ -334,7 +338,7 @@ ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4
        "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
        "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_step",
        "ternary_skip_8192x28672", "ternary_skip_4096x14336", "ternary_skip_8192x28672_b4",
-       "ternary_skip_8192x28672_b8"]
+       "ternary_skip_8192x28672_b8", "cassandra_spec_mx"]
 
 
 def time_workload(wl, steps, warmup, use_graph=True):

@@ -56,8 +56,10 @@ typedef enum {
     MBD_INT4_G128    = 2,   /* [GPT54-INT4] 3.2: 4-bit codes + fp16 scale per 128   */
     MBD_CASSANDRA    = 3,   /* [Cassandra] 3.2-3.3: bit-split speculation / verify  */
     MBD_MX32         = 4,   /* [Cassandra] 3.3: shared max exponent per 32 values   */
-    MBD_TERNARY_SKIP = 5    /* [Bonsai2] 1.2 + 3.4 / 5.5: ternary, all-zero blocks
+    MBD_TERNARY_SKIP = 5,   /* [Bonsai2] 1.2 + 3.4 / 5.5: ternary, all-zero blocks
                                flagged and not stored                              */
+    MBD_CASSANDRA_MX = 6    /* [Cassandra] 3.3 Cassandra-2: speculation data with the
+                               kept exponents as MX-32 instead of unary codes      */
 } mbd_format;
 
 /* ------------------------------------------------------------------ packing
@@ -123,6 +125,22 @@ typedef enum {
  *                   (sec 6) "lo_nib"   uint32 [ceil(kept/8)]: verification, M & 15
  *                   (sec 7) "pruned"   uint16 [M*K - kept]: verification, raw bits
  *                   Sections 0-5 are the speculation data, 6-7 the verification data.
+ * MBD_CASSANDRA_MX  Speculation data only, the MBD_CASSANDRA keep rule and bitmap;
+ *                   the kept values in kept flat order form groups of 32 (the last
+ *                   may be short).  A kept value (S, E, H = 3 high mantissa bits)
+ *                   has significand sig = E ? 8 + H : H and e' = max(E, 1); X is
+ *                   the largest e' of its group; mag = sig >> (X - e'), 0 once the
+ *                   shift reaches 4.  Draft value (-1)^S * mag * 2^(X - 130), exact
+ *                   in bf16 (-0.0 when mag = 0 and S = 1); pruned positions +0.0.
+ *                   (sec 0) "bitmap"  as MBD_CASSANDRA
+ *                   (sec 1) "mx_nib"  uint32 [ceil(kept/8)]: mag of kept value i at
+ *                                     bits 4*(i%8) of word i/8
+ *                   (sec 2) "mx_sign" uint32 [ceil(kept/32)]: S of kept value i at
+ *                                     bit i%32 of word i/32
+ *                   (sec 3) "mx_exp"  uint8 [ceil(kept/32)]: X of each group
+ *                   (sec 4) "kprefix" uint32 [T+1]: kept values before tile t
+ *                   mbd_spec_decode and mbd_spec_gemv take it; mbd_gemv does not
+ *                   (no verification data).
  * MBD_MX32          (sec 0) "mx_exp"  uint8 [M][K/32]: X = max over the group of
  *                                     max(E, 1)
  *                   (sec 1) "mx_sign" uint32 [M][K/32]: bit i = sign of element i

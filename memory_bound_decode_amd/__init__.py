@@ -13,7 +13,7 @@ import numpy as np
 
 from ._native import (  # noqa: F401
     MBD_CASSANDRA, MBD_EALIGN, MBD_EFORMAT, MBD_EHIP, MBD_EINVAL, MBD_ENOMEM, MBD_ERANGE,
-    MBD_ESHAPE, MBD_INT4_G128, MBD_MX32, MBD_OK, MBD_TERNARY_B128, MBD_TERNARY_SKIP, MbdDWeights, MbdError,
+    MBD_CASSANDRA_MX, MBD_ESHAPE, MBD_INT4_G128, MBD_MX32, MBD_OK, MBD_TERNARY_B128, MBD_TERNARY_SKIP, MbdDWeights, MbdError,
     MbdPackParams, MbdSection, MbdStats, check, lib,
 )
 
@@ -23,6 +23,7 @@ SECTION_NAMES = {
     MBD_CASSANDRA: ["bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix", "lo_nib", "pruned"],
     MBD_MX32: ["mx_exp", "mx_sign", "mx_mag"],
     MBD_TERNARY_SKIP: ["codes", "scales", "slabs", "tile_base"],
+    MBD_CASSANDRA_MX: ["bitmap", "mx_nib", "mx_sign", "mx_exp", "kprefix"],
 }
 SPEC_SECTIONS = ("bitmap", "spec_nib", "unary", "codebook", "bitoff", "kprefix")
 

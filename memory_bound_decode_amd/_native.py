@@ -8,7 +8,7 @@ from ctypes import POINTER, Structure, c_char_p, c_double, c_int32, c_int64, c_u
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmbd.so")
 
 MBD_OK, MBD_EINVAL, MBD_ESHAPE, MBD_EALIGN, MBD_ERANGE, MBD_EFORMAT, MBD_EHIP, MBD_ENOMEM = range(8)
-MBD_TERNARY_B128, MBD_INT4_G128, MBD_CASSANDRA, MBD_MX32, MBD_TERNARY_SKIP = 1, 2, 3, 4, 5
+MBD_TERNARY_B128, MBD_INT4_G128, MBD_CASSANDRA, MBD_MX32, MBD_TERNARY_SKIP, MBD_CASSANDRA_MX = 1, 2, 3, 4, 5, 6
 MBD_MAX_SECTIONS = 8
 
 

@@ -1160,6 +1160,220 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(MxArgs a, float* __rest
     }
 }
 
+// ------------------------------------------------------------------ Cassandra-2 draft (MX-32 exponent code)
+//
+// [Cassandra] 3.3, Cassandra-2: the kept values' exponents are not coded one by
+// one; 32 consecutive kept values share the largest exponent X and keep a 4-bit
+// magnitude, so kept value j is (-1)^S mag 2^(X - 130) with no stream to parse.
+// A lane owns 64 positions of a 4096-element tile (two bitmap words, never across
+// a row since K % 128 == 0); a wave prefix sum of their popcounts gives its first
+// kept index, and it walks its set bits, reading kept values j, j + 1, ... with
+// the nibble word (8 values) and the group's sign word and exponent (32 values)
+// cached in registers.
+
+struct MxSpecArgs {
+    const uint32_t* bitmap;
+    const uint32_t* nib;
+    const uint32_t* sign;
+    const uint8_t* xexp;
+    const uint32_t* kprefix;
+    int64_t M, K, N, T;
+};
+
+struct MxCursor {
+    uint32_t nwi = 0xFFFFFFFFu, gi = 0xFFFFFFFFu, nw = 0, sw = 0;
+    float scale = 0.f;
+    // draft value of kept value j (consecutive calls read cached words)
+    __device__ __forceinline__ float value(const MxSpecArgs& a, uint32_t j) {
+        const uint32_t wi = j >> 3, g = j >> 5;
+        if (wi != nwi) { nw = a.nib[wi]; nwi = wi; }
+        if (g != gi) { sw = a.sign[g]; scale = ldexpf(1.f, int(a.xexp[g]) - 130); gi = g; }
+        const float v = float((nw >> (4 * (j & 7))) & 15u) * scale;   // exact: <= 4 significant bits
+        return ((sw >> (j & 31)) & 1u) ? -v : v;
+    }
+};
+
+// Draft weights, one wave per tile: a lane's 64 values go out as 8 16-byte stores.
+constexpr int MXD_WAVES = 4;
+
+__global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecArgs a, uint16_t* __restrict__ out) {
+    const int lane = lane_id();
+    const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * MXD_WAVES + int(threadIdx.x >> 6));
+    if (t >= a.T) return;
+    const int64_t f = t * TILE + 64 * lane;
+    const bool live = f < a.N;                       // N % 64 == 0: a live lane has both words
+    const uint32_t w0 = live ? a.bitmap[f >> 5] : 0u, w1 = live ? a.bitmap[(f >> 5) + 1] : 0u;
+    const int pc = __popc(w0) + __popc(w1);
+    uint32_t j = a.kprefix[t] + uint32_t(wave_incl_add(pc) - pc);
+    MxCursor c;
+    uint32_t o[32];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        const uint32_t bit = ((i < 32 ? w0 : w1) >> (i & 31)) & 1u;
+        uint32_t v = 0;
+        if (bit) v = __float_as_uint(c.value(a, j++)) >> 16;
+        if (i & 1) o[i >> 1] |= v << 16;
+        else o[i >> 1] = v;
+    }
+    if (live) {
+        uint4* d = reinterpret_cast<uint4*>(out + f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    }
+}
+
+// Draft GEMV.  Block = R consecutive rows, its waves taking the tiles that meet
+// them round robin (a tile shared with the next block is walked by both, each
+// keeping its own rows).  Per tile every lane has one row; the lanes of a row
+// are consecutive, a segmented shuffle sum leaves the row's sum in its first
+// lane, which adds it to the wave's row total in LDS; the waves' totals are
+// summed in wave order at the end.  XL: activations staged in LDS.
+//
+// Software pipeline: a tile's bitmap words are loaded two tiles ahead, and its
+// lanes' nibble, sign and exponent words (all a lane's up to 64 kept values can
+// need: 9 nibble words, 3 groups) one tile ahead, so the walk itself never waits
+// for memory.  In the walk the words move through register queues.
+struct MxLane {
+    uint32_t w0, w1;            // bitmap words of the lane's 64 positions
+    uint32_t j0;                // first kept index
+    uint32_t q[9], sg[3];       // nibble words from j0 / 8, sign words from j0 / 32
+    uint32_t xe;                // exponents of groups j0 / 32 .. + 2 (bytes 0..2)
+};
+
+__device__ __forceinline__ void mx_bitmap(const MxSpecArgs& a, int64_t t, MxLane& L) {
+    const uint32_t f = uint32_t(t * TILE) + 64u * uint32_t(lane_id());
+    const bool live = int64_t(f) < a.N;
+    const uint32_t wi = live ? f >> 5 : 0u;
+    const uint32_t v0 = a.bitmap[wi], v1 = a.bitmap[wi + 1];
+    L.w0 = live ? v0 : 0u;
+    L.w1 = live ? v1 : 0u;
+}
+
+typedef uint32_t mx_u32x4_dw_t __attribute__((ext_vector_type(4), aligned(4)));
+
+// Kept index of the lane's first value and the loads of its words.  Every load
+// is unconditional: indices past the data stay inside the sections' padding.
+__device__ __forceinline__ void mx_prep(const MxSpecArgs& a, int64_t t, MxLane& L) {
+    const int pc = __popc(L.w0) + __popc(L.w1);
+    L.j0 = a.kprefix[t] + uint32_t(wave_incl_add(pc) - pc);
+    const uint32_t* np = a.nib + (L.j0 >> 3);
+    const mx_u32x4_dw_t n0 = *reinterpret_cast<const mx_u32x4_dw_t*>(np);
+    const mx_u32x4_dw_t n1 = *reinterpret_cast<const mx_u32x4_dw_t*>(np + 4);
+    L.q[0] = n0.x; L.q[1] = n0.y; L.q[2] = n0.z; L.q[3] = n0.w;
+    L.q[4] = n1.x; L.q[5] = n1.y; L.q[6] = n1.z; L.q[7] = n1.w;
+    L.q[8] = np[8];
+    const uint32_t g = L.j0 >> 5;
+    L.sg[0] = a.sign[g]; L.sg[1] = a.sign[g + 1]; L.sg[2] = a.sign[g + 2];
+    L.xe = uint32_t(a.xexp[g]) | (uint32_t(a.xexp[g + 1]) << 8) | (uint32_t(a.xexp[g + 2]) << 16);
+}
+
+template <int BMAX, bool XL>
+__global__ __launch_bounds__(1024) void mx_spec_gemv_kernel(MxSpecArgs a, const uint16_t* __restrict__ x, int B,
+                                                            float* __restrict__ y, int R) {
+    extern __shared__ __attribute__((aligned(16))) uint4 sm4[];
+    const int nw = blockDim.x >> 6, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t K = uint32_t(a.K);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(sm4);                          // [BMAX][K]
+    float* red = reinterpret_cast<float*>(xs + (XL ? BMAX * int64_t(K) : 0)); // [nw][R][BMAX]
+    if constexpr (XL)
+        for (int i = threadIdx.x; i < int(uint32_t(B) * K / 8); i += blockDim.x)
+            reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    for (int i = threadIdx.x; i < nw * R * BMAX; i += blockDim.x) red[i] = 0.f;
+    __syncthreads();
+    const uint16_t* xv = XL ? xs : x;
+    const int64_t r0 = int64_t(blockIdx.x) * R, r1 = min<int64_t>(a.M, r0 + R);
+    const int64_t t_a = (r0 * K) / TILE, t_b = (r1 * K - 1) / TILE;
+    float* wred = red + wave * R * BMAX;
+    const int64_t tw0 = t_a + wave;
+    const int ntiles = t_b >= tw0 ? int((t_b - tw0) / nw) + 1 : 0;
+    auto tile_of = [&](int i) { return tw0 + int64_t(min(i, ntiles - 1)) * nw; };
+
+    auto walk = [&](int64_t t, const MxLane& L) {
+        const uint32_t f = uint32_t(t * TILE) + 64u * uint32_t(lane);   // N <= 2^32
+        const bool live = int64_t(f) < a.N;
+        const uint32_t row = f / K, col0 = f - row * K;
+        const bool mine = live && int64_t(row) >= r0 && int64_t(row) < r1;
+        float acc[BMAX];
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) acc[b] = 0.f;
+        if (mine) {
+            uint64_t mm = uint64_t(L.w0) | (uint64_t(L.w1) << 32);
+            uint32_t q0 = L.q[0] >> (4 * (L.j0 & 7)), q1 = L.q[1], q2 = L.q[2], q3 = L.q[3], q4 = L.q[4],
+                     q5 = L.q[5], q6 = L.q[6], q7 = L.q[7], q8 = L.q[8];
+            uint32_t s0 = L.sg[0] >> (L.j0 & 31), s1 = L.sg[1], s2 = L.sg[2], xe = L.xe;
+            int ni = int(L.j0 & 7), si = int(L.j0 & 31);
+            float scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
+            const uint16_t* xc = xv + col0;
+            while (mm) {
+                const int p = __builtin_ctzll(mm);
+                mm &= mm - 1;
+                float v = float(q0 & 15u) * scale;               // exact: <= 4 significant bits
+                v = (s0 & 1u) ? -v : v;
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b)
+                    if (b < B) acc[b] = fmaf(v, __uint_as_float(uint32_t(xc[b * K + p]) << 16), acc[b]);
+                q0 >>= 4;
+                s0 >>= 1;
+                if (++ni == 8) {
+                    ni = 0;
+                    q0 = q1; q1 = q2; q2 = q3; q3 = q4; q4 = q5; q5 = q6; q6 = q7; q7 = q8;
+                }
+                if (++si == 32) {
+                    si = 0;
+                    s0 = s1; s1 = s2;
+                    xe >>= 8;
+                    scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
+                }
+            }
+        }
+        // segmented suffix sums over the lanes of each row (rows are contiguous
+        // lane ranges): afterwards the first lane of a row holds the row's sum
+        const int rid = int(row);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int orow = __shfl_down(rid, off, 64);
+            const bool add = lane + off < 64 && orow == rid;
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+                const float o = __shfl_down(acc[b], off, 64);
+                acc[b] = add ? acc[b] + o : acc[b];
+            }
+        }
+        const int prow = __shfl_up(rid, 1, 64);
+        if (mine && (lane == 0 || prow != rid)) {
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) wred[int(row - r0) * BMAX + b] += acc[b];
+        }
+    };
+
+    // two lane buffers: tile i walks from one while tile i + 1's words load into
+    // the other (a buffer is never copied while its loads are in flight)
+    MxLane la, lb;
+    if (ntiles > 0) {
+        mx_bitmap(a, tile_of(0), la);
+        mx_bitmap(a, tile_of(1), lb);
+        mx_prep(a, tile_of(0), la);
+    }
+    for (int i = 0; i < ntiles; i += 2) {
+        mx_prep(a, tile_of(i + 1), lb);
+        walk(tile_of(i), la);
+        mx_bitmap(a, tile_of(i + 2), la);
+        mx_prep(a, tile_of(i + 2), la);
+        if (i + 1 < ntiles) walk(tile_of(i + 1), lb);
+        mx_bitmap(a, tile_of(i + 3), lb);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * BMAX; i += blockDim.x) {
+        const int r = i / BMAX, b = i - r * BMAX;
+        if (b < B && r0 + r < r1) {
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += red[(w * R + r) * BMAX + b];
+            y[int64_t(b) * a.M + r0 + r] = sum;
+        }
+    }
+}
+
 }  // namespace cas
 }  // namespace mbd
 
@@ -1236,6 +1450,73 @@ mbd_status decode_dense(const mbd_dweights* w, uint16_t* out, hipStream_t st, bo
     return hip_check(restore ? "restore launch" : "spec decode launch");
 }
 
+mbd_status mx_spec_args(const mbd_dweights* w, MxSpecArgs* a) {
+    if (!w) return fail(MBD_EINVAL, "NULL descriptor");
+    if (w->M < 0 || w->K < 128 || w->K % 128) return fail(MBD_ESHAPE, "Cassandra needs K a positive multiple of 128");
+    if (w->M * w->K > int64_t(UINT32_MAX)) return fail(MBD_ESHAPE, "M*K exceeds the 32-bit kept prefix");
+    for (int i = 0; i < 5; ++i) {
+        if (!w->sec[i]) return fail(MBD_EINVAL, "section %d is NULL", i);
+        if (!aligned(w->sec[i], 16)) return fail(MBD_EALIGN, "section %d is not 16-byte aligned", i);
+    }
+    a->bitmap = static_cast<const uint32_t*>(w->sec[0]);
+    a->nib = static_cast<const uint32_t*>(w->sec[1]);
+    a->sign = static_cast<const uint32_t*>(w->sec[2]);
+    a->xexp = static_cast<const uint8_t*>(w->sec[3]);
+    a->kprefix = static_cast<const uint32_t*>(w->sec[4]);
+    a->M = w->M;
+    a->K = w->K;
+    a->N = w->M * w->K;
+    a->T = (a->N + TILE - 1) / TILE;
+    return MBD_OK;
+}
+
+mbd_status mx_spec_decode(const mbd_dweights* w, uint16_t* out, hipStream_t st) {
+    MxSpecArgs a;
+    mbd_status s = mx_spec_args(w, &a);
+    if (s != MBD_OK) return s;
+    if (!out) return fail(MBD_EINVAL, "output is NULL");
+    if (!aligned(out, 16)) return fail(MBD_EALIGN, "output must be 16-byte aligned");
+    if (a.N == 0) return MBD_OK;
+    hipLaunchKernelGGL(mx_spec_decode_kernel, dim3(unsigned((a.T + MXD_WAVES - 1) / MXD_WAVES)), dim3(64 * MXD_WAVES),
+                       0, st, a, out);
+    return hip_check("spec decode launch");
+}
+
+// Rows per block: about 32 tiles a block; waves: up to 16, one per tile.
+// Activations go to LDS when they fit in 64 KB.
+mbd_status mx_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y, hipStream_t st) {
+    MxSpecArgs a;
+    mbd_status s = mx_spec_args(w, &a);
+    if (s != MBD_OK) return s;
+    if (!x || !y) return fail(MBD_EINVAL, "NULL argument");
+    if (B < 1 || B > 16) return fail(MBD_ESHAPE, "B=%d outside [1, 16]", B);
+    if (!aligned(x, 16) || !aligned(y, 4)) return fail(MBD_EALIGN, "x must be 16-byte and y 4-byte aligned");
+    if (a.M == 0) return MBD_OK;
+    const int bmax = round_batch(B);
+    const bool xl = int64_t(bmax) * a.K * 2 <= 64 * 1024;
+    int R = int(std::max<int64_t>(1, std::min<int64_t>(64, (32 * TILE) / a.K))), nw = 1;
+    size_t lds = 0;
+    for (;; R /= 2) {                                   // fewer rows until the LDS fits
+        const int64_t tiles = (int64_t(R) * a.K + TILE - 1) / TILE + 1;
+        nw = int(std::min<int64_t>(16, tiles));
+        lds = (xl ? size_t(bmax) * a.K * 2 : 0) + size_t(nw) * R * bmax * 4;
+        if (lds <= 150 * 1024 || R == 1) break;
+    }
+    const unsigned blocks = unsigned((a.M + R - 1) / R);
+#define MBD_MXS_CASE(BM, XL)                                                                                     \
+    if (bmax == BM && xl == XL) {                                                                                \
+        static std::atomic<int> done{0};                                                                         \
+        const void* kern = reinterpret_cast<const void*>(mx_spec_gemv_kernel<BM, XL>);                           \
+        if ((s = lds_limit(kern, done, lds, "draft GEMV")) != MBD_OK) return s;                                  \
+        hipLaunchKernelGGL((mx_spec_gemv_kernel<BM, XL>), dim3(blocks), dim3(64 * nw), lds, st, a, x, B, y, R);  \
+        return hip_check("spec GEMV launch");                                                                    \
+    }
+    MBD_MXS_CASE(1, true) MBD_MXS_CASE(2, true) MBD_MXS_CASE(4, true) MBD_MXS_CASE(8, true) MBD_MXS_CASE(16, true)
+    MBD_MXS_CASE(1, false) MBD_MXS_CASE(2, false) MBD_MXS_CASE(4, false) MBD_MXS_CASE(8, false) MBD_MXS_CASE(16, false)
+#undef MBD_MXS_CASE
+    return fail(MBD_EINVAL, "no draft GEMV variant");
+}
+
 }  // namespace
 
 mbd_status mbd_gemv_cassandra(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y, hipStream_t st) {
@@ -1282,6 +1563,7 @@ mbd_status mbd_dequant_mx32(const mbd_dweights* w, float* out, hipStream_t st) {
 extern "C" {
 
 mbd_status mbd_spec_decode(const mbd_dweights* w, uint16_t* w_spec, void* stream) {
+    if (w && w->fmt == MBD_CASSANDRA_MX) return mx_spec_decode(w, w_spec, reinterpret_cast<hipStream_t>(stream));
     return decode_dense(w, w_spec, reinterpret_cast<hipStream_t>(stream), false);
 }
 
@@ -1290,6 +1572,7 @@ mbd_status mbd_verify_restore(const mbd_dweights* w, uint16_t* w_out, void* stre
 }
 
 mbd_status mbd_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y, void* stream) {
+    if (w && w->fmt == MBD_CASSANDRA_MX) return mx_spec_gemv(w, x, B, y, reinterpret_cast<hipStream_t>(stream));
     CasArgs a;
     mbd_status s = cas_args(w, false, &a);
     if (s != MBD_OK) return s;

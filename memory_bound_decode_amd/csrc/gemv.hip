@@ -1018,6 +1018,8 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (w->fmt == MBD_CASSANDRA) return mbd_gemv_cassandra(w, x, B, y, st);
     if (w->fmt == MBD_MX32) return mbd_gemv_mx32(w, x, B, y, st);
     if (w->fmt == MBD_TERNARY_SKIP) return gemv_skip(w, x, B, y, st);
+    if (w->fmt == MBD_CASSANDRA_MX)
+        return fail(MBD_EINVAL, "MBD_CASSANDRA_MX holds speculation data only: use mbd_spec_gemv");
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128) return fail(MBD_EINVAL, "unknown format %d", w->fmt);
     if (w->K % 128) return fail(MBD_ESHAPE, "K=%lld is not a multiple of 128", (long long)w->K);
     if (w->M > INT32_MAX || w->K > INT32_MAX) return fail(MBD_ESHAPE, "shape too large");

@@ -230,7 +230,9 @@ mbd_status pack_ternary_skip(mbd_packed* h, const uint16_t* w) {
 
 // ------------------------------------------------------------------ Cassandra
 
-mbd_status pack_cassandra(mbd_packed* h, const uint16_t* w, const float* norm) {
+// Wanda keep bitmap ([Cassandra] 3.2): per row the floor(K * keep) highest
+// |w| * norm, ties to the lower k; also rejects non-finite inputs.
+mbd_status wanda_bitmap(const mbd_packed* h, const uint16_t* w, const float* norm, std::vector<uint32_t>& bitmap) {
     const int64_t M = h->M, K = h->K, N = M * K;
     const int64_t nk_row = (K * h->keep_num) / h->keep_den;
     for (int64_t k = 0; k < K; ++k)
@@ -238,10 +240,7 @@ mbd_status pack_cassandra(mbd_packed* h, const uint16_t* w, const float* norm) {
             return fail(MBD_ERANGE, "act_norm[%lld] is negative or not finite", (long long)k);
     for (int64_t f = 0; f < N; ++f)
         if (bf16_nonfinite(w[f])) return fail(MBD_ERANGE, "bf16 Inf/NaN at flat index %lld", (long long)f);
-
-    // 1. Wanda keep bitmap: per row the nk_row highest |w| * norm, ties to lower k.
-    const int64_t nbw = (N + 31) / 32;
-    std::vector<uint32_t> bitmap(nbw, 0);
+    bitmap.assign((N + 31) / 32, 0);
     parallel_rows(M, [&](int64_t r0, int64_t r1) {
         std::vector<double> score(K);
         std::vector<int32_t> idx(K);
@@ -262,6 +261,16 @@ mbd_status pack_cassandra(mbd_packed* h, const uint16_t* w, const float* norm) {
             }
         }
     });
+    return MBD_OK;
+}
+
+mbd_status pack_cassandra(mbd_packed* h, const uint16_t* w, const float* norm) {
+    const int64_t N = h->M * h->K;
+    // 1. Wanda keep bitmap.
+    std::vector<uint32_t> bitmap;
+    mbd_status st = wanda_bitmap(h, w, norm, bitmap);
+    if (st != MBD_OK) return st;
+    const int64_t nbw = int64_t(bitmap.size());
 
     // 2. Exponent histogram of kept values -> codebook by (-count, exponent).
     int64_t hist[256] = {0};
@@ -362,6 +371,64 @@ mbd_status pack_mx32(mbd_packed* h, const uint16_t* w) {
     return MBD_OK;
 }
 
+// Cassandra-2 speculation data ([Cassandra] 3.3): the kept values of the same
+// Wanda bitmap, in groups of 32 consecutive kept values sharing their largest
+// effective exponent X = max(max(E, 1)); each keeps sign and the 4-bit
+// significand (implicit one + 3 high mantissa bits) shifted right by X - e'.
+mbd_status pack_cassandra_mx(mbd_packed* h, const uint16_t* w, const float* norm) {
+    const int64_t N = h->M * h->K;
+    std::vector<uint32_t> bitmap;
+    mbd_status st = wanda_bitmap(h, w, norm, bitmap);
+    if (st != MBD_OK) return st;
+    int64_t nk = 0;
+    for (uint32_t b : bitmap) nk += __builtin_popcount(b);
+    const int64_t T = (N + kTile - 1) / kTile, ng = (nk + 31) / 32;
+    h->n_kept = nk;
+    h->n_tiles = T;
+    h->sec.resize(5);
+    const char* names[5] = {"bitmap", "mx_nib", "mx_sign", "mx_exp", "kprefix"};
+    for (int i = 0; i < 5; ++i) h->sec[i].name = names[i];
+    h->sec[0].resize(uint64_t(bitmap.size()) * 4);
+    h->sec[1].resize(uint64_t((nk + 7) / 8) * 4);
+    h->sec[2].resize(uint64_t(ng) * 4);
+    h->sec[3].resize(uint64_t(ng));
+    h->sec[4].resize(uint64_t(T + 1) * 4);
+    std::memcpy(h->sec[0].buf.data(), bitmap.data(), bitmap.size() * 4);
+    uint32_t* nib = h->sec[1].as<uint32_t>();
+    uint32_t* sign = h->sec[2].as<uint32_t>();
+    uint8_t* xexp = h->sec[3].as<uint8_t>();
+    uint32_t* kprefix = h->sec[4].as<uint32_t>();
+    uint16_t grp[32];
+    int gn = 0;
+    int64_t j = 0;
+    auto flush = [&]() {
+        const int64_t g = (j - gn) / 32;
+        int X = 1;
+        for (int i = 0; i < gn; ++i) X = std::max(X, std::max(int((grp[i] >> 7) & 0xFF), 1));
+        for (int i = 0; i < gn; ++i) {
+            const uint32_t b = grp[i], E = (b >> 7) & 0xFF, H = (b & 0x7F) >> (7 - kMantHiBits);
+            const int d = X - std::max(int(E), 1);
+            const uint32_t sig = E ? 8u + H : H, mag = d >= 4 ? 0u : sig >> d;
+            const int64_t idx = 32 * g + i;
+            nib[idx >> 3] |= mag << (4 * (idx & 7));
+            sign[g] |= (b >> 15) << i;
+        }
+        xexp[g] = uint8_t(X);
+        gn = 0;
+    };
+    for (int64_t f = 0; f < N; ++f) {
+        if ((f % kTile) == 0) kprefix[f / kTile] = uint32_t(j);
+        if ((bitmap[f >> 5] >> (f & 31)) & 1) {
+            grp[gn++] = w[f];
+            ++j;
+            if (gn == 32) flush();
+        }
+    }
+    if (gn) flush();
+    kprefix[T] = uint32_t(j);
+    return MBD_OK;
+}
+
 // ------------------------------------------------------------------ validation
 
 mbd_status validate(const mbd_packed* h) {
@@ -407,6 +474,26 @@ mbd_status validate(const mbd_packed* h) {
         const uint16_t* s = h->sec[1].as<uint16_t>();
         for (int64_t i = 0; i < M * G; ++i)
             if ((s[i] & 0x7C00) == 0x7C00) return fail(MBD_EFORMAT, "non-finite scale %lld", (long long)i);
+        return MBD_OK;
+    }
+    if (h->fmt == MBD_CASSANDRA_MX) {
+        const uint32_t* bm = h->sec[0].as<uint32_t>();
+        const uint8_t* xe = h->sec[3].as<uint8_t>();
+        const uint32_t* kp = h->sec[4].as<uint32_t>();
+        const int64_t nk_row = (K * h->keep_num) / h->keep_den;
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t c = 0;
+            for (int64_t k = 0; k < K; ++k) { int64_t f = m * K + k; c += (bm[f >> 5] >> (f & 31)) & 1; }
+            if (c != nk_row) return fail(MBD_EFORMAT, "row %lld keeps %lld, expected %lld", (long long)m, (long long)c, (long long)nk_row);
+        }
+        int64_t j = 0;
+        for (int64_t t = 0; t < h->n_tiles; ++t) {
+            if (int64_t(kp[t]) != j) return fail(MBD_EFORMAT, "kprefix mismatch at tile %lld", (long long)t);
+            for (int64_t f = t * kTile; f < std::min(N, (t + 1) * kTile); ++f) j += (bm[f >> 5] >> (f & 31)) & 1;
+        }
+        if (int64_t(kp[h->n_tiles]) != j || j != h->n_kept) return fail(MBD_EFORMAT, "kprefix sentinel mismatch");
+        for (int64_t g = 0; g < (h->n_kept + 31) / 32; ++g)
+            if (xe[g] == 0 || xe[g] == 255) return fail(MBD_EFORMAT, "bad shared exponent in group %lld", (long long)g);
         return MBD_OK;
     }
     if (h->fmt == MBD_MX32) {
@@ -478,18 +565,19 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w, int64_t M, int64_t K, const 
     if (!out) return fail(MBD_EINVAL, "out is NULL");
     *out = nullptr;
     if (!w) return fail(MBD_EINVAL, "w_bf16_host is NULL");
-    if (fmt < MBD_TERNARY_B128 || fmt > MBD_TERNARY_SKIP) return fail(MBD_EINVAL, "unknown format %d", fmt);
+    if (fmt < MBD_TERNARY_B128 || fmt > MBD_CASSANDRA_MX) return fail(MBD_EINVAL, "unknown format %d", fmt);
+    const bool cas = fmt == MBD_CASSANDRA || fmt == MBD_CASSANDRA_MX;
     if (M < 1 || K < 1) return fail(MBD_ESHAPE, "M and K must be positive");
     int64_t kmul = fmt == MBD_MX32 ? 32 : 128;
     if (K % kmul) return fail(MBD_ESHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)kmul);
-    if (fmt == MBD_CASSANDRA && !act_norm) return fail(MBD_EINVAL, "Cassandra packing needs act_norm_host");
+    if (cas && !act_norm) return fail(MBD_EINVAL, "Cassandra packing needs act_norm_host");
     int32_t kn = 3, kd = 10;
     int64_t nm = 1;
     if (params) { kn = params->keep_num; kd = params->keep_den; nm = params->n_mats ? params->n_mats : 1; }
     if (nm < 1 || M % nm) return fail(MBD_EINVAL, "n_mats=%lld does not divide M=%lld", (long long)nm, (long long)M);
     if (nm > 1 && fmt != MBD_TERNARY_B128 && fmt != MBD_INT4_G128) return fail(MBD_EINVAL, "n_mats > 1 needs TERNARY or INT4");
-    if (fmt == MBD_CASSANDRA && (kd < 1 || kn < 0 || kn > kd)) return fail(MBD_EINVAL, "keep fraction %d/%d", kn, kd);
-    if (fmt == MBD_CASSANDRA && M * K > int64_t(UINT32_MAX)) return fail(MBD_ESHAPE, "M*K exceeds the 32-bit kept prefix");
+    if (cas && (kd < 1 || kn < 0 || kn > kd)) return fail(MBD_EINVAL, "keep fraction %d/%d", kn, kd);
+    if (cas && M * K > int64_t(UINT32_MAX)) return fail(MBD_ESHAPE, "M*K exceeds the 32-bit kept prefix");
     mbd_packed* h = nullptr;
     try {
         h = new mbd_packed();
@@ -501,6 +589,7 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w, int64_t M, int64_t K, const 
             case MBD_INT4_G128: s = pack_block_quant(h, w, false, nm); break;
             case MBD_CASSANDRA: s = pack_cassandra(h, w, act_norm); break;
             case MBD_TERNARY_SKIP: s = pack_ternary_skip(h, w); break;
+            case MBD_CASSANDRA_MX: s = pack_cassandra_mx(h, w, act_norm); break;
             default: s = pack_mx32(h, w); break;
         }
         if (s != MBD_OK) { delete h; return s; }
@@ -529,6 +618,7 @@ mbd_status mbd_packed_stats(const mbd_packed* h, mbd_stats* o) {
     double n = double(h->M) * double(h->K), total = 0;
     for (auto& s : h->sec) total += double(s.bytes) * 8;
     o->bpw = total / n;
+    if (h->fmt == MBD_CASSANDRA_MX) o->spec_bpw = o->bpw;   // speculation data only
     if (h->fmt == MBD_CASSANDRA) {
         double spec = 0;
         for (int i = 0; i < 6; ++i) spec += double(h->sec[i].bytes) * 8;

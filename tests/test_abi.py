@@ -161,6 +161,20 @@ def test_skip_format_argument_errors(L):
     assert L.mbd_moe_gemv(ctypes.byref(e), P16, 1, 1, P16, 0, P16, P16, 1 << 20, None) == mbd.MBD_EINVAL
 
 
+def test_cassandra_mx_argument_errors(L):
+    d = _desc(mbd.MBD_CASSANDRA_MX, 16, 256, ptr=0x10000)
+    assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EINVAL    # speculation data only
+    assert L.mbd_spec_gemv(ctypes.byref(d), P16, 17, P16, None) == mbd.MBD_ESHAPE
+    d.sec[4] = None
+    assert L.mbd_spec_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EINVAL  # kprefix missing
+    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_EINVAL
+    d.sec[4] = 0x10008
+    assert L.mbd_spec_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EALIGN
+    d.sec[4] = 0x10000
+    d.K = 200
+    assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_ESHAPE
+
+
 def test_cassandra_and_moe_argument_errors(L):
     d = _desc(mbd.MBD_CASSANDRA, 16, 256, n_sym=0)
     d.n_kept = 5

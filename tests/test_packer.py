@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import cassandra, int4, mx, ternary, ternary_skip
+from oracle import cassandra, cassandra_mx, int4, mx, ternary, ternary_skip
 
 mbd = pytest.importorskip("memory_bound_decode_amd")
 
@@ -128,6 +128,34 @@ def test_cassandra_ragged_and_keep_fraction():
         norms = rng.lognormal(0, 1, K).astype(np.float32)
         p = mbd.mbd_pack(mbd.MBD_CASSANDRA, w, norms, kn, kd)
         _check_sections(p, cassandra.pack(w, norms, kn, kd), CAS_NAMES)
+        p.validate()
+
+
+CASMX_NAMES = ["bitmap", "mx_nib", "mx_sign", "mx_exp", "kprefix"]
+
+
+def test_cassandra_mx_spec_workload():
+    wl = synth.WORKLOADS["cassandra_spec"]
+    w = synth.gen_weights(wl, 0, 256)
+    norms = synth.gen_act_norms(wl)
+    p = mbd.mbd_pack(mbd.MBD_CASSANDRA_MX, w, norms)
+    ref = cassandra_mx.pack_spec(w, norms)
+    _check_sections(p, ref, CASMX_NAMES)
+    p.validate()
+    st = p.stats()
+    assert st.n_kept == ref["n_kept"]
+    assert st.spec_bpw * w.size == pytest.approx(cassandra_mx.spec_bits(ref))
+
+
+def test_cassandra_mx_ragged_and_keep_fraction():
+    rng = np.random.default_rng(19)
+    for (M, K, kn, kd) in [(3, 1024, 3, 10), (5, 128, 1, 2), (3, 1152, 3, 10), (2, 4096 + 128, 3, 10),
+                           (7, 256, 0, 1), (2, 256, 1, 1), (33, 384, 3, 10)]:
+        w = synth.f32_to_bf16_bits((rng.standard_t(4, (M, K)) * 0.02).astype(np.float32))
+        w[0, :7] = [0, 0x8000, 1, 0x8001, 0x0080, 0x3F80, 0xBF80]     # zeros, subnormals, a normal min, +-1
+        norms = rng.lognormal(0, 1, K).astype(np.float32)
+        p = mbd.mbd_pack(mbd.MBD_CASSANDRA_MX, w, norms, kn, kd)
+        _check_sections(p, cassandra_mx.pack_spec(w, norms, kn, kd), CASMX_NAMES)
         p.validate()
 
 
