@@ -301,6 +301,42 @@ class CassandraStep(Workload):
                 "byte_speedup_vs_bf16": round(bf16_per_token / (self.weight_step / tokens), 4)}
 
 
+class CassandraEncode(Workload):
+    """Device encoder: the eight Cassandra sections of the 4096 x 14336 draft
+    workload's weight from device bf16 weights and activation norms (the encode
+    call; its plan is made once, outside the timed region)."""
+    kernel = "enc_select_kernel"
+
+    def __init__(self, dev):
+        import torch
+        import memory_bound_decode_amd as mbd
+        import synth
+        wl = synth.WORKLOADS["cassandra_spec"]
+        self.M, self.K = wl.M, wl.K
+        w = synth.gen_weights(wl)
+        norms = synth.gen_act_norms(wl)
+        self.n = _pool_copies(w.nbytes)
+        self.wd = [torch.from_numpy(w.view(np.int16)).to(dev) for _ in range(self.n)]
+        self.nd = torch.from_numpy(norms).to(dev)
+        self.ws = torch.empty(mbd.mbd_encode_workspace_bytes(self.M), dtype=torch.uint8, device=dev)
+        self.plan = mbd.mbd_encode_plan(self.wd[0], self.nd, 3, 10, self.ws)
+        self.secs = [torch.empty(int(self.plan.padded_bytes[i]), dtype=torch.uint8, device=dev) for i in range(8)]
+        self.name = "cassandra_encode_4096x14336"
+        self.fmt_name = "cassandra"
+        self.mbd = mbd
+
+    def bytes_per_step(self):
+        return self.M * self.K * 2 + self.K * 4 + sum(int(b) for b in self.plan.bytes)
+
+    def launch(self, i):
+        self.mbd.mbd_encode_cassandra(self.wd[i % self.n], self.nd, 3, 10, self.plan, self.secs, self.ws)
+
+    def config(self):
+        return {"workload": self.name, "M": self.M, "K": self.K, "weight_format": self.fmt_name,
+                "kept": int(self.plan.n_kept), "n_sym": int(self.plan.n_sym), "unary_bits": int(self.plan.unary_bits),
+                "rotation_copies": self.n, "bytes_per_step": self.bytes_per_step()}
+
+
 def make_workload(name, dev):
     if name == "int4_8k":
         return BlockQuantGemv("int4", 8192, 8192, 1, dev, "int4_g128_gemv_8192x8192_b1", "int4_8k")
@@ -328,6 +364,8 @@ def make_workload(name, dev):
         return MoeGemv(8, dev)
     if name == "cassandra_step":
         return CassandraStep(dev)
+    if name == "cassandra_encode":
+        return CassandraEncode(dev)
     if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_spec_mx"):
         return CassandraWl({"cassandra_spec": "spec", "cassandra_restore": "restore", "cassandra_spec_mx": "spec_mx",
                             "cassandra_verify": "verify", "mx_verify": "mx"}[name], dev)
@@ -338,7 +376,7 @@ ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4
        "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
        "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_step",
        "ternary_skip_8192x28672", "ternary_skip_4096x14336", "ternary_skip_8192x28672_b4",
-       "ternary_skip_8192x28672_b8", "cassandra_spec_mx"]
+       "ternary_skip_8192x28672_b8", "cassandra_spec_mx", "cassandra_encode"]
 
 
 def time_workload(wl, steps, warmup, use_graph=True):

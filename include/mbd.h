@@ -255,6 +255,38 @@ mbd_status mbd_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, fl
  * 3.2, path c): bf16 w_out [M][K], 16-byte aligned. */
 mbd_status mbd_verify_restore(const mbd_dweights* w, uint16_t* w_out, void* stream);
 
+/* ------------------------------------------------------------------ device encoder
+ * [Cassandra] 3.2-3.3 (and 3.5, the online encoder the paper builds in hardware):
+ * the eight MBD_CASSANDRA sections of a bf16 weight already in device memory,
+ * bit-identical to mbd_pack(MBD_CASSANDRA) with the same keep fraction.
+ * w: bf16 [M][K] device, 16-byte aligned; act_norm: fp32 [K] device; K % 128 == 0,
+ * M*K < 2^32.  ws: device workspace of mbd_encode_workspace_bytes(M) bytes,
+ * 16-byte aligned, shared by both calls (contents overwritten).
+ * mbd_encode_plan runs the pruning and the exponent histogram and returns the
+ * section sizes; it SYNCHRONISES `stream` to read two totals back, and reports
+ * MBD_ERANGE for Inf/NaN in w or a negative / non-finite act_norm entry.
+ * mbd_encode_cassandra then writes every section: sec[i] is a device buffer of at
+ * least plan->padded_bytes[i] bytes, 16-byte aligned (padding zeroed by the call).
+ * It only enqueues work; w and act_norm must be those the plan was made from (the
+ * unary stream is cut at the planned size otherwise).  Calls that share a
+ * workspace must not overlap. */
+typedef struct {
+    int64_t n_kept;
+    int64_t unary_bits;
+    int64_t n_tiles;
+    int32_t n_sym;
+    int32_t reserved;
+    uint64_t bytes[8];         /* meaningful bytes of each section, MBD_CASSANDRA order */
+    uint64_t padded_bytes[8];  /* buffer bytes the encode call writes               */
+} mbd_encode_plan_t;
+mbd_status mbd_encode_workspace_bytes(int64_t M, uint64_t* bytes);
+mbd_status mbd_encode_plan(const uint16_t* w, const float* act_norm, int64_t M, int64_t K,
+                           int32_t keep_num, int32_t keep_den, void* ws, uint64_t ws_bytes,
+                           mbd_encode_plan_t* plan, void* stream);
+mbd_status mbd_encode_cassandra(const uint16_t* w, const float* act_norm, int64_t M, int64_t K,
+                                int32_t keep_num, int32_t keep_den, const mbd_encode_plan_t* plan,
+                                void* const* sec, void* ws, uint64_t ws_bytes, void* stream);
+
 const char* mbd_status_str(mbd_status s);
 const char* mbd_last_error(void);
 

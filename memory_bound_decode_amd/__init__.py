@@ -14,7 +14,7 @@ import numpy as np
 from ._native import (  # noqa: F401
     MBD_CASSANDRA, MBD_EALIGN, MBD_EFORMAT, MBD_EHIP, MBD_EINVAL, MBD_ENOMEM, MBD_ERANGE,
     MBD_CASSANDRA_MX, MBD_ESHAPE, MBD_INT4_G128, MBD_MX32, MBD_OK, MBD_TERNARY_B128, MBD_TERNARY_SKIP, MbdDWeights, MbdError,
-    MbdPackParams, MbdSection, MbdStats, check, lib,
+    MbdEncodePlan, MbdPackParams, MbdSection, MbdStats, check, lib,
 )
 
 SECTION_NAMES = {
@@ -171,3 +171,28 @@ def mbd_spec_gemv(dw: DeviceWeights, x, y, stream=None) -> None:
 
 def mbd_verify_restore(dw: DeviceWeights, out, stream=None) -> None:
     check(lib().mbd_verify_restore(dw.ref(), _ptr(out), _stream(stream)), "mbd_verify_restore")
+
+
+def mbd_encode_workspace_bytes(M: int) -> int:
+    n = ctypes.c_uint64(0)
+    check(lib().mbd_encode_workspace_bytes(M, ctypes.byref(n)), "mbd_encode_workspace_bytes")
+    return int(n.value)
+
+
+def mbd_encode_plan(w, act_norm, keep_num: int, keep_den: int, ws, stream=None) -> MbdEncodePlan:
+    """Device encoder, first call (synchronises the stream): section sizes of the
+    Cassandra sections of device bf16 w [M][K] (int16 tensor) and fp32 act_norm."""
+    M, K = w.shape
+    plan = MbdEncodePlan()
+    check(lib().mbd_encode_plan(_ptr(w), _ptr(act_norm), M, K, keep_num, keep_den, _ptr(ws), ws.numel() * ws.element_size(),
+                                ctypes.byref(plan), _stream(stream)), "mbd_encode_plan")
+    return plan
+
+
+def mbd_encode_cassandra(w, act_norm, keep_num: int, keep_den: int, plan: MbdEncodePlan, sections, ws, stream=None) -> None:
+    """Device encoder, second call: writes the eight sections into ``sections``
+    (device uint8 tensors of at least plan.padded_bytes[i] bytes each)."""
+    M, K = w.shape
+    arr = (ctypes.c_void_p * 8)(*[t.data_ptr() for t in sections])
+    check(lib().mbd_encode_cassandra(_ptr(w), _ptr(act_norm), M, K, keep_num, keep_den, ctypes.byref(plan), arr, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "mbd_encode_cassandra")

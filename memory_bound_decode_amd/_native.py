@@ -37,6 +37,11 @@ class MbdDWeights(Structure):
 
 
 # name -> (restype, argtypes); every symbol include/mbd.h declares
+class MbdEncodePlan(Structure):
+    _fields_ = [("n_kept", c_int64), ("unary_bits", c_int64), ("n_tiles", c_int64), ("n_sym", c_int32),
+                ("reserved", c_int32), ("bytes", c_uint64 * 8), ("padded_bytes", c_uint64 * 8)]
+
+
 SIGNATURES = {
     "mbd_pack": (c_int32, [c_int32, POINTER(c_uint16), c_int64, c_int64, c_void_p,
                            POINTER(MbdPackParams), POINTER(c_void_p)]),
@@ -52,6 +57,11 @@ SIGNATURES = {
     "mbd_spec_decode": (c_int32, [POINTER(MbdDWeights), c_void_p, c_void_p]),
     "mbd_spec_gemv": (c_int32, [POINTER(MbdDWeights), c_void_p, c_int32, c_void_p, c_void_p]),
     "mbd_verify_restore": (c_int32, [POINTER(MbdDWeights), c_void_p, c_void_p]),
+    "mbd_encode_workspace_bytes": (c_int32, [c_int64, POINTER(c_uint64)]),
+    "mbd_encode_plan": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int32, c_int32, c_void_p, c_uint64,
+                                  POINTER(MbdEncodePlan), c_void_p]),
+    "mbd_encode_cassandra": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int32, c_int32,
+                                       POINTER(MbdEncodePlan), POINTER(c_void_p), c_void_p, c_uint64, c_void_p]),
     "mbd_status_str": (c_char_p, [c_int32]),
     "mbd_last_error": (c_char_p, []),
 }

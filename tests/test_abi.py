@@ -175,6 +175,28 @@ def test_cassandra_mx_argument_errors(L):
     assert L.mbd_spec_decode(ctypes.byref(d), P16, None) == mbd.MBD_ESHAPE
 
 
+def test_encoder_argument_errors(L):
+    n = ctypes.c_uint64()
+    assert L.mbd_encode_workspace_bytes(0, ctypes.byref(n)) == mbd.MBD_ESHAPE
+    assert L.mbd_encode_workspace_bytes(8, ctypes.byref(n)) == mbd.MBD_OK and n.value >= 8 * 8
+    plan = mbd.MbdEncodePlan()
+    args = lambda M, K, ws, wsb, w=P16: L.mbd_encode_plan(w, P16, M, K, 3, 10, ws, wsb, ctypes.byref(plan), None)
+    assert args(8, 256, P16, n.value, w=None) == mbd.MBD_EINVAL
+    assert args(8, 200, P16, n.value) == mbd.MBD_ESHAPE                             # K % 128
+    assert args(8, 256, P16, 16) == mbd.MBD_EINVAL                                  # workspace too small
+    assert args(8, 256, ctypes.c_void_p(0x10008), n.value) == mbd.MBD_EALIGN
+    assert L.mbd_encode_plan(P16, P16, 8, 256, 3, 10, P16, n.value, None, None) == mbd.MBD_EINVAL
+    # every call below fails validation before anything is enqueued (fake pointers)
+    secs = (ctypes.c_void_p * 8)(*([0x10000] * 8))
+    plan.n_kept, plan.n_tiles = 8 * 76 + 1, 1                                       # a plan of another shape
+    assert L.mbd_encode_cassandra(P16, P16, 8, 256, 3, 10, ctypes.byref(plan), secs, P16, n.value, None) == mbd.MBD_EINVAL
+    plan.n_kept = 8 * 76
+    secs[2] = None                                                                  # unary buffer missing
+    assert L.mbd_encode_cassandra(P16, P16, 8, 256, 3, 10, ctypes.byref(plan), secs, P16, n.value, None) == mbd.MBD_EINVAL
+    secs[2] = 0x10008
+    assert L.mbd_encode_cassandra(P16, P16, 8, 256, 3, 10, ctypes.byref(plan), secs, P16, n.value, None) == mbd.MBD_EALIGN
+
+
 def test_cassandra_and_moe_argument_errors(L):
     d = _desc(mbd.MBD_CASSANDRA, 16, 256, n_sym=0)
     d.n_kept = 5
