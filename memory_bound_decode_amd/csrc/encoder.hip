@@ -332,65 +332,92 @@ struct WordSink {
 
 // The streams of one row: kept values' nibbles and unary codes in kept order,
 // pruned values raw, and the tile-table entries of tiles that start in the row.
-// Unary writes stay below cap_words (the caller's buffer), also if w changed
-// between the plan and this call.
-__global__ __launch_bounds__(NT) void enc_write_kernel(EncArgs a, int64_t T, uint64_t total_bits, uint64_t cap_words) {
-    __shared__ uint32_t scan32[NT];
-    __shared__ uint64_t scan64[NT];
+// NS threads; a thread owns WPT bitmap words (32 WPT columns), read as 16-byte
+// loads into registers (WPT = 0: any width, read element by element).  Unary
+// writes stay below cap_words (the caller's buffer), also if w changed between
+// the plan and this call.
+template <int WPT>
+__global__ __launch_bounds__(NS) void enc_write_kernel(EncArgs a, int64_t T, uint64_t total_bits, uint64_t cap_words) {
+    __shared__ uint32_t scan32[NS];
+    __shared__ uint64_t scan64[NS];
     __shared__ uint32_t rk[256];
+    constexpr int CPT = WPT > 0 ? 32 * WPT : 2;
     const int t = threadIdx.x;
-    rk[t] = a.rank_of[t];
+    if (t < 256) rk[t] = a.rank_of[t];
     __syncthreads();
     const int64_t r = blockIdx.x, K = a.K;
-    const int nwords = int(K / 32), wpt = (nwords + NT - 1) / NT;
+    const int nwords = int(K / 32), wpt = WPT > 0 ? WPT : (nwords + NS - 1) / NS;
     const int w0 = min(nwords, t * wpt), w1 = min(nwords, w0 + wpt);
+    const int c0 = 32 * w0, c1 = 32 * w1;
     const uint16_t* wr = a.w + r * K;
     const uint32_t* bm = a.bitmap + (r * K) / 32;
+    uint32_t wv[CPT / 2], bw[WPT > 0 ? WPT : 1];
+    if constexpr (WPT > 0) {
+        // words past the thread's last (the row's last thread may own fewer) read as 0
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const bool own = w0 + q < w1;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint4 v = own ? *reinterpret_cast<const uint4*>(wr + c0 + 32 * q + 8 * h) : make_uint4(0, 0, 0, 0);
+                wv[16 * q + 4 * h] = v.x; wv[16 * q + 4 * h + 1] = v.y;
+                wv[16 * q + 4 * h + 2] = v.z; wv[16 * q + 4 * h + 3] = v.w;
+            }
+            bw[q] = own ? bm[w0 + q] : 0u;
+        }
+    }
+    // f(i, w bits, kept) for the thread's columns c0 + i in order
+    auto each = [&](auto&& f) __attribute__((always_inline)) {
+        if constexpr (WPT > 0) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i)
+                if (c0 + i < c1) f(i, uint16_t(wv[i >> 1] >> (16 * (i & 1))), ((bw[i >> 5] >> (i & 31)) & 1u) != 0u);
+        } else {
+            for (int i = 0; i < c1 - c0; ++i) f(i, wr[c0 + i], ((bm[w0 + (i >> 5)] >> (i & 31)) & 1u) != 0u);
+        }
+    };
     uint32_t kc = 0;
     uint64_t bc = 0;
-    for (int wd = w0; wd < w1; ++wd) {
-        const uint32_t b = bm[wd];
-        kc += __popc(b);
-        for (int i = 0; i < 32; ++i)
-            if ((b >> i) & 1u) bc += rk[(wr[32 * wd + i] >> 7) & 0xFF] + 1;
-    }
+    each([&](int, uint16_t v, bool kept) {
+        if (kept) {
+            ++kc;
+            bc += rk[(v >> 7) & 0xFF] + 1;
+        }
+    });
     uint32_t j = block_excl_scan<uint32_t>(kc, scan32, nullptr);      // kept before, in the row
     uint64_t bit = a.rows[r] + block_excl_scan<uint64_t>(bc, scan64, nullptr);
+    if (r == a.M - 1 && t == 0) {                                      // sentinel
+        a.kprefix[T] = uint32_t(a.M * int64_t(a.nk));
+        a.bitoff[T] = total_bits;
+    }
+    if (c0 >= c1) return;
     const int64_t kbase = r * int64_t(a.nk), pbase = r * (K - a.nk);
     const uint64_t g0 = uint64_t(kbase + j), nib_words = (uint64_t(a.M) * a.nk + 7) / 8;
     WordSink sn{a.spec_nib, 4 * g0, 4 * (g0 + kc), nib_words};
     WordSink ln{a.lo_nib, 4 * g0, 4 * (g0 + kc), nib_words};
     WordSink un{a.unary, bit, bit + bc, cap_words};
-    for (int wd = w0; wd < w1; ++wd) {
-        const uint32_t b = bm[wd];
-        for (int i = 0; i < 32; ++i) {
-            const int64_t c = 32 * wd + i, f = r * K + c;
-            if (f % TILE == 0) {                                       // a tile starts here
-                a.kprefix[f / TILE] = uint32_t(kbase + j);
-                a.bitoff[f / TILE] = bit;
-            }
-            const uint16_t v = wr[c];
-            if ((b >> i) & 1u) {
-                const uint64_t g = uint64_t(kbase + j);
-                const uint32_t S = v >> 15, E = (v >> 7) & 0xFF, Mn = v & 0x7F;
-                sn.put(4 * g, (S << 3) | (Mn >> MANT_LO_BITS));
-                ln.put(4 * g, Mn & ((1u << MANT_LO_BITS) - 1));
-                const uint64_t end = bit + rk[E];                     // rank zeros, then the one
-                un.put(end, 1u);
-                bit = end + 1;
-                ++j;
-            } else {
-                a.pruned[pbase + (c - j)] = v;
-            }
+    each([&](int i, uint16_t v, bool kept) {
+        const int64_t c = c0 + i, f = r * K + c;
+        if (f % TILE == 0) {                                           // a tile starts here
+            a.kprefix[f / TILE] = uint32_t(kbase + j);
+            a.bitoff[f / TILE] = bit;
         }
-    }
+        if (kept) {
+            const uint64_t g = uint64_t(kbase + j);
+            const uint32_t S = v >> 15, E = (v >> 7) & 0xFF, Mn = v & 0x7F;
+            sn.put(4 * g, (S << 3) | (Mn >> MANT_LO_BITS));
+            ln.put(4 * g, Mn & ((1u << MANT_LO_BITS) - 1));
+            const uint64_t end = bit + rk[E];                         // rank zeros, then the one
+            un.put(end, 1u);
+            bit = end + 1;
+            ++j;
+        } else {
+            a.pruned[pbase + (c - j)] = v;
+        }
+    });
     sn.flush();
     ln.flush();
     un.flush();
-    if (r == a.M - 1 && t == 0) {                                      // sentinel
-        a.kprefix[T] = uint32_t(a.M * int64_t(a.nk));
-        a.bitoff[T] = total_bits;
-    }
 }
 
 }  // namespace enc
@@ -528,8 +555,14 @@ mbd_status mbd_encode_cassandra(const uint16_t* w, const float* act_norm, int64_
     hipLaunchKernelGGL(enc_codebook_kernel, dim3(1), dim3(256), 0, st, a, 1);
     hipLaunchKernelGGL(enc_rowbits_kernel, dim3(unsigned(M)), dim3(NT), 0, st, a);
     hipLaunchKernelGGL(enc_rowscan_kernel, dim3(1), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(enc_write_kernel, dim3(unsigned(M)), dim3(NT), 0, st, a, T, uint64_t(plan->unary_bits),
-                       plan->padded_bytes[2] / 4);
+    {
+        const int64_t wpt = (K / 32 + NS - 1) / NS;
+        const dim3 g(static_cast<unsigned>(M)), b(NS);
+        const uint64_t ub = uint64_t(plan->unary_bits), cap = plan->padded_bytes[2] / 4;
+        if (wpt <= 1) hipLaunchKernelGGL((enc_write_kernel<1>), g, b, 0, st, a, T, ub, cap);
+        else if (wpt <= 2) hipLaunchKernelGGL((enc_write_kernel<2>), g, b, 0, st, a, T, ub, cap);
+        else hipLaunchKernelGGL((enc_write_kernel<0>), g, b, 0, st, a, T, ub, cap);
+    }
     return enc_hip("encoder launch");
 }
 

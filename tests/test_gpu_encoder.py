@@ -60,7 +60,8 @@ def _check(dev, w, norms, keep):
 
 
 SHAPES = [(3, 1024, (3, 10)), (5, 128, (1, 2)), (33, 1152, (3, 10)), (2, 4096 + 128, (3, 10)), (7, 256, (0, 1)),
-          (2, 256, (1, 1)), (17, 8192, (3, 10)), (1, 28672, (3, 10))]
+          (2, 256, (1, 1)), (17, 8192, (3, 10)), (1, 28672, (3, 10)),
+          (2, 40960, (3, 10)), (1, 65536 + 128, (3, 10))]      # wider rows: other thread layouts
 
 
 @pytest.mark.parametrize("M,K,keep", SHAPES)
