@@ -559,10 +559,18 @@ inline int mq_waves(int64_t K) {
 
 struct MqGroup {
     uint4 code[MQ_TILES];          // INT4: 4 words (32 codes); ternary: .x, .y (32 codes)
-    uint32_t sc[MQ_TILES][4];      // raw fp16 scales of the lane's 4 output rows: packing them
-                                   // at issue would wait for the loads (and all before them)
+    uint32_t sc[MQ_TILES][4];      // raw fp16 scales of the lane's 4 output rows (global
+                                   // path): packing them at issue would wait for the loads
     uint4 xv[4];                   // 32 activations of batch row n
+    int g;                         // the group (scales from LDS)
 };
+
+// Scales staged in LDS per block, [group][MQ_ROWS], while they fit this budget.
+constexpr int MQ_SCALE_LDS = 32 * 1024;
+#ifndef MBD_MQ_DEPTH
+#define MBD_MQ_DEPTH 2        // group buffers per wave
+#endif
+constexpr int MQ_DEPTH = MBD_MQ_DEPTH;
 
 struct MqArgs {
     const uint8_t* codes;   // [n_mats][M][K * bits / 8]
@@ -597,17 +605,21 @@ __device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s, const Unpac
 }
 
 // Rows [row_base, row_base + MQ_ROWS) of one matrix; nb <= 16 batch rows whose
-// activations / outputs are xrow(b) / yrow(b).  SK: the ternary skip format; the
+// activations / outputs are xrow(b) / yrow(b).  SL: the block's fp16 scales are
+// staged in LDS once (coalesced row runs) and a lane reads its 4 rows' scales of
+// a group with one 8-byte LDS read, instead of 4 global loads per tile and group.
+// SK: the ternary skip format; the
 // waves take single block columns, and lane j of sw holds the slab word of this
 // wave's column j / MQ_TILES in tile j % MQ_TILES (the launcher keeps a wave's
 // columns times MQ_TILES within 64).
-template <bool TER, bool SK, class XRow, class YRow>
+template <bool TER, bool SK, bool SL, class XRow, class YRow>
 __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int row_base, int nb, XRow xrow,
                                         YRow yrow) {
     static_assert(TER || !SK, "the skip format is ternary");
     constexpr int BPR = TER ? 4 : 2;                       // elements per byte
     __shared__ float red[MQ_MAXW][MQ_TILES][64][4];
+    extern __shared__ uint16_t mq_sc[];                    // SL: [ngroups][MQ_ROWS]
     const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, q = lane >> 4;
@@ -631,6 +643,13 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
         orow[t] = row_base + 16 * t + 4 * q;
 #pragma unroll
         for (int j = 0; j < 4; ++j) soff[t][j] = uint32_t(min(orow[t] + j, M - 1)) * uint32_t(2 * ngroups);   // bytes
+    }
+    if constexpr (SL) {
+        for (int i = threadIdx.x; i < ngroups * MQ_ROWS; i += blockDim.x) {
+            const int rr = i / ngroups, g = i - rr * ngroups;
+            mq_sc[g * MQ_ROWS + rr] = scales[size_t(min(row_base + rr, M - 1)) * ngroups + g];
+        }
+        __syncthreads();
     }
     const bool xlive = n < nb;
     const uint16_t* xr = xrow(xlive ? n : 0);
@@ -665,10 +684,13 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             } else {
                 d.code[t] = *reinterpret_cast<const uint4*>(codes + size_t(g) * item[t] + coff[t]);
             }
-            const char* sg = reinterpret_cast<const char*>(scales + g);
+            if constexpr (!SL) {
+                const char* sg = reinterpret_cast<const char*>(scales + g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) d.sc[t][j] = *reinterpret_cast<const uint16_t*>(sg + soff[t][j]);
+                for (int j = 0; j < 4; ++j) d.sc[t][j] = *reinterpret_cast<const uint16_t*>(sg + soff[t][j]);
+            }
         }
+        d.g = g;
         const uint4* px = reinterpret_cast<const uint4*>(xr + size_t(g) * 128 + 32 * q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) d.xv[i] = px[i];
@@ -702,9 +724,17 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             for (int s = 0; s < 4; ++s)
                 cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(cw, s, kc),
                                                              __builtin_bit_cast(bf16x8_t, xb[s]), cg, 0, 0, 0);
+            uint32_t scr[4];
+            if constexpr (SL) {
+                const uint2 sv = *reinterpret_cast<const uint2*>(mq_sc + d.g * MQ_ROWS + 16 * t + 4 * q);
+                scr[0] = sv.x; scr[1] = sv.x >> 16; scr[2] = sv.y; scr[3] = sv.y >> 16;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) scr[j] = d.sc[t][j];
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sc = half_bits_to_f32(uint16_t(d.sc[t][j]));
+                const float sc = half_bits_to_f32(uint16_t(scr[j]));
                 acc[t][j] = fmaf(sc, cg[j], acc[t][j]);
             }
         }
@@ -717,15 +747,21 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     const bool odd_tail = PAIRS && (ngroups & 1) && mine > 0 && wave + nw * (mine - 1) == npairs;
     const int cnt = PAIRS ? 2 * mine - (odd_tail ? 1 : 0) : mine;
     auto gidx = [&](int i) { return PAIRS ? 2 * (wave + nw * (i >> 1)) + (i & 1) : wave + nw * i; };
-    // two group buffers, so a buffer is never copied while its loads are in flight
-    MqGroup g0, g1;
-    if (cnt > 0) load(0, gidx(0), g0);
-    for (int i = 0; i < cnt; i += 2) {
-        const int i1 = min(i + 1, cnt - 1), i2 = min(i + 2, cnt - 1);
-        load(i1, gidx(i1), g1);
-        compute(g0);
-        load(i2, gidx(i2), g0);
-        if (i + 1 < cnt) compute(g1);
+    // MQ_DEPTH group buffers (a buffer is never copied while its loads are in
+    // flight): the next MQ_DEPTH - 1 groups' loads are in flight while one is
+    // computed; indices past the last group reload the last one
+    MqGroup gb[MQ_DEPTH];
+    if (cnt > 0) {
+#pragma unroll
+        for (int p = 0; p < MQ_DEPTH - 1; ++p) load(min(p, cnt - 1), gidx(min(p, cnt - 1)), gb[p]);
+    }
+    for (int i = 0; i < cnt; i += MQ_DEPTH) {
+#pragma unroll
+        for (int p = 0; p < MQ_DEPTH; ++p) {
+            const int ln = min(i + p + MQ_DEPTH - 1, cnt - 1);
+            load(ln, gidx(ln), gb[(p + MQ_DEPTH - 1) % MQ_DEPTH]);
+            if (i + p < cnt) compute(gb[p]);
+        }
     }
 #pragma unroll
     for (int t = 0; t < MQ_TILES; ++t)
@@ -750,16 +786,16 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     }
 }
 
-template <bool TER, bool SK>
+template <bool TER, bool SK, bool SL>
 __global__ __launch_bounds__(64 * MQ_MAXW) void gemv_mq_kernel(MqArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    mq_core<TER, SK>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return x + (size_t)b * K; },
+    mq_core<TER, SK, SL>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return x + (size_t)b * K; },
                  [=](int b) { return y + (size_t)b * M; });
 }
 
-template <bool TER>
+template <bool TER, bool SL>
 __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
     __shared__ int g[6][kFusedPairs];
     __shared__ int4 gjob;
@@ -785,7 +821,7 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
     float* y = a.y;
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)M * K / (TER ? 4 : 2), per_scales = (size_t)M * (K / 128);
-    mq_core<TER, false>(
+    mq_core<TER, false, SL>(
         a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * MQ_ROWS, nb,
         [=](int b) {
             const int p = pids[b];
@@ -981,7 +1017,11 @@ mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float*
         m.tile_base = static_cast<const uint32_t*>(w->sec[3]);
         m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
         const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
-        hipLaunchKernelGGL((gemv_mq_kernel<true, true>), dim3(blocks), dim3(64 * nw_mq), 0, st, m);
+        const size_t sl = size_t(ngroups) * MQ_ROWS * 2;
+        if (sl <= size_t(MQ_SCALE_LDS))
+            hipLaunchKernelGGL((gemv_mq_kernel<true, true, true>), dim3(blocks), dim3(64 * nw_mq), sl, st, m);
+        else
+            hipLaunchKernelGGL((gemv_mq_kernel<true, true, false>), dim3(blocks), dim3(64 * nw_mq), 0, st, m);
         return hip_check("batched gemv launch");
     }
     for (int b0 = 0; b0 < B; b0 += 4) {
@@ -1036,8 +1076,12 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
         const int nw = mq_waves(w->K);
         const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
-        if (ter) hipLaunchKernelGGL((gemv_mq_kernel<true, false>), dim3(blocks), dim3(64 * nw), 0, st, m);
-        else hipLaunchKernelGGL((gemv_mq_kernel<false, false>), dim3(blocks), dim3(64 * nw), 0, st, m);
+        const size_t sl = size_t(w->K / 128) * MQ_ROWS * 2;
+        const bool sll = sl <= size_t(MQ_SCALE_LDS);
+        if (ter && sll) hipLaunchKernelGGL((gemv_mq_kernel<true, false, true>), dim3(blocks), dim3(64 * nw), sl, st, m);
+        else if (ter) hipLaunchKernelGGL((gemv_mq_kernel<true, false, false>), dim3(blocks), dim3(64 * nw), 0, st, m);
+        else if (sll) hipLaunchKernelGGL((gemv_mq_kernel<false, false, true>), dim3(blocks), dim3(64 * nw), sl, st, m);
+        else hipLaunchKernelGGL((gemv_mq_kernel<false, false, false>), dim3(blocks), dim3(64 * nw), 0, st, m);
         return hip_check("batched gemv launch");
     }
     const int tiles = int((w->M + 15) / 16);
@@ -1161,12 +1205,16 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
     m.row_blocks = int((w->M + MQ_ROWS - 1) / MQ_ROWS);
     const int nw = mq_waves(w->K);
+    const size_t sl = size_t(w->K / 128) * MQ_ROWS * 2;
+    const bool sll = sl <= size_t(MQ_SCALE_LDS);
     const int64_t grid = max_jobs * m.row_blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
     if (ter)
-        hipLaunchKernelGGL(moe_mq_kernel<true>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
+        if (sll) hipLaunchKernelGGL((moe_mq_kernel<true, true>), dim3(unsigned(grid)), dim3(64 * nw), sl, st, m);
+        else hipLaunchKernelGGL((moe_mq_kernel<true, false>), dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
     else
-        hipLaunchKernelGGL(moe_mq_kernel<false>, dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
+        if (sll) hipLaunchKernelGGL((moe_mq_kernel<false, true>), dim3(unsigned(grid)), dim3(64 * nw), sl, st, m);
+        else hipLaunchKernelGGL((moe_mq_kernel<false, false>), dim3(unsigned(grid)), dim3(64 * nw), 0, st, m);
     return hip_check("expert gemv launch");
 }
 
