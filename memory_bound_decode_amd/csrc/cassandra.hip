@@ -1374,6 +1374,154 @@ __global__ __launch_bounds__(1024) void mx_spec_gemv_kernel(MxSpecArgs a, const 
     }
 }
 
+// Kept-domain draft GEMV (K >= 4096, batch <= 2, activations in LDS): every lane
+// takes an even share of the tile's kept values (c = ceil(kept / 64) consecutive
+// ones), finds the first one's position with the bitmap cursor over the tile's
+// staged bitmap words, and walks on, so no lane idles while another walks a
+// dense stretch.  A tile meets at most two rows, so a lane keeps two sums.  A
+// tile's table entries, bitmap words and the lane's nibble, sign and exponent
+// words are loaded one tile ahead.
+struct MxKept {
+    uint32_t kp0, nk;           // the tile's first kept index and kept count
+    uint32_t first;             // the lane's first kept value, tile relative
+    int cnt;                    // its count
+    uint32_t b0, b1;            // bitmap words 2 lane, 2 lane + 1 of the tile
+    uint32_t q[9], sg[3], xe;   // as MxLane, from kept index kp0 + first
+};
+
+__device__ __forceinline__ void mx_kept_issue(const MxSpecArgs& a, int64_t t, MxKept& L) {
+    const int lane = lane_id();
+    L.kp0 = a.kprefix[t];
+    L.nk = a.kprefix[t + 1] - L.kp0;
+    int first, cnt;
+    lane_share(int(L.nk), 64, lane, first, cnt);
+    L.first = uint32_t(first);
+    L.cnt = cnt;
+    const int64_t nwords = (a.N + 31) >> 5, wi = t * (TILE / 32) + 2 * lane;
+    const uint32_t v0 = a.bitmap[min<int64_t>(wi, nwords - 1)], v1 = a.bitmap[min<int64_t>(wi + 1, nwords - 1)];
+    L.b0 = wi < nwords ? v0 : 0u;
+    L.b1 = wi + 1 < nwords ? v1 : 0u;
+    const uint32_t j0 = L.kp0 + L.first;                 // at most 63 values past the stream
+    const uint32_t* np = a.nib + (j0 >> 3);
+    const mx_u32x4_dw_t n0 = *reinterpret_cast<const mx_u32x4_dw_t*>(np);
+    const mx_u32x4_dw_t n1 = *reinterpret_cast<const mx_u32x4_dw_t*>(np + 4);
+    L.q[0] = n0.x; L.q[1] = n0.y; L.q[2] = n0.z; L.q[3] = n0.w;
+    L.q[4] = n1.x; L.q[5] = n1.y; L.q[6] = n1.z; L.q[7] = n1.w;
+    L.q[8] = np[8];
+    const uint32_t g = j0 >> 5;
+    L.sg[0] = a.sign[g]; L.sg[1] = a.sign[g + 1]; L.sg[2] = a.sign[g + 2];
+    L.xe = uint32_t(a.xexp[g]) | (uint32_t(a.xexp[g + 1]) << 8) | (uint32_t(a.xexp[g + 2]) << 16);
+}
+
+template <int BMAX>
+__global__ __launch_bounds__(1024) void mx_spec_gemv_kept_kernel(MxSpecArgs a, const uint16_t* __restrict__ x, int B,
+                                                                 float* __restrict__ y, int R) {
+    extern __shared__ __attribute__((aligned(16))) uint4 sm4[];
+    const int nw = blockDim.x >> 6, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = int(a.K);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(sm4);                     // [BMAX][K]
+    WaveArea* areas = reinterpret_cast<WaveArea*>(xs + BMAX * K);        // [nw]
+    float* red = reinterpret_cast<float*>(areas + nw);                   // [nw][R][BMAX]
+    for (int i = threadIdx.x; i < B * K / 8; i += blockDim.x)
+        reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    for (int i = threadIdx.x; i < nw * R * BMAX; i += blockDim.x) red[i] = 0.f;
+    __syncthreads();
+    const int64_t r0 = int64_t(blockIdx.x) * R, r1 = min<int64_t>(a.M, r0 + R);
+    const int64_t t_a = (r0 * K) / TILE, t_b = (r1 * K - 1) / TILE;
+    WaveArea& W = areas[wave];
+    float* wred = red + wave * R * BMAX;
+    const int64_t tw0 = t_a + wave;
+    const int ntiles = t_b >= tw0 ? int((t_b - tw0) / nw) + 1 : 0;
+    auto tile_of = [&](int i) { return tw0 + int64_t(min(i, ntiles - 1)) * nw; };
+
+    auto walk = [&](int64_t t, const MxKept& L) {
+        // stage the tile's bitmap words with exclusive prefix counts per word pair
+        W.bw[2 * lane] = L.b0;
+        W.bw[2 * lane + 1] = L.b1;
+        const int pc = __popc(L.b0) + __popc(L.b1);
+        W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+        wave_sync_lds();
+        const int64_t f0 = t * TILE;
+        const int tl = int(min<int64_t>(TILE, a.N - f0));
+        const int64_t row_a = f0 / K;
+        const int bnd = int(min<int64_t>(tl, (row_a + 1) * K - f0));   // first position of the next row
+        const int colbase = int(f0 - row_a * K);
+        float accA[BMAX], accB[BMAX];
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) accA[b] = accB[b] = 0.f;
+        if (L.cnt > 0) {
+            BitCursor<false> kc;
+            kc.start(W, int(L.first));
+            const uint32_t j0 = L.kp0 + L.first;
+            uint32_t q0 = L.q[0] >> (4 * (j0 & 7)), q1 = L.q[1], q2 = L.q[2], q3 = L.q[3], q4 = L.q[4],
+                     q5 = L.q[5], q6 = L.q[6], q7 = L.q[7], q8 = L.q[8];
+            uint32_t s0 = L.sg[0] >> (j0 & 31), s1 = L.sg[1], s2 = L.sg[2], xe = L.xe;
+            int ni = int(j0 & 7), si = int(j0 & 31);
+            float scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
+            for (int v = 0; v < L.cnt; ++v) {
+                const int pos = kc.next(W);
+                float w = float(q0 & 15u) * scale;               // exact: <= 4 significant bits
+                w = (s0 & 1u) ? -w : w;
+                const bool inA = pos < bnd;
+                const int col = colbase + pos - (inA ? 0 : K);
+#pragma unroll
+                for (int b = 0; b < BMAX; ++b) {
+                    if (b < B) {
+                        const float xv = __uint_as_float(uint32_t(xs[b * K + col]) << 16);
+                        const float pA = fmaf(w, xv, accA[b]), pB = fmaf(w, xv, accB[b]);
+                        accA[b] = inA ? pA : accA[b];
+                        accB[b] = inA ? accB[b] : pB;
+                    }
+                }
+                q0 >>= 4;
+                s0 >>= 1;
+                if (++ni == 8) {
+                    ni = 0;
+                    q0 = q1; q1 = q2; q2 = q3; q3 = q4; q4 = q5; q5 = q6; q6 = q7; q7 = q8;
+                }
+                if (++si == 32) {
+                    si = 0;
+                    s0 = s1; s1 = s2;
+                    xe >>= 8;
+                    scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < BMAX; ++b) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                accA[b] += __shfl_xor(accA[b], off, 64);
+                accB[b] += __shfl_xor(accB[b], off, 64);
+            }
+            if (lane == 0) {
+                if (row_a >= r0 && row_a < r1) wred[int(row_a - r0) * BMAX + b] += accA[b];
+                if (bnd < tl && row_a + 1 >= r0 && row_a + 1 < r1) wred[int(row_a + 1 - r0) * BMAX + b] += accB[b];
+            }
+        }
+        wave_sync_lds();                                 // the staged words are rewritten next tile
+    };
+
+    MxKept la, lb;
+    if (ntiles > 0) mx_kept_issue(a, tile_of(0), la);
+    for (int i = 0; i < ntiles; i += 2) {
+        mx_kept_issue(a, tile_of(i + 1), lb);
+        walk(tile_of(i), la);
+        mx_kept_issue(a, tile_of(i + 2), la);
+        if (i + 1 < ntiles) walk(tile_of(i + 1), lb);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * BMAX; i += blockDim.x) {
+        const int r = i / BMAX, b = i - r * BMAX;
+        if (b < B && r0 + r < r1) {
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += red[(w * R + r) * BMAX + b];
+            y[int64_t(b) * a.M + r0 + r] = sum;
+        }
+    }
+}
+
 }  // namespace cas
 }  // namespace mbd
 
@@ -1493,6 +1641,23 @@ mbd_status mx_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, flo
     if (!aligned(x, 16) || !aligned(y, 4)) return fail(MBD_EALIGN, "x must be 16-byte and y 4-byte aligned");
     if (a.M == 0) return MBD_OK;
     const int bmax = round_batch(B);
+    if (a.K >= TILE && bmax <= 2) {
+        // kept-domain walk: a tile meets at most two rows
+        constexpr int KW = 16, KR = 16;
+        const size_t kl = size_t(bmax) * a.K * 2 + KW * sizeof(WaveArea) + size_t(KW) * KR * bmax * 4;
+        if (kl <= 150 * 1024) {
+            static std::atomic<int> d1{0}, d2{0};
+            const void* kern = bmax == 1 ? reinterpret_cast<const void*>(mx_spec_gemv_kept_kernel<1>)
+                                         : reinterpret_cast<const void*>(mx_spec_gemv_kept_kernel<2>);
+            if ((s = lds_limit(kern, bmax == 1 ? d1 : d2, kl, "draft GEMV")) != MBD_OK) return s;
+            const unsigned blocks = unsigned((a.M + KR - 1) / KR);
+            if (bmax == 1)
+                hipLaunchKernelGGL(mx_spec_gemv_kept_kernel<1>, dim3(blocks), dim3(64 * KW), kl, st, a, x, B, y, KR);
+            else
+                hipLaunchKernelGGL(mx_spec_gemv_kept_kernel<2>, dim3(blocks), dim3(64 * KW), kl, st, a, x, B, y, KR);
+            return hip_check("spec GEMV launch");
+        }
+    }
     const bool xl = int64_t(bmax) * a.K * 2 <= 64 * 1024;
     int R = int(std::max<int64_t>(1, std::min<int64_t>(64, (32 * TILE) / a.K))), nw = 1;
     size_t lds = 0;
