@@ -270,8 +270,11 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
 constexpr int BN_REC = 80;
 
 // Groups one wave stages per round: at most 8, and at most 16 / NB so that the
-// staging jobs (16 per group and row) fit four passes of 64 lanes.
-constexpr int bn_max_groups(int NB) { return NB >= 4 ? 4 : 8; }
+// staging jobs (16 per group and row) fit four passes of 64 lanes.  INT4 with 4
+// rows takes 2: two staging passes keep it at <= 64 VGPRs, so two 16-wave blocks
+// share a CU (batch 4, 8192^2: 9.7 us against 11.0 us with 4 groups); ternary,
+// whose items are group pairs, keeps 4.
+constexpr int bn_max_groups(int NB, bool ter) { return NB >= 4 ? (ter ? 4 : 2) : 8; }
 constexpr int bn_group_lds(int NB) { return 4 * NB * BN_REC + 32; }
 
 struct BnArgs {
@@ -945,14 +948,14 @@ struct BnPlan {
 // Waves per 16-row tile and items per wave for NB activation rows.  Up to
 // MBD_B1_IPW items per wave, fewer while the call (tiles = 16-row tiles over all
 // its matrices and jobs) would have under about 8192 waves, more when a tile
-// would need over 16 waves; a wave stages at most bn_max_groups(NB) groups per
+// would need over 16 waves; a wave stages at most bn_max_groups(NB, ter) groups per
 // round.
 BnPlan plan_bn(bool ter, int64_t K, int64_t tiles, int NB) {
     BnPlan p{};
     p.nb_max = NB;
     const int64_t IG = ter ? 2 : 1;
     const int64_t ngroups = K / 128, n_items = ter ? (ngroups + 1) / 2 : ngroups;
-    const int64_t max_ipw = std::max<int64_t>(1, bn_max_groups(NB) / IG);
+    const int64_t max_ipw = std::max<int64_t>(1, bn_max_groups(NB, ter) / IG);
     const int64_t fill = (tiles * n_items + 8191) / 8192;      // items per wave for ~8192 waves
     int64_t ipw = std::max<int64_t>((n_items + 15) / 16, std::min<int64_t>(MBD_B1_IPW, fill));
     ipw = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ipw, max_ipw), n_items));
