@@ -553,11 +553,14 @@ constexpr int MQ_TILES = MBD_MQ_TILES;
 constexpr int MQ_ROWS = 16 * MQ_TILES;
 constexpr int MQ_MAXW = 16;
 #ifndef MBD_MQ_GPW
-#define MBD_MQ_GPW 4          // scale groups per wave (sets the waves per block)
+#define MBD_MQ_GPW 4          // expert jobs: scale groups per wave (sets the waves per block)
+#endif
+#ifndef MBD_MQ_GPW_GEMV
+#define MBD_MQ_GPW_GEMV 8     // plain GEMV: longer per-wave pipelines measured faster
 #endif
 
-inline int mq_waves(int64_t K) {
-    return int(std::max<int64_t>(1, std::min<int64_t>(MQ_MAXW, (K / 128) / MBD_MQ_GPW)));
+inline int mq_waves(int64_t K, int gpw) {
+    return int(std::max<int64_t>(1, std::min<int64_t>(MQ_MAXW, (K / 128) / gpw)));
 }
 
 struct MqGroup {
@@ -1011,7 +1014,7 @@ mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float*
     if (w->M == 0) return MBD_OK;
     const int tiles = int((w->M + 15) / 16);
     const int ngroups = int(w->K / 128);
-    const int nw_mq = mq_waves(w->K);
+    const int nw_mq = mq_waves(w->K, MBD_MQ_GPW_GEMV);
     if (B > 4 && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
@@ -1077,7 +1080,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
         m.scales = static_cast<const uint16_t*>(w->sec[1]);
         m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K); m.B = B;
-        const int nw = mq_waves(w->K);
+        const int nw = mq_waves(w->K, MBD_MQ_GPW_GEMV);
         const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
         const size_t sl = size_t(w->K / 128) * MQ_ROWS * 2;
         const bool sll = sl <= size_t(MQ_SCALE_LDS);
@@ -1207,7 +1210,7 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     m.route = fused ? route : nullptr;
     m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
     m.row_blocks = int((w->M + MQ_ROWS - 1) / MQ_ROWS);
-    const int nw = mq_waves(w->K);
+    const int nw = mq_waves(w->K, MBD_MQ_GPW);
     const size_t sl = size_t(w->K / 128) * MQ_ROWS * 2;
     const bool sll = sl <= size_t(MQ_SCALE_LDS);
     const int64_t grid = max_jobs * m.row_blocks;
