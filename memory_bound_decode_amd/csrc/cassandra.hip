@@ -1532,6 +1532,13 @@ using namespace mbd::cas;
 
 namespace {
 
+#ifndef MBD_SPEC_KW
+#define MBD_SPEC_KW 16        // kept-domain draft GEMV: waves per block
+#endif
+#ifndef MBD_SPEC_KR
+#define MBD_SPEC_KR 16        // kept-domain draft GEMV: rows per block
+#endif
+
 inline bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
 
 mbd_status hip_check(const char* what) {
@@ -1643,7 +1650,7 @@ mbd_status mx_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, flo
     const int bmax = round_batch(B);
     if (a.K >= TILE && bmax <= 2) {
         // kept-domain walk: a tile meets at most two rows
-        constexpr int KW = 16, KR = 16;
+        constexpr int KW = MBD_SPEC_KW, KR = MBD_SPEC_KR;
         const size_t kl = size_t(bmax) * a.K * 2 + KW * sizeof(WaveArea) + size_t(KW) * KR * bmax * 4;
         if (kl <= 150 * 1024) {
             static std::atomic<int> d1{0}, d2{0};
@@ -1749,7 +1756,7 @@ mbd_status mbd_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, fl
     const int bmax = round_batch(B);
     // kept-domain kernel: K >= 4096 (a tile meets at most two rows), batch <= 2,
     // activations staged in LDS
-    constexpr int KW = 16, KR = 16;
+    constexpr int KW = MBD_SPEC_KW, KR = MBD_SPEC_KR;
     const size_t kl = size_t(bmax) * a.K * 2 + KW * sizeof(WaveArea) + size_t(KW) * KR * bmax * 4 +
                       (size_t(std::max(1, a.n_sym)) * 16 + 1) * 4;
     if (a.K >= TILE && bmax <= 2 && kl <= 160 * 1024) {
