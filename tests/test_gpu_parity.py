@@ -516,3 +516,31 @@ def test_verify_gemm_needs_tile_aligned_k(dev):
     with pytest.raises(mbd.MbdError) as e:
         mbd.mbd_gemv(cw, x, y)
     assert e.value.status == mbd.MBD_ESHAPE
+
+
+# ------------------------------------------------------------ random shapes
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        K = 128 * int(rng.integers(1, 90))
+        B = int(rng.choice([1, 2, 3, 4, 5, 7, 9, 12, 16]))
+        out.append((M, K, B))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["ternary", "int4"])
+@pytest.mark.parametrize("M,K,B", _random_cases(12, 2026))
+def test_gemv_random_shapes(dev, kind, M, K, B):
+    """Seeded random (M, K, B): ragged last tiles, odd group counts, every batch
+    kernel, against the oracle."""
+    print("case random gemv", kind, M, K, B, flush=True)
+    w = _rand_w(M * 13 + K + B, M, K)
+    x = _rand_x(B * 7 + K, B, K)
+    dw = _mbd().to_device(_mbd().mbd_pack(_fmt(kind), w), dev)
+    q, s = QUANT[kind].quantize(w)
+    y = _run_gemv(dw, x, dev)
+    assert np.all(np.isfinite(y))
+    assert gemv.rel_l2(y, gemv.gemv(QUANT[kind].dequant(q, s), x)) <= TOL
