@@ -397,6 +397,7 @@ struct UnaryCursor {
     int k;          // current word
     uint32_t cw;    // its unconsumed bits
     int q;          // position of the last one bit consumed (window relative)
+    uint32_t nx;    // FAST: word k + 1, read one refill ahead
     __device__ __forceinline__ uint32_t word(const CasArgs& a, const TileHdr& h, const WaveArea& W, int i) const {
         if constexpr (FAST) return W.uw[i];
         else return unary_word(a, h, i);
@@ -425,10 +426,21 @@ struct UnaryCursor {
         k = kk;
         q = 32 * kk + b;
         cw = j0 > 0 ? w & ~((2u << b) - 1u) : w;
+        if constexpr (FAST) nx = W.uw[k + 1];
     }
     // rank of the next codeword
     __device__ __forceinline__ int next(const CasArgs& a, const TileHdr& h, const WaveArea& W) {
-        while (cw == 0) cw = word(a, h, W, ++k);
+        if constexpr (FAST) {
+            // branch-free refill from the word read ahead; a further empty word
+            // (a codeword longer than 32 bits) takes the loop
+            const bool e = cw == 0;
+            cw = e ? nx : cw;
+            k += e;
+            while (cw == 0) cw = word(a, h, W, ++k);
+            nx = W.uw[k + 1];
+        } else {
+            while (cw == 0) cw = word(a, h, W, ++k);
+        }
         const int pos = 32 * k + __builtin_ctz(cw);
         const int rank = pos - q - 1;
         q = pos;
@@ -443,6 +455,7 @@ template <bool ZEROS>
 struct BitCursor {
     int k;
     uint32_t cw;
+    uint32_t nx;    // word k + 1, read one refill ahead
     __device__ __forceinline__ uint32_t word(const WaveArea& W, int i) const {
         return ZEROS ? ~W.bw[i] : W.bw[i];
     }
@@ -464,9 +477,14 @@ struct BitCursor {
             w = word(W, k);
         }
         cw = w & (~0u << select32(w, r));
+        nx = word(W, k + 1);
     }
     __device__ __forceinline__ int next(const WaveArea& W) {
+        const bool e = cw == 0;              // branch-free refill; a further empty word loops
+        cw = e ? nx : cw;
+        k += e;
         while (cw == 0) cw = word(W, ++k);
+        nx = word(W, k + 1);
         const int pos = 32 * k + __builtin_ctz(cw);
         cw &= cw - 1u;
         return pos;
