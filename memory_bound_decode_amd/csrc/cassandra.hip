@@ -558,7 +558,8 @@ __device__ __forceinline__ void lane_share(int n, int lanes, int l, int& first, 
 }
 
 // Pruned values [p0, p0 + cnt) of the tile (raw bf16), PRU_CHUNK at a time:
-// emit(pos, value).  The first chunk's words come preloaded (pru_load at e0).
+// emit(pos, value).  The first chunk's words come preloaded (pru_load at e0);
+// each later chunk's are loaded while the one before is walked.
 constexpr int PRU_WORDS = PRU_CHUNK / 2 + 1;
 
 // 16 of the 17 words come in four 16-byte loads: global multi-dword loads need
@@ -583,15 +584,17 @@ __device__ __forceinline__ void walk_pruned(const CasArgs& a, const TileHdr& h, 
     BitCursor<true> zc;
     zc.start(W, p0);
     const int64_t e0 = (h.f0 - h.kp0) + p0;          // pruned stream index of the first value
+    uint32_t raw[PRU_WORDS], nxt[PRU_WORDS];
+#pragma unroll
+    for (int i = 0; i < PRU_WORDS; ++i) raw[i] = raw0[i];
     for (int base = 0; base < cnt; base += PRU_CHUNK) {
         const int64_t e = e0 + base;
-        uint32_t raw[PRU_WORDS];
-        if (base == 0) {
+        if (base > 0) {
 #pragma unroll
-            for (int i = 0; i < PRU_WORDS; ++i) raw[i] = raw0[i];
-        } else {
-            pru_load(a, e, raw);
+            for (int i = 0; i < PRU_WORDS; ++i) raw[i] = nxt[i];
         }
+        // the next chunk's words load while this one is walked
+        if (base + PRU_CHUNK < cnt) pru_load(a, e + PRU_CHUNK, nxt);
         const uint32_t sh = uint32_t(16 * (e & 1));
         uint32_t v[PRU_CHUNK / 2];
 #pragma unroll
