@@ -826,6 +826,29 @@ __device__ __forceinline__ void decode_tile_lds(const CasArgs& a, int64_t t, Wav
     }
 }
 
+// Restore of a tile whose header, bitmap and unary words and first spec nibble
+// window were loaded ahead by tile_issue (the verify GEMM issues the next tile's
+// loads before its MFMA phase).
+__device__ __forceinline__ void decode_tile_issued(const CasArgs& a, const TileWords& tw, WaveArea& W,
+                                                   const uint8_t* cb, uint16_t* d) {
+    const int lane = lane_id();
+    const TileHdr& h = tw.h;
+    int p0, pc;
+    lane_share(h.tl - h.nk, 64, lane, p0, pc);
+    uint32_t lraw[5], praw[PRU_WORDS];
+    nib_load(a.lo_nib, h.kp0 + tw.j0, lraw);
+    tile_stage(a, tw, W);
+    ScatterSink sk;
+    sk.W = &W;
+    sk.cb = cb;
+    sk.d = d;
+    if (tw.cnt > 0) sk.kc.start(W, tw.j0);
+    if (h.nuw <= STAGE_UW) walk_kept<true, true>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
+    else walk_kept<false, true>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
+    pru_load(a, (h.f0 - h.kp0) + p0, praw);
+    walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
+}
+
 // One wave per tile: kept values (and, when restoring, pruned values) are
 // scattered into the wave's LDS tile, which is then written out 16 bytes a lane.
 template <bool RESTORE>
@@ -992,6 +1015,10 @@ __global__ __launch_bounds__(64 * VG_WAVES) void verify_gemm_kernel(CasArgs a, c
     const int64_t r0 = int64_t(blockIdx.x) * 16, row = r0 + wave;
     const int n = lane & 15, kq = lane >> 4;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // the next tile's words load during this tile's MFMA phase
+    TileWords tw;
+    const bool live = row < a.M;                     // rows past M are not decoded
+    if (live) tile_issue(a, tile_hdr(a, row * tpr), row * tpr, tw);
     for (int64_t kt = 0; kt < tpr; ++kt) {
         // this wave's activations for its 8 k-steps, loaded ahead of the decode
         uint4 bv[8];
@@ -1002,7 +1029,11 @@ __global__ __launch_bounds__(64 * VG_WAVES) void verify_gemm_kernel(CasArgs a, c
             bv[s] = n < B ? *reinterpret_cast<const uint4*>(xrow + k) : make_uint4(0, 0, 0, 0);
         }
         // rows past M are not decoded: the outputs they feed are never stored
-        if (row < a.M) decode_tile_lds<true, false>(a, row * tpr + kt, areas[wave], cb, rows + wave * VROW);
+        if (live) {
+            decode_tile_issued(a, tw, areas[wave], cb, rows + wave * VROW);
+            const int64_t tn = row * tpr + min<int64_t>(kt + 1, tpr - 1);
+            tile_issue(a, tile_hdr(a, tn), tn, tw);
+        }
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
