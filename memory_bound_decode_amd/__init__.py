@@ -33,12 +33,13 @@ class Packed:
 
     def __init__(self, handle: ctypes.c_void_p, fmt: int, M: int, K: int, n_mats: int = 1):
         self._h = handle
+        self._free = lib().mbd_packed_free        # the library that allocated the handle frees it
         self.fmt, self.M, self.K, self.n_mats = fmt, M, K, n_mats
 
     def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib().mbd_packed_free(h)
+        h, free = getattr(self, "_h", None), getattr(self, "_free", None)
+        if h is not None and h.value and free is not None:
+            free(h)
             self._h = None
 
     def sections(self) -> dict:

@@ -917,7 +917,8 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
         const int64_t tn = tw0 + int64_t(i) * nw;
         tile_issue(a, i < 64 ? hdr_get(a, hv, i, tn) : tile_hdr(a, tn), tn, dst);
     };
-    auto process = [&](const TileWords& cur) {
+    // inlined: as a call, the tile buffers would pass through the stack
+    auto process = [&](const TileWords& cur) __attribute__((always_inline)) {
         const TileHdr h = cur.h;
         const int j0 = cur.j0, cnt = cur.cnt;
         tile_stage(a, cur, W);
