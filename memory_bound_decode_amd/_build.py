@@ -33,19 +33,27 @@ def _run(cmd):
         raise RuntimeError("build step failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
 
 
+def _run_all(cmds):
+    """Run the compile commands side by side; raise on the first that failed."""
+    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)) for c in cmds]
+    outs = [(c, p.communicate(), p.returncode) for c, p in procs]
+    for c, (out, err), rc in outs:
+        if rc != 0:
+            raise RuntimeError("build step failed: %s\n%s%s" % (" ".join(c), out, err))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source (always) and link libmbd.so; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
-    objs = []
-    for s in CXX_SOURCES:
-        o = os.path.join(OBJ, s + ".o")
-        _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
-        objs.append(o)
     hipcc = _hipcc()
+    cmds, objs = [], []
+    for s in CXX_SOURCES:
+        objs.append(os.path.join(OBJ, s + ".o"))
+        cmds.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", objs[-1]])
     for s in HIP_SOURCES:
-        o = os.path.join(OBJ, s + ".o")
-        _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
-        objs.append(o)
+        objs.append(os.path.join(OBJ, s + ".o"))
+        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", objs[-1]])
+    _run_all(cmds)
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
@@ -56,3 +64,34 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+
+
+def kernel_resources() -> dict:
+    """Per-kernel register, scratch and occupancy figures the compiler reports for
+    every HIP source (a device-only compile with the build's flags):
+    {mangled name: {"vgprs": n, "scratch": bytes per lane, "occupancy": waves per SIMD}}."""
+    import re
+    import tempfile
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory() as td:
+        cmds = [[hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-c", os.path.join(CSRC, s),
+                 "-o", os.path.join(td, s + ".o"), "-Rpass-analysis=kernel-resource-usage"] for s in HIP_SOURCES]
+        procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True) for c in cmds]
+        texts = []
+        for c, p in zip(cmds, procs):
+            out, err = p.communicate()
+            if p.returncode != 0:
+                raise RuntimeError("compile failed: %s\n%s" % (" ".join(c), err))
+            texts.append(err)
+    res, cur = {}, None
+    for line in "\n".join(texts).splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = res.setdefault(m.group(1), {})
+            continue
+        for key, pat in (("vgprs", r"\bVGPRs: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                         ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)")):
+            m = re.search(pat, line)
+            if m and cur is not None:
+                cur[key] = int(m.group(1))
+    return res
