@@ -234,7 +234,8 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
  * (x_per_pair = 1).  y fp32 [T][k][M]: y[t][j] = W[route[t][j]] @ x_row.  An
  * expert's weights are read once per group of up to 16 tokens routed to it.  At
  * most 4096 experts (MBD_ESHAPE beyond).  Ids outside [0, n_mats) leave their y
- * rows unwritten.  ws: device workspace of at least
+ * rows unwritten; an id repeated within a token is outside this contract (with at
+ * most 16 tokens, pairs past an expert's 16th may be left unwritten).  ws: device workspace of at least
  * mbd_moe_workspace_bytes(n_mats, T, k) bytes, 16-byte aligned, contents
  * overwritten.  Calls that share a workspace must not overlap. */
 mbd_status mbd_moe_workspace_bytes(int64_t n_mats, int32_t T, int32_t k, uint64_t* bytes);

@@ -118,6 +118,10 @@ __device__ __forceinline__ float dpp_quad_sum(float v) {
 // moe_group_kernel.
 constexpr int kFusedPairs = 32;
 constexpr int kSortPairs = 256;
+// Routes of at most 16 tokens and kExpertPairs pairs over few enough experts run
+// one block row per expert, each block listing its expert's pairs itself (no
+// grouping at all).
+constexpr int kExpertPairs = 256;
 
 // Workgroup-wide grouping.  Pairs are ordered by (expert, pair id): a pair's rank
 // is the number of pairs with a smaller expert plus the number of earlier pairs
@@ -602,6 +606,7 @@ struct MqArgs {
     const int* pair_ids;
     const int* route;       // grouped in the kernel when set (at most kFusedPairs pairs)
     int n_pairs, n_experts, topk, x_per_pair, row_blocks, B;
+    int by_expert;          // block index = expert * row_blocks + row block (route set)
 };
 
 // A operand of MFMA step s from the lane's codes of one group, every pair shifted
@@ -822,30 +827,58 @@ template <bool TER, bool SL>
 __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
     __shared__ int g[6][kFusedPairs];
     __shared__ int4 gjob;
-    const int job = blockIdx.x / a.row_blocks, rb = blockIdx.x - job * a.row_blocks;
-    int4 jd;
+    __shared__ int plist[kExpertPairs];
+    int e, rb, cnt;
     const int* pids;
-    if (a.route) {
-        if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
-        moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, 16, g);
-        for (int qq = threadIdx.x; qq < a.n_pairs; qq += blockDim.x)
-            if (g[4][qq] >= 0 && g[1][qq] == job) gjob = make_int4(g[4][qq] >> 5, qq, g[4][qq] & 31, 0);
+    if (a.by_expert) {
+        // One expert per block row: wave 0 lists the expert's pairs in ascending
+        // order with ballots over the route (no grouping pass); a block with no
+        // pair exits.  The launcher takes this mode for at most 16 tokens, so an
+        // expert meets at most 16 pairs when each token's ids are distinct.
+        e = blockIdx.x / a.row_blocks;
+        rb = blockIdx.x - e * a.row_blocks;
+        if (threadIdx.x < 64) {
+            int c = 0;
+            for (int p0 = 0; p0 < a.n_pairs; p0 += 64) {
+                const int p = p0 + int(threadIdx.x);
+                const bool hit = p < a.n_pairs && a.route[p] == e;
+                const unsigned long long m = __ballot(hit);
+                if (hit) plist[c + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0)))] = p;
+                c += __popcll(m);
+            }
+            if (threadIdx.x == 0) gjob = make_int4(c, 0, 0, 0);
+        }
         __syncthreads();
-        jd = gjob;
-        if (jd.x < 0) return;
-        pids = g[5] + jd.y;
+        cnt = gjob.x;
+        pids = plist;
     } else {
-        if (job >= *a.n_jobs) return;
-        jd = a.jobs[job];
-        pids = a.pair_ids + jd.y;
+        const int job = blockIdx.x / a.row_blocks;
+        rb = blockIdx.x - job * a.row_blocks;
+        int4 jd;
+        if (a.route) {
+            if (threadIdx.x == 0) gjob = make_int4(-1, 0, 0, 0);
+            moe_sort_block<kFusedPairs>(a.route, a.n_pairs, a.n_experts, 16, g);
+            for (int qq = threadIdx.x; qq < a.n_pairs; qq += blockDim.x)
+                if (g[4][qq] >= 0 && g[1][qq] == job) gjob = make_int4(g[4][qq] >> 5, qq, g[4][qq] & 31, 0);
+            __syncthreads();
+            jd = gjob;
+            if (jd.x < 0) return;
+            pids = g[5] + jd.y;
+        } else {
+            if (job >= *a.n_jobs) return;
+            jd = a.jobs[job];
+            pids = a.pair_ids + jd.y;
+        }
+        e = jd.x;
+        cnt = jd.z;
     }
-    const int e = jd.x, nb = jd.z;
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)M * K / (TER ? 4 : 2), per_scales = (size_t)M * (K / 128);
+    if (cnt == 0) return;
     mq_core<TER, false, SL, true>(
-        a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * MQ_ROWS, nb,
+        a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * MQ_ROWS, min(16, cnt),
         [=](int b) {
             const int p = pids[b];
             return x + (size_t)(xpp ? p : p / topk) * K;
@@ -1209,11 +1242,14 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     constexpr int bmax = 16;
     // sum over experts of ceil(pairs / bmax) <= D + (P - D) / bmax, D = distinct experts
     const int64_t D = std::min<int64_t>(E, P), max_jobs = D + (P - D) / bmax;
-    const bool fused = P <= kFusedPairs;
+    // few experts against the route: a block row per expert (blocks of experts no
+    // pair routes to exit at once); else jobs grouped in the kernel or beforehand
+    const bool by_expert = T <= 16 && P <= kExpertPairs && E <= 2 * P + 64;
+    const bool fused = !by_expert && P <= kFusedPairs;
     int* n_jobs = static_cast<int*>(ws);
     int* pair_ids = n_jobs + 4;
     int4* jobs = reinterpret_cast<int4*>(pair_ids + ((P * 4 + 15) / 16) * 4);
-    if (!fused) {
+    if (!fused && !by_expert) {
         if (P <= kSortPairs)
             hipLaunchKernelGGL(moe_group_sort_kernel, dim3(1), dim3(1024), 0, st, route, P, E, bmax, pair_ids, jobs, n_jobs);
         else
@@ -1225,7 +1261,8 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     m.scales = static_cast<const uint16_t*>(w->sec[1]);
     m.x = x; m.y = y; m.M = int(w->M); m.K = int(w->K);
     m.jobs = jobs; m.n_jobs = n_jobs; m.pair_ids = pair_ids;
-    m.route = fused ? route : nullptr;
+    m.route = (fused || by_expert) ? route : nullptr;
+    m.by_expert = by_expert ? 1 : 0;
     m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
     m.row_blocks = int((w->M + MQ_ROWS - 1) / MQ_ROWS);
     const int nw = mq_waves(w->K, MBD_MQ_GPW);
@@ -1233,7 +1270,7 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
     // 64 KiB a launch gets without raising the kernel's limit, with its static part)
     const bool sll = mq_lds_bytes(nw, int(w->K / 128), true) <= size_t(60 * 1024);
     const size_t lds = mq_lds_bytes(nw, int(w->K / 128), sll);
-    const int64_t grid = max_jobs * m.row_blocks;
+    const int64_t grid = (by_expert ? int64_t(E) : max_jobs) * m.row_blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
     if (ter)
         if (sll) hipLaunchKernelGGL((moe_mq_kernel<true, true>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);

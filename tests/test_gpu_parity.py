@@ -239,8 +239,9 @@ def test_moe_full(dev, T, which):
 
 
 MOE_CASES = [
-    # (format, experts, M, K, T, k, x_per_pair): fused in-kernel grouping for T*k <= 256,
-    # the separate grouping kernel above; few experts => several jobs per expert
+    # (format, experts, M, K, T, k, x_per_pair): a block row per expert while T*k <= 256
+    # over few experts (several jobs per expert when more than 16 pairs meet one);
+    # the grouping kernels above 256 pairs or with many experts
     ("ternary", 16, 72, 384, 3, 4, False),
     ("int4", 16, 40, 640, 5, 3, True),
     ("ternary", 4, 24, 1536, 13, 3, False),
@@ -250,6 +251,10 @@ MOE_CASES = [
     ("ternary", 3, 64, 128, 100, 3, False),
     # long rows: 16 waves' partial tiles leave no room for the staged scales
     ("int4", 2, 40, 61440, 3, 2, False),
+    # many experts against the route: jobs grouped inside the kernel (8 pairs) and
+    # by the one-workgroup grouping kernel (160 pairs)
+    ("ternary", 200, 24, 256, 2, 4, False),
+    ("int4", 400, 24, 128, 20, 8, True),
 ]
 
 
