@@ -557,7 +557,7 @@ constexpr int MQ_TILES = MBD_MQ_TILES;
 constexpr int MQ_ROWS = 16 * MQ_TILES;
 constexpr int MQ_MAXW = 16;
 #ifndef MBD_MQ_GPW
-#define MBD_MQ_GPW 4          // expert jobs: scale groups per wave (sets the waves per block)
+#define MBD_MQ_GPW 8          // expert jobs: scale groups per wave (sets the waves per block; 4, 6, 12 and 16 measured slower)
 #endif
 #ifndef MBD_MQ_GPW_GEMV
 #define MBD_MQ_GPW_GEMV 8     // plain GEMV: longer per-wave pipelines measured faster
@@ -580,9 +580,9 @@ constexpr int MQ_SCALE_LDS = 32 * 1024;
 
 // Dynamic LDS of a block: the staged scales when SL, then, for expert jobs, the
 // waves' partial tiles sized to the block's nw waves (a short expert matrix runs
-// 3 waves, and a 16-wave array would cap the blocks a CU holds).  The plain GEMV
-// keeps a static 16-wave array: with it the compiler schedules the INT4 group
-// loads ahead of the MFMAs, measured 8% faster at 8192 x 8192, batch 8.
+// one or a few waves, and a 16-wave array would cap the blocks a CU holds).  The
+// plain GEMV keeps a static 16-wave array: with it the compiler schedules the
+// INT4 group loads ahead of the MFMAs, measured 8% faster at 8192 x 8192, batch 8.
 inline size_t mq_scale_lds(int ngroups, bool sl) { return sl ? size_t(ngroups) * MQ_ROWS * 2 : 0; }
 inline size_t mq_lds_bytes(int nw, int ngroups, bool sl) {
     return mq_scale_lds(ngroups, sl) + size_t(nw) * MQ_TILES * 64 * 4 * sizeof(float);
