@@ -1652,9 +1652,9 @@ mbd_status decode_dense(const mbd_dweights* w, uint16_t* out, hipStream_t st, bo
     if (a.N == 0) return MBD_OK;
     const unsigned blocks = unsigned((a.T + DD_WAVES - 1) / DD_WAVES);
     if (restore)
-        hipLaunchKernelGGL(decode_dense_kernel<true>, dim3(blocks), dim3(256), 0, st, a, out);
+        hipLaunchKernelGGL(decode_dense_kernel<true>, dim3(blocks), dim3(64 * DD_WAVES), 0, st, a, out);
     else
-        hipLaunchKernelGGL(decode_dense_kernel<false>, dim3(blocks), dim3(256), 0, st, a, out);
+        hipLaunchKernelGGL(decode_dense_kernel<false>, dim3(blocks), dim3(64 * DD_WAVES), 0, st, a, out);
     return hip_check(restore ? "restore launch" : "spec decode launch");
 }
 
