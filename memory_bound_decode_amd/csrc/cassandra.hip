@@ -849,8 +849,9 @@ __device__ __forceinline__ void decode_tile_issued(const CasArgs& a, const TileW
     walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
 }
 
-// One wave per tile: kept values (and, when restoring, pruned values) are
-// scattered into the wave's LDS tile, which is then written out 16 bytes a lane.
+// Kept values (and, when restoring, pruned values) of a tile are scattered into
+// the wave's LDS tile, then written out 16 bytes a lane: a wave restores two
+// tiles, or draft-decodes one.
 template <bool RESTORE>
 __global__ __launch_bounds__(64 * DD_WAVES) void decode_dense_kernel(CasArgs a, uint16_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint16_t dense[DD_WAVES][TILE];
@@ -859,19 +860,39 @@ __global__ __launch_bounds__(64 * DD_WAVES) void decode_dense_kernel(CasArgs a, 
     for (int i = threadIdx.x; i < 256; i += blockDim.x) cb[i] = i < a.n_sym ? a.codebook[i] : 0;
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = lane_id();
-    const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * DD_WAVES + wave);
-    if (t >= a.T) return;
     uint16_t* d = dense[wave];
-    if constexpr (!RESTORE) {
+    auto write_out = [&](int64_t t) {
+        wave_sync_lds();
+        const int tl = int(min<int64_t>(TILE, a.N - t * TILE));
+        uint4* o = reinterpret_cast<uint4*>(out + t * TILE);
+        for (int g = lane; g < tl / 8; g += 64) o[g] = *reinterpret_cast<const uint4*>(d + 8 * g);
+    };
+    if constexpr (RESTORE) {
+        // two tiles per wave, DD_WAVES apart: both tiles' header, bitmap, unary and
+        // first nibble words are issued up front, so the second tile's arrive while
+        // the first is decoded (more tiles per wave measured slower)
+        const int64_t t0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 2 * DD_WAVES + wave);
+        const int64_t t1 = t0 + DD_WAVES;
+        if (t0 >= a.T) return;
+        TileWords w0, w1;
+        tile_issue(a, tile_hdr(a, t0), t0, w0);
+        const int64_t t1c = min<int64_t>(t1, a.T - 1);
+        tile_issue(a, tile_hdr(a, t1c), t1c, w1);
+        decode_tile_issued(a, w0, areas[wave], cb, d);
+        write_out(t0);
+        if (t1 >= a.T) return;
+        wave_sync_lds();                                    // the tile is read out before it is overwritten
+        decode_tile_issued(a, w1, areas[wave], cb, d);
+        write_out(t1);
+    } else {
+        const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * DD_WAVES + wave);
+        if (t >= a.T) return;
         uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
 #pragma unroll
         for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+        decode_tile_lds<false>(a, t, areas[wave], cb, d);
+        write_out(t);
     }
-    decode_tile_lds<RESTORE>(a, t, areas[wave], cb, d);
-    wave_sync_lds();
-    const int tl = int(min<int64_t>(TILE, a.N - t * TILE));
-    uint4* o = reinterpret_cast<uint4*>(out + t * TILE);
-    for (int g = lane; g < tl / 8; g += 64) o[g] = *reinterpret_cast<const uint4*>(d + 8 * g);
 }
 
 // ------------------------------------------------------------------ draft GEMV (kept domain)
@@ -1650,7 +1671,8 @@ mbd_status decode_dense(const mbd_dweights* w, uint16_t* out, hipStream_t st, bo
     if (!out) return fail(MBD_EINVAL, "output is NULL");
     if (!aligned(out, 16)) return fail(MBD_EALIGN, "output must be 16-byte aligned");
     if (a.N == 0) return MBD_OK;
-    const unsigned blocks = unsigned((a.T + DD_WAVES - 1) / DD_WAVES);
+    const int per_block = restore ? 2 * DD_WAVES : DD_WAVES;           // tiles per block
+    const unsigned blocks = unsigned((a.T + per_block - 1) / per_block);
     if (restore)
         hipLaunchKernelGGL(decode_dense_kernel<true>, dim3(blocks), dim3(64 * DD_WAVES), 0, st, a, out);
     else
