@@ -176,20 +176,22 @@ class CassandraWl(Workload):
         import torch
         import memory_bound_decode_amd as mbd
         import synth
-        wl = synth.WORKLOADS["cassandra_spec" if mode in ("spec", "spec_mx") else "cassandra_verify"]
+        draft = mode in ("spec", "spec_mx", "decode", "decode_mx")
+        wl = synth.WORKLOADS["cassandra_spec" if draft else "cassandra_verify"]
         self.mode, self.M, self.K = mode, wl.M, wl.K
         self.w = synth.gen_weights(wl)
         norms = synth.gen_act_norms(wl)
-        self.fmt_name = {"mx": "mx32", "spec_mx": "cassandra2_mx32_spec"}.get(mode, "cassandra")
+        self.fmt_name = {"mx": "mx32", "spec_mx": "cassandra2_mx32_spec", "decode_mx": "cassandra2_mx32_spec"}.get(
+            mode, "cassandra")
         if mode == "mx":
             p = mbd.mbd_pack(mbd.MBD_MX32, self.w)
             used = list(p.sections().keys())
-        elif mode == "spec_mx":
+        elif mode in ("spec_mx", "decode_mx"):
             p = mbd.mbd_pack(mbd.MBD_CASSANDRA_MX, self.w, norms)
             used = list(p.sections().keys())
         else:
             p = mbd.mbd_pack(mbd.MBD_CASSANDRA, self.w, norms)
-            used = list(mbd.SPEC_SECTIONS) if mode == "spec" else list(mbd.SECTION_NAMES[mbd.MBD_CASSANDRA])
+            used = list(mbd.SPEC_SECTIONS) if mode in ("spec", "decode") else list(mbd.SECTION_NAMES[mbd.MBD_CASSANDRA])
         st = p.stats()
         self.stats = {"spec_bpw": round(st.spec_bpw, 4), "bpw": round(st.bpw, 4),
                       "exp_entropy_bits": round(st.exp_entropy_bits, 4), "unary_avg_bits": round(st.unary_avg_bits, 4),
@@ -198,12 +200,14 @@ class CassandraWl(Workload):
         self.weight_bytes = sum(secs[k][1] for k in used)
         self.n = _pool_copies(self.weight_bytes)
         self.copies = [mbd.to_device(p, dev, only=used) for _ in range(self.n)]
-        self.B = {"spec": 1, "spec_mx": 1, "restore": 0, "verify": 16, "mx": 16}[mode]
+        self.B = {"spec": 1, "spec_mx": 1, "restore": 0, "decode": 0, "decode_mx": 0, "verify": 16, "mx": 16}[mode]
         self.name = {"spec": "cassandra_spec_gemv_4096x14336_b1", "restore": "cassandra_restore_8192x28672",
                      "verify": "cassandra_verify_gemm_8192x28672_b16", "mx": "mx32_gemm_8192x28672_b16",
-                     "spec_mx": "cassandra2_mx_spec_gemv_4096x14336_b1"}[mode]
+                     "spec_mx": "cassandra2_mx_spec_gemv_4096x14336_b1",
+                     "decode": "cassandra_spec_decode_4096x14336", "decode_mx": "cassandra2_mx_spec_decode_4096x14336"}[mode]
         self.kernel = {"spec": "spec_gemv_kernel", "restore": "decode_dense_kernel", "verify": "verify_gemm_kernel",
-                       "mx": "mx_gemm_kernel", "spec_mx": "mx_spec_gemv_kernel"}[mode]
+                       "mx": "mx_gemm_kernel", "spec_mx": "mx_spec_gemv_kernel", "decode": "decode_dense_kernel",
+                       "decode_mx": "mx_spec_decode_kernel"}[mode]
         if self.B:
             self.xt = _x_dev(synth.gen_x(wl, self.B), dev)
             self.y = torch.empty((self.B, self.M), dtype=torch.float32, device=dev)
@@ -212,7 +216,7 @@ class CassandraWl(Workload):
         self.mbd = mbd
 
     def bytes_per_step(self):
-        if self.mode == "restore":
+        if self.B == 0:                                  # restore / draft decode: sections read, bf16 written
             return self.weight_bytes + self.M * self.K * 2
         return self.weight_bytes + self.B * self.K * 2 + self.B * self.M * 4
 
@@ -222,6 +226,8 @@ class CassandraWl(Workload):
             m.mbd_spec_gemv(c, self.xt, self.y)
         elif self.mode == "restore":
             m.mbd_verify_restore(c, self.out)
+        elif self.mode in ("decode", "decode_mx"):
+            m.mbd_spec_decode(c, self.out)
         else:
             m.mbd_gemv(c, self.xt, self.y)
 
@@ -366,15 +372,18 @@ def make_workload(name, dev):
         return CassandraStep(dev)
     if name == "cassandra_encode":
         return CassandraEncode(dev)
-    if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_spec_mx"):
+    if name in ("cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_spec_mx",
+                "cassandra_decode", "cassandra_decode_mx"):
         return CassandraWl({"cassandra_spec": "spec", "cassandra_restore": "restore", "cassandra_spec_mx": "spec_mx",
-                            "cassandra_verify": "verify", "mx_verify": "mx"}[name], dev)
+                            "cassandra_verify": "verify", "mx_verify": "mx", "cassandra_decode": "decode",
+                            "cassandra_decode_mx": "decode_mx"}[name], dev)
     raise SystemExit("unknown workload %s" % name)
 
 
 ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4_4096x14336", "int4_14336x4096", "int4_8192x28672",
        "ternary_4096x14336", "ternary_14336x4096", "ternary_8192x28672", "moe_t1", "moe_t8",
        "cassandra_spec", "cassandra_restore", "cassandra_verify", "mx_verify", "cassandra_step",
+       "cassandra_decode", "cassandra_decode_mx",
        "ternary_skip_8192x28672", "ternary_skip_4096x14336", "ternary_skip_8192x28672_b4",
        "ternary_skip_8192x28672_b8", "cassandra_spec_mx", "cassandra_encode"]
 

@@ -365,32 +365,6 @@ __device__ __forceinline__ int select32(uint32_t w, int r) {
     return pos;
 }
 
-// Stage the tile's bitmap (and, when it fits, its unary words) with prefix counts.
-__device__ __forceinline__ void stage_tile(const CasArgs& a, const TileHdr& h, int64_t t, WaveArea& W) {
-    const int lane = lane_id();
-    if (h.nuw <= STAGE_UW) {
-        const uint32_t u0 = lane < h.nuw ? unary_word(a, h, lane) : 0u;
-        const uint32_t u1 = lane + 64 < h.nuw ? unary_word(a, h, lane + 64) : 0u;
-        // both counts in one scan: each prefix stays below 2^11
-        const int c0 = __popc(u0), c1 = __popc(u1);
-        const int inc = wave_incl_add(c0 | (c1 << 16));
-        const int tot0 = __shfl(inc, 63, 64) & 0xFFFF;
-        W.uw[lane] = u0;
-        W.uw[lane + 64] = u1;
-        W.up[lane] = uint16_t((inc & 0xFFFF) - c0);
-        W.up[lane + 64] = uint16_t(tot0 + (inc >> 16) - c1);
-    }
-    const int64_t wi = t * (TILE / 32) + 2 * lane;
-    const int64_t nwords = (a.N + 31) >> 5;
-    const uint32_t b0 = wi < nwords ? a.bitmap[wi] : 0u;
-    const uint32_t b1 = wi + 1 < nwords ? a.bitmap[wi + 1] : 0u;
-    W.bw[2 * lane] = b0;
-    W.bw[2 * lane + 1] = b1;
-    const int pc = __popc(b0) + __popc(b1);
-    W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
-    wave_sync_lds();
-}
-
 // Cursor over the tile's unary codewords.
 template <bool FAST>
 struct UnaryCursor {
@@ -676,7 +650,8 @@ __device__ __forceinline__ void tile_issue(const CasArgs& a, const TileHdr& h, i
     tw.b1 = a.bitmap[min<int64_t>(wi + 1, nwords - 1)];
 }
 
-// stage_tile from words loaded by tile_issue.
+// Stage the tile's bitmap (and, when it fits, its unary words) with prefix
+// counts, from the words tile_issue loaded.
 __device__ __forceinline__ void tile_stage(const CasArgs& a, const TileWords& tw, WaveArea& W) {
     const int lane = lane_id();
     const TileHdr& h = tw.h;
@@ -795,63 +770,35 @@ struct DotSink {
 
 constexpr int DD_WAVES = 4;
 
-// Restore (RESTORE) or draft decode of tile t into the LDS tile d.
-// The tile's global loads are issued before any of them is waited on (the first
-// pruned chunk too when PRE_PRUNED; otherwise it is loaded when reached).
-template <bool RESTORE, bool PRE_PRUNED = true>
-__device__ __forceinline__ void decode_tile_lds(const CasArgs& a, int64_t t, WaveArea& W, const uint8_t* cb,
-                                                uint16_t* d) {
-    const int lane = lane_id();
-    const TileHdr h = tile_hdr(a, t);
-    int j0, cnt, p0 = 0, pc = 0;
-    lane_share(h.nk, 64, lane, j0, cnt);
-    uint32_t sraw[5], lraw[5], praw[PRU_WORDS];
-    nib_load(a.spec_nib, h.kp0 + j0, sraw);
-    if constexpr (RESTORE) {
-        nib_load(a.lo_nib, h.kp0 + j0, lraw);
-        lane_share(h.tl - h.nk, 64, lane, p0, pc);
-        if constexpr (PRE_PRUNED) pru_load(a, (h.f0 - h.kp0) + p0, praw);
-    }
-    stage_tile(a, h, t, W);
-    ScatterSink sk;
-    sk.W = &W;
-    sk.cb = cb;
-    sk.d = d;
-    if (cnt > 0) sk.kc.start(W, j0);
-    if (h.nuw <= STAGE_UW) walk_kept<true, RESTORE>(a, h, W, j0, cnt, sraw, lraw, sk);
-    else walk_kept<false, RESTORE>(a, h, W, j0, cnt, sraw, lraw, sk);
-    if constexpr (RESTORE) {
-        if constexpr (!PRE_PRUNED) pru_load(a, (h.f0 - h.kp0) + p0, praw);
-        walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
-    }
-}
-
-// Restore of a tile whose header, bitmap and unary words and first spec nibble
-// window were loaded ahead by tile_issue (the verify GEMM issues the next tile's
-// loads before its MFMA phase).
+// Restore (RESTORE) or draft decode of a tile whose header, bitmap and unary
+// words and first spec nibble window were loaded ahead by tile_issue (the verify
+// GEMM issues the next tile's loads before its MFMA phase).  The draft decode
+// scatters kept values only: pruned positions keep what the tile held.
+template <bool RESTORE = true>
 __device__ __forceinline__ void decode_tile_issued(const CasArgs& a, const TileWords& tw, WaveArea& W,
                                                    const uint8_t* cb, uint16_t* d) {
-    const int lane = lane_id();
     const TileHdr& h = tw.h;
-    int p0, pc;
-    lane_share(h.tl - h.nk, 64, lane, p0, pc);
-    uint32_t lraw[5], praw[PRU_WORDS];
-    nib_load(a.lo_nib, h.kp0 + tw.j0, lraw);
+    uint32_t lraw[5];
+    if constexpr (RESTORE) nib_load(a.lo_nib, h.kp0 + tw.j0, lraw);
     tile_stage(a, tw, W);
     ScatterSink sk;
     sk.W = &W;
     sk.cb = cb;
     sk.d = d;
     if (tw.cnt > 0) sk.kc.start(W, tw.j0);
-    if (h.nuw <= STAGE_UW) walk_kept<true, true>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
-    else walk_kept<false, true>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
-    pru_load(a, (h.f0 - h.kp0) + p0, praw);
-    walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
+    if (h.nuw <= STAGE_UW) walk_kept<true, RESTORE>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
+    else walk_kept<false, RESTORE>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
+    if constexpr (RESTORE) {
+        int p0, pc;
+        lane_share(h.tl - h.nk, 64, lane_id(), p0, pc);
+        uint32_t praw[PRU_WORDS];
+        pru_load(a, (h.f0 - h.kp0) + p0, praw);
+        walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
+    }
 }
 
 // Kept values (and, when restoring, pruned values) of a tile are scattered into
-// the wave's LDS tile, then written out 16 bytes a lane: a wave restores two
-// tiles, or draft-decodes one.
+// the wave's LDS tile, then written out 16 bytes a lane; a wave takes two tiles.
 template <bool RESTORE>
 __global__ __launch_bounds__(64 * DD_WAVES) void decode_dense_kernel(CasArgs a, uint16_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint16_t dense[DD_WAVES][TILE];
@@ -867,32 +814,31 @@ __global__ __launch_bounds__(64 * DD_WAVES) void decode_dense_kernel(CasArgs a, 
         uint4* o = reinterpret_cast<uint4*>(out + t * TILE);
         for (int g = lane; g < tl / 8; g += 64) o[g] = *reinterpret_cast<const uint4*>(d + 8 * g);
     };
-    if constexpr (RESTORE) {
-        // two tiles per wave, DD_WAVES apart: both tiles' header, bitmap, unary and
-        // first nibble words are issued up front, so the second tile's arrive while
-        // the first is decoded (more tiles per wave measured slower)
-        const int64_t t0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 2 * DD_WAVES + wave);
-        const int64_t t1 = t0 + DD_WAVES;
-        if (t0 >= a.T) return;
-        TileWords w0, w1;
-        tile_issue(a, tile_hdr(a, t0), t0, w0);
-        const int64_t t1c = min<int64_t>(t1, a.T - 1);
-        tile_issue(a, tile_hdr(a, t1c), t1c, w1);
-        decode_tile_issued(a, w0, areas[wave], cb, d);
-        write_out(t0);
-        if (t1 >= a.T) return;
-        wave_sync_lds();                                    // the tile is read out before it is overwritten
-        decode_tile_issued(a, w1, areas[wave], cb, d);
-        write_out(t1);
-    } else {
-        const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * DD_WAVES + wave);
-        if (t >= a.T) return;
-        uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
+    // two tiles per wave, DD_WAVES apart: both tiles' header, bitmap, unary and
+    // first nibble words are issued up front, so the second tile's arrive while
+    // the first is decoded (more tiles per wave measured slower)
+    auto clear = [&]() {
+        if constexpr (!RESTORE) {
+            uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
-        decode_tile_lds<false>(a, t, areas[wave], cb, d);
-        write_out(t);
-    }
+            for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+        }
+    };
+    const int64_t t0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 2 * DD_WAVES + wave);
+    const int64_t t1 = t0 + DD_WAVES;
+    if (t0 >= a.T) return;
+    TileWords w0, w1;
+    tile_issue(a, tile_hdr(a, t0), t0, w0);
+    const int64_t t1c = min<int64_t>(t1, a.T - 1);
+    tile_issue(a, tile_hdr(a, t1c), t1c, w1);
+    clear();
+    decode_tile_issued<RESTORE>(a, w0, areas[wave], cb, d);
+    write_out(t0);
+    if (t1 >= a.T) return;
+    wave_sync_lds();                                        // the tile is read out before it is overwritten
+    clear();
+    decode_tile_issued<RESTORE>(a, w1, areas[wave], cb, d);
+    write_out(t1);
 }
 
 // ------------------------------------------------------------------ draft GEMV (kept domain)
@@ -1671,7 +1617,7 @@ mbd_status decode_dense(const mbd_dweights* w, uint16_t* out, hipStream_t st, bo
     if (!out) return fail(MBD_EINVAL, "output is NULL");
     if (!aligned(out, 16)) return fail(MBD_EALIGN, "output must be 16-byte aligned");
     if (a.N == 0) return MBD_OK;
-    const int per_block = restore ? 2 * DD_WAVES : DD_WAVES;           // tiles per block
+    const int per_block = 2 * DD_WAVES;                                 // tiles per block
     const unsigned blocks = unsigned((a.T + per_block - 1) / per_block);
     if (restore)
         hipLaunchKernelGGL(decode_dense_kernel<true>, dim3(blocks), dim3(64 * DD_WAVES), 0, st, a, out);
