@@ -1189,7 +1189,8 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(MxArgs a, float* __rest
 // a row since K % 128 == 0); a wave prefix sum of their popcounts gives its first
 // kept index, and it walks its set bits, reading kept values j, j + 1, ... with
 // the nibble word (8 values) and the group's sign word and exponent (32 values)
-// cached in registers.
+// cached in registers (the draft decode reads them from the tile's words staged
+// in LDS).
 
 struct MxSpecArgs {
     const uint32_t* bitmap;
@@ -1200,38 +1201,66 @@ struct MxSpecArgs {
     int64_t M, K, N, T;
 };
 
-struct MxCursor {
+// Draft weights, one wave per tile: a lane's 64 values go out as 8 16-byte stores.
+constexpr int MXD_WAVES = 4;
+constexpr int MXD_NIB = TILE / 8 + 8;     // nibble words a tile's kept values span (<= TILE / 8 + 1)
+constexpr int MXD_GRP = TILE / 32 + 4;    // MX groups a tile's kept values span (<= TILE / 32 + 1)
+
+// Draft value of kept value j from the tile's words staged in LDS (nibble word
+// nb + i at nib[i], group gb + i at sgn[i] / xe[i]); consecutive calls reuse the
+// cached words.
+struct MxLdsCursor {
+    const uint32_t* nib;
+    const uint32_t* sgn;
+    const uint8_t* xe;
+    uint32_t nb, gb;
     uint32_t nwi = 0xFFFFFFFFu, gi = 0xFFFFFFFFu, nw = 0, sw = 0;
     float scale = 0.f;
-    // draft value of kept value j (consecutive calls read cached words)
-    __device__ __forceinline__ float value(const MxSpecArgs& a, uint32_t j) {
-        const uint32_t wi = j >> 3, g = j >> 5;
-        if (wi != nwi) { nw = a.nib[wi]; nwi = wi; }
-        if (g != gi) { sw = a.sign[g]; scale = ldexpf(1.f, int(a.xexp[g]) - 130); gi = g; }
+    __device__ __forceinline__ float value(uint32_t j) {
+        const uint32_t wi = (j >> 3) - nb, g = (j >> 5) - gb;
+        if (wi != nwi) { nw = nib[wi]; nwi = wi; }
+        if (g != gi) { sw = sgn[g]; scale = ldexpf(1.f, int(xe[g]) - 130); gi = g; }
         const float v = float((nw >> (4 * (j & 7))) & 15u) * scale;   // exact: <= 4 significant bits
         return ((sw >> (j & 31)) & 1u) ? -v : v;
     }
 };
 
-// Draft weights, one wave per tile: a lane's 64 values go out as 8 16-byte stores.
-constexpr int MXD_WAVES = 4;
-
+// One wave per tile, lane = 64 positions.  The tile's nibble, sign and exponent
+// words are staged in the wave's LDS first (coalesced), so the walk over the
+// positions never waits on a global load.
 __global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecArgs a, uint16_t* __restrict__ out) {
-    const int lane = lane_id();
-    const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * MXD_WAVES + int(threadIdx.x >> 6));
+    __shared__ uint32_t snib[MXD_WAVES][MXD_NIB];
+    __shared__ uint32_t ssgn[MXD_WAVES][MXD_GRP];
+    __shared__ uint8_t sexp[MXD_WAVES][MXD_GRP];
+    const int lane = lane_id(), wave = int(threadIdx.x >> 6);
+    const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * MXD_WAVES + wave);
     if (t >= a.T) return;
     const int64_t f = t * TILE + 64 * lane;
     const bool live = f < a.N;                       // N % 64 == 0: a live lane has both words
     const uint32_t w0 = live ? a.bitmap[f >> 5] : 0u, w1 = live ? a.bitmap[(f >> 5) + 1] : 0u;
+    const uint32_t kp0 = a.kprefix[t], kp1 = a.kprefix[t + 1];
+    const uint32_t nb = kp0 >> 3, nn = ((kp1 + 7) >> 3) - nb;     // <= TILE / 8 + 1
+    const uint32_t gb = kp0 >> 5, ng = ((kp1 + 31) >> 5) - gb;    // <= TILE / 32 + 1
+    for (uint32_t i = lane; i < nn; i += 64) snib[wave][i] = a.nib[nb + i];
+    for (uint32_t i = lane; i < ng; i += 64) {
+        ssgn[wave][i] = a.sign[gb + i];
+        sexp[wave][i] = a.xexp[gb + i];
+    }
     const int pc = __popc(w0) + __popc(w1);
-    uint32_t j = a.kprefix[t] + uint32_t(wave_incl_add(pc) - pc);
-    MxCursor c;
+    uint32_t j = kp0 + uint32_t(wave_incl_add(pc) - pc);
+    wave_sync_lds();
+    MxLdsCursor c;
+    c.nib = snib[wave];
+    c.sgn = ssgn[wave];
+    c.xe = sexp[wave];
+    c.nb = nb;
+    c.gb = gb;
     uint32_t o[32];
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
         const uint32_t bit = ((i < 32 ? w0 : w1) >> (i & 31)) & 1u;
         uint32_t v = 0;
-        if (bit) v = __float_as_uint(c.value(a, j++)) >> 16;
+        if (bit) v = __float_as_uint(c.value(j++)) >> 16;
         if (i & 1) o[i >> 1] |= v << 16;
         else o[i >> 1] = v;
     }
