@@ -1189,8 +1189,7 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(MxArgs a, float* __rest
 // a row since K % 128 == 0); a wave prefix sum of their popcounts gives its first
 // kept index, and it walks its set bits, reading kept values j, j + 1, ... with
 // the nibble word (8 values) and the group's sign word and exponent (32 values)
-// cached in registers (the draft decode reads them from the tile's words staged
-// in LDS).
+// cached in registers.
 
 struct MxSpecArgs {
     const uint32_t* bitmap;
@@ -1200,76 +1199,6 @@ struct MxSpecArgs {
     const uint32_t* kprefix;
     int64_t M, K, N, T;
 };
-
-// Draft weights, one wave per tile: a lane's 64 values go out as 8 16-byte stores.
-constexpr int MXD_WAVES = 4;
-constexpr int MXD_NIB = TILE / 8 + 8;     // nibble words a tile's kept values span (<= TILE / 8 + 1)
-constexpr int MXD_GRP = TILE / 32 + 4;    // MX groups a tile's kept values span (<= TILE / 32 + 1)
-
-// Draft value of kept value j from the tile's words staged in LDS (nibble word
-// nb + i at nib[i], group gb + i at sgn[i] / xe[i]); consecutive calls reuse the
-// cached words.
-struct MxLdsCursor {
-    const uint32_t* nib;
-    const uint32_t* sgn;
-    const uint8_t* xe;
-    uint32_t nb, gb;
-    uint32_t nwi = 0xFFFFFFFFu, gi = 0xFFFFFFFFu, nw = 0, sw = 0;
-    float scale = 0.f;
-    __device__ __forceinline__ float value(uint32_t j) {
-        const uint32_t wi = (j >> 3) - nb, g = (j >> 5) - gb;
-        if (wi != nwi) { nw = nib[wi]; nwi = wi; }
-        if (g != gi) { sw = sgn[g]; scale = ldexpf(1.f, int(xe[g]) - 130); gi = g; }
-        const float v = float((nw >> (4 * (j & 7))) & 15u) * scale;   // exact: <= 4 significant bits
-        return ((sw >> (j & 31)) & 1u) ? -v : v;
-    }
-};
-
-// One wave per tile, lane = 64 positions.  The tile's nibble, sign and exponent
-// words are staged in the wave's LDS first (coalesced), so the walk over the
-// positions never waits on a global load.
-__global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecArgs a, uint16_t* __restrict__ out) {
-    __shared__ uint32_t snib[MXD_WAVES][MXD_NIB];
-    __shared__ uint32_t ssgn[MXD_WAVES][MXD_GRP];
-    __shared__ uint8_t sexp[MXD_WAVES][MXD_GRP];
-    const int lane = lane_id(), wave = int(threadIdx.x >> 6);
-    const int64_t t = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * MXD_WAVES + wave);
-    if (t >= a.T) return;
-    const int64_t f = t * TILE + 64 * lane;
-    const bool live = f < a.N;                       // N % 64 == 0: a live lane has both words
-    const uint32_t w0 = live ? a.bitmap[f >> 5] : 0u, w1 = live ? a.bitmap[(f >> 5) + 1] : 0u;
-    const uint32_t kp0 = a.kprefix[t], kp1 = a.kprefix[t + 1];
-    const uint32_t nb = kp0 >> 3, nn = ((kp1 + 7) >> 3) - nb;     // <= TILE / 8 + 1
-    const uint32_t gb = kp0 >> 5, ng = ((kp1 + 31) >> 5) - gb;    // <= TILE / 32 + 1
-    for (uint32_t i = lane; i < nn; i += 64) snib[wave][i] = a.nib[nb + i];
-    for (uint32_t i = lane; i < ng; i += 64) {
-        ssgn[wave][i] = a.sign[gb + i];
-        sexp[wave][i] = a.xexp[gb + i];
-    }
-    const int pc = __popc(w0) + __popc(w1);
-    uint32_t j = kp0 + uint32_t(wave_incl_add(pc) - pc);
-    wave_sync_lds();
-    MxLdsCursor c;
-    c.nib = snib[wave];
-    c.sgn = ssgn[wave];
-    c.xe = sexp[wave];
-    c.nb = nb;
-    c.gb = gb;
-    uint32_t o[32];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        const uint32_t bit = ((i < 32 ? w0 : w1) >> (i & 31)) & 1u;
-        uint32_t v = 0;
-        if (bit) v = __float_as_uint(c.value(j++)) >> 16;
-        if (i & 1) o[i >> 1] |= v << 16;
-        else o[i >> 1] = v;
-    }
-    if (live) {
-        uint4* d = reinterpret_cast<uint4*>(out + f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-    }
-}
 
 // Draft GEMV.  Block = R consecutive rows, its waves taking the tiles that meet
 // them round robin (a tile shared with the next block is walked by both, each
@@ -1460,6 +1389,72 @@ __device__ __forceinline__ void mx_kept_issue(const MxSpecArgs& a, int64_t t, Mx
     const uint32_t g = j0 >> 5;
     L.sg[0] = a.sign[g]; L.sg[1] = a.sign[g + 1]; L.sg[2] = a.sign[g + 2];
     L.xe = uint32_t(a.xexp[g]) | (uint32_t(a.xexp[g + 1]) << 8) | (uint32_t(a.xexp[g + 2]) << 16);
+}
+
+// Draft weights: two tiles per wave (both tiles' loads issued up front).  Lanes
+// take even shares of a tile's kept values, find their positions with the bitmap
+// cursor and scatter the bf16 values into the wave's zeroed LDS tile, which is
+// then written out 16 bytes a lane.
+constexpr int MXD_WAVES = 4;
+
+__global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecArgs a, uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint16_t dense[MXD_WAVES][TILE];
+    __shared__ WaveArea areas[MXD_WAVES];
+    const int wave = int(threadIdx.x >> 6), lane = lane_id();
+    uint16_t* d = dense[wave];
+    WaveArea& W = areas[wave];
+    auto decode = [&](int64_t t, const MxKept& L) {
+        uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+        W.bw[2 * lane] = L.b0;
+        W.bw[2 * lane + 1] = L.b1;
+        const int pc = __popc(L.b0) + __popc(L.b1);
+        W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+        wave_sync_lds();
+        if (L.cnt > 0) {
+            BitCursor<false> kc;
+            kc.start(W, int(L.first));
+            const uint32_t j0 = L.kp0 + L.first;
+            uint32_t q0 = L.q[0] >> (4 * (j0 & 7)), q1 = L.q[1], q2 = L.q[2], q3 = L.q[3], q4 = L.q[4],
+                     q5 = L.q[5], q6 = L.q[6], q7 = L.q[7], q8 = L.q[8];
+            uint32_t s0 = L.sg[0] >> (j0 & 31), s1 = L.sg[1], s2 = L.sg[2], xe = L.xe;
+            int ni = int(j0 & 7), si = int(j0 & 31);
+            float scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
+            for (int v = 0; v < L.cnt; ++v) {
+                const int pos = kc.next(W);
+                float w = float(q0 & 15u) * scale;               // exact: <= 4 significant bits
+                w = (s0 & 1u) ? -w : w;
+                d[pos] = uint16_t(__float_as_uint(w) >> 16);
+                q0 >>= 4;
+                s0 >>= 1;
+                if (++ni == 8) {
+                    ni = 0;
+                    q0 = q1; q1 = q2; q2 = q3; q3 = q4; q4 = q5; q5 = q6; q6 = q7; q7 = q8;
+                }
+                if (++si == 32) {
+                    si = 0;
+                    s0 = s1; s1 = s2;
+                    xe >>= 8;
+                    scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
+                }
+            }
+        }
+        wave_sync_lds();
+        const int tl = int(min<int64_t>(TILE, a.N - t * TILE));
+        uint4* o = reinterpret_cast<uint4*>(out + t * TILE);
+        for (int g = lane; g < tl / 8; g += 64) o[g] = *reinterpret_cast<const uint4*>(d + 8 * g);
+    };
+    const int64_t t0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 2 * MXD_WAVES + wave);
+    const int64_t t1 = t0 + MXD_WAVES;
+    if (t0 >= a.T) return;
+    MxKept l0, l1;
+    mx_kept_issue(a, t0, l0);
+    mx_kept_issue(a, min<int64_t>(t1, a.T - 1), l1);
+    decode(t0, l0);
+    if (t1 >= a.T) return;
+    wave_sync_lds();                                         // the tile is read out before it is overwritten
+    decode(t1, l1);
 }
 
 template <int BMAX>
@@ -1682,7 +1677,7 @@ mbd_status mx_spec_decode(const mbd_dweights* w, uint16_t* out, hipStream_t st) 
     if (!out) return fail(MBD_EINVAL, "output is NULL");
     if (!aligned(out, 16)) return fail(MBD_EALIGN, "output must be 16-byte aligned");
     if (a.N == 0) return MBD_OK;
-    hipLaunchKernelGGL(mx_spec_decode_kernel, dim3(unsigned((a.T + MXD_WAVES - 1) / MXD_WAVES)), dim3(64 * MXD_WAVES),
+    hipLaunchKernelGGL(mx_spec_decode_kernel, dim3(unsigned((a.T + 2 * MXD_WAVES - 1) / (2 * MXD_WAVES))), dim3(64 * MXD_WAVES),
                        0, st, a, out);
     return hip_check("spec decode launch");
 }
