@@ -108,6 +108,16 @@ class BlockQuantGemv(Workload):
             c["dense_format_bytes"] = self.M * self.K // 4 + self.M * (self.K // 128) * 2
         return c
 
+    def oracle_pack(self):
+        """The oracle's pack of the whole matrix (quantize + code packing), once."""
+        from oracle import int4, ternary, ternary_skip
+        if self.kind == "ternary_skip":
+            return ternary_skip.pack(self.w)
+        return (int4 if self.kind == "int4" else ternary).pack(self.w)
+
+    def bf16_bytes(self):
+        return 2 * self.M * self.K
+
     def oracle_call(self):
         """One oracle call: unpack + dequant from the packed sections + fp64 matvec."""
         from oracle import gemv, int4, ternary, ternary_skip
@@ -153,6 +163,9 @@ class MoeGemv(Workload):
         self.yd = torch.empty((T, wl.topk, wl.K), dtype=torch.float32, device=dev)
         self.ws = torch.empty(mbd.mbd_moe_workspace_bytes(wl.experts, T, wl.topk), dtype=torch.uint8, device=dev)
         self.wl, self.mbd = wl, mbd
+
+    def bf16_bytes(self):
+        return 2 * 2 * self.wl.M * self.wl.K * self.distinct      # up and down matrices of each distinct expert
 
     def bytes_per_step(self):
         wl, T = self.wl, self.T
@@ -214,6 +227,9 @@ class CassandraWl(Workload):
         else:
             self.out = torch.empty((self.M, self.K), dtype=torch.int16, device=dev)
         self.mbd = mbd
+
+    def bf16_bytes(self):
+        return 2 * self.M * self.K
 
     def bytes_per_step(self):
         if self.B == 0:                                  # restore / draft decode: sections read, bf16 written
@@ -388,6 +404,28 @@ ALL = ["int4_8k", "int4_8k_b4", "int4_8k_b8", "int4_8k_b16", "ternary_1k", "int4
        "ternary_skip_8192x28672_b8", "cassandra_spec_mx", "cassandra_encode"]
 
 
+_HOLD_CYCLES = None
+
+
+def hold_gpu(us=400.0):
+    """Enqueue a spin kernel of about ``us`` microseconds on the current stream.  The
+    host submits the timed launches while the GPU spins, so the start event, which
+    the stream reaches only after the spin, is not delayed by the host's submission
+    of the first launches: the timed region holds the K steps and nothing else."""
+    import torch
+    global _HOLD_CYCLES
+    if _HOLD_CYCLES is None:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 1 << 20
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        _HOLD_CYCLES = n / max(1e-3, e0.elapsed_time(e1) * 1000.0)     # cycles per microsecond
+    torch.cuda._sleep(int(_HOLD_CYCLES * us))
+
+
 def time_workload(wl, steps, warmup, use_graph=True):
     """(seconds for `steps` steps, per-step ms) with HIP events on the launch stream."""
     import torch
@@ -413,6 +451,7 @@ def time_workload(wl, steps, warmup, use_graph=True):
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    hold_gpu(400.0 if use_graph else 400.0 + 10.0 * steps)
     e0.record(stream)
     if use_graph:
         g.replay()
@@ -423,6 +462,52 @@ def time_workload(wl, steps, warmup, use_graph=True):
     torch.cuda.synchronize()
     sec = e0.elapsed_time(e1) / 1000.0
     return sec, 1000.0 * sec / steps
+
+
+def read_peak(nbytes, dev, steps=100, shapes=None):
+    """Best streaming-read rate over launch shapes for a read of ``nbytes`` per launch
+    (the library's probe kernel: 16-byte non-temporal loads, eight in flight per
+    thread), cycling through copies of >= 1.1 GiB in total as the workloads do.
+    Returns (best record, all records); a record gives the shape, the per-launch
+    microseconds and GB/s."""
+    import torch
+    import memory_bound_decode_amd as mbd
+    n16 = max(1, nbytes // 16)
+    nbytes = 16 * n16
+    copies = [torch.empty(n16 * 4, dtype=torch.int32, device=dev) for _ in range(_pool_copies(nbytes))]
+    for c in copies:
+        c.fill_(1)
+    if shapes is None:
+        shapes = []
+        for threads in (256, 512, 1024):
+            one_round = -(-n16 // (threads * 8))
+            for blocks in sorted({256, 512, 1024, 2048, 4096, 8192, one_round}):
+                if blocks <= 4 * one_round:
+                    shapes.append((blocks, threads))
+    sink = torch.zeros(max(b for b, _ in shapes), dtype=torch.int32, device=dev)
+    recs = []
+    for blocks, threads in shapes:
+        for i in range(3):
+            mbd.mbd_probe_stream_read(copies[i % len(copies)], sink, blocks, threads)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                mbd.mbd_probe_stream_read(copies[i % len(copies)], sink, blocks, threads)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_gpu()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / steps
+        recs.append({"blocks": blocks, "threads": threads, "us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1)})
+        del g
+    best = max(recs, key=lambda r: r["gbs"])
+    return dict(best, bytes=nbytes), recs
 
 
 def traffic_from_profiles(wl):
@@ -466,13 +551,18 @@ def cpu_baseline(wl, budget_s=15.0):
         elapsed += time.perf_counter() - t1
         calls += 1
     gbs = wl.bytes_per_step() * calls / elapsed / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+    extra = {"cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": int(blas)}
+    if hasattr(wl, "oracle_pack"):
+        t1 = time.perf_counter()
+        wl.oracle_pack()
+        extra["oracle_pack_s"] = round(time.perf_counter() - t1, 2)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle", **extra,
             "sample": "%d full oracle calls (unpack + fp64 dequant + numpy fp64 matvec) over the whole "
                       "%s matrix in %.1f s; elementwise steps single-threaded, matvec on %d BLAS threads"
                       % (calls, wl.name, elapsed, blas)}, ref
 
 
-def measure(name, dev, steps, warmup, with_cpu, use_graph=True):
+def measure(name, dev, steps, warmup, with_cpu, use_graph=True, with_read_peak=False):
     wl = make_workload(name, dev)
     sec, ms = time_workload(wl, steps, warmup, use_graph)
     bps = wl.bytes_per_step()
@@ -489,6 +579,17 @@ def measure(name, dev, steps, warmup, with_cpu, use_graph=True):
     }
     if hasattr(wl, "B") and getattr(wl, "B", 0):
         out["tok_per_s_equiv"] = round(wl.B / (ms / 1000.0), 1)
+    if hasattr(wl, "bf16_bytes"):
+        # the same weights read as bf16 in the same time (not comparable to the peak)
+        out["bf16_equiv_gbs"] = round(wl.bf16_bytes() / (ms / 1000.0) / 1e9, 1)
+    if hasattr(wl, "bpw"):
+        # context: tokens/s of a 9B-active model whose weights stream at this rate
+        out["tok_per_s_9b_active_equiv"] = round(gbs * 1e9 / (9e9 * wl.bpw / 8.0), 1)
+    if with_read_peak:
+        best, _ = read_peak(bps, dev)
+        out["read_peak"] = best
+        out["roofline"]["read_peak"] = best["gbs"]
+        out["roofline"]["frac_of_read_peak"] = round(gbs / best["gbs"], 4)
     if with_cpu:
         cb, ref = cpu_baseline(wl)
         out["cpu_baseline"] = cb
@@ -507,6 +608,9 @@ def main():
     ap.add_argument("--all", default=None, help="append one JSON line per workload to this file")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of one HIP graph")
+    ap.add_argument("--read-peak", type=int, default=0, metavar="BYTES",
+                    help="only sweep the streaming-read probe over launch shapes for reads of BYTES per launch")
+    ap.add_argument("--no-read-peak", action="store_true", help="leave the read-peak field out of the bench line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy (y = -x, fp32) reading and writing BYTES per "
                          "launch, --steps times: the reference kernel for scaling the HBM byte counters")
@@ -538,7 +642,15 @@ def main():
             with open(args.all, "a") as f:
                 f.write(json.dumps(r) + "\n")
             torch.cuda.empty_cache()
-    res = measure(args.workload, dev, args.steps, args.warmup, with_cpu=not args.no_cpu, use_graph=not args.no_graph)
+    if args.read_peak:
+        best, recs = read_peak(args.read_peak, dev, steps=args.steps)
+        for r in recs:
+            print(json.dumps(dict(r, bytes=best["bytes"])), flush=True)
+        print(json.dumps({"read_peak": best, "peak_gbs": HBM_PEAK_GBS, "frac": round(best["gbs"] / HBM_PEAK_GBS, 4)}),
+              flush=True)
+        return
+    res = measure(args.workload, dev, args.steps, args.warmup, with_cpu=not args.no_cpu, use_graph=not args.no_graph,
+                  with_read_peak=not args.no_read_peak)
     if args.all:
         with open(args.all, "a") as f:
             f.write(json.dumps(res) + "\n")

@@ -192,12 +192,24 @@ mbd_status mbd_pack(int32_t fmt, const uint16_t* w_bf16_host, int64_t M, int64_t
                     mbd_packed** out);
 
 /* Copy up to `cap` section descriptors into arr (section order as documented above)
- * and the total count into *n.  Pointers stay valid until mbd_packed_free(h). */
+ * and the total count into *n.  Pointers stay valid until mbd_packed_free(h).  The
+ * sections are the saved form of a quantized weight: codes and scales stored apart
+ * ([GPT54-INT4] 3.2, the weight saved with its scales; [Bonsai2] 3.6, export of the
+ * packed model), or the speculation and verification parts ([Cassandra] 3.2: the
+ * draft loads the first only, the target both).  cap = 0 only reports *n.
+ * Errors: EINVAL (NULL h or n, or arr NULL with cap > 0). */
 mbd_status mbd_packed_sections(const mbd_packed* h, mbd_section* arr, int32_t cap, int32_t* n);
+/* Format statistics of a handle ([Cassandra] 3.3: exponent entropy of the kept
+ * values and average unary code length; bits per weight of all sections and of
+ * the speculation sections; [Bonsai2] 1.2: fraction of ternary zeros).
+ * Errors: EINVAL (NULL argument). */
 mbd_status mbd_packed_stats(const mbd_packed* h, mbd_stats* out);
 /* Full CPU consistency check of a handle's sections (codes in range, bitmap row
- * counts, tile table vs unary stream, codebook ranks).  EFORMAT on failure. */
+ * counts, tile table vs unary stream, codebook ranks): the conditions under which
+ * the decode of [Cassandra] 3.5 and the dequantization of [Bonsai2] 1.2 and
+ * [GPT54-INT4] 3.2 are defined.  EFORMAT on failure, EINVAL for NULL. */
 mbd_status mbd_validate(const mbd_packed* h);
+/* Releases the handle and its host sections; NULL is a no-op. */
 void mbd_packed_free(mbd_packed* h);
 
 /* ------------------------------------------------------------------ device data
@@ -215,8 +227,12 @@ typedef struct {
     const void* sec[MBD_MAX_SECTIONS];
 } mbd_dweights;
 
-/* Dense dequantized weight w_out fp32 [M][K] (TERNARY, INT4, MX32): q*s or
- * (-1)^S*mag*2^(X-134), both exact in fp32.  w_out 16-byte aligned. */
+/* Dense dequantized weight w_out fp32 [M][K] (TERNARY, TERNARY_SKIP, INT4, MX32):
+ * q*s ([Bonsai2] 1.2, the ternary value is the code times its block scale;
+ * [GPT54-INT4] 3.2, the INT4 value is the code times its group scale) or
+ * (-1)^S*mag*2^(X-134) ([Cassandra] 3.3, the MX value is the shifted significand at
+ * the shared exponent), all exact in fp32.  w_out 16-byte aligned, caller-owned.
+ * Errors: EINVAL (NULL, unknown format), ESHAPE, EALIGN, EHIP. */
 mbd_status mbd_dequant(const mbd_dweights* w, float* w_out, void* stream);
 
 /* Fused dequant-GEMV / skinny GEMM: y[b][m] = sum_k deq(W)[m][k] * x[b][k] with fp32
@@ -287,6 +303,17 @@ mbd_status mbd_encode_plan(const uint16_t* w, const float* act_norm, int64_t M, 
 mbd_status mbd_encode_cassandra(const uint16_t* w, const float* act_norm, int64_t M, int64_t K,
                                 int32_t keep_num, int32_t keep_den, const mbd_encode_plan_t* plan,
                                 void* const* sec, void* ws, uint64_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ measurement aid
+ * Streaming-read probe, not a step of the method: reads `bytes` of device memory at
+ * src (16-byte aligned, a multiple of 16) with `blocks` x `threads` threads (threads
+ * a multiple of 64, at most 1024), 16-byte non-temporal loads, eight in flight per
+ * thread.  The measured rate is the practical ceiling of the weight-streaming kernels
+ * ([Bolt] background: a decode step's time is the weight bytes it reads).  sink:
+ * device uint32 [blocks], never written in practice (it keeps the loads alive).
+ * Errors: EINVAL, EALIGN, ESHAPE, EHIP. */
+mbd_status mbd_probe_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int32_t blocks,
+                                 int32_t threads, void* stream);
 
 const char* mbd_status_str(mbd_status s);
 const char* mbd_last_error(void);

@@ -197,3 +197,9 @@ def mbd_encode_cassandra(w, act_norm, keep_num: int, keep_den: int, plan: MbdEnc
     arr = (ctypes.c_void_p * 8)(*[t.data_ptr() for t in sections])
     check(lib().mbd_encode_cassandra(_ptr(w), _ptr(act_norm), M, K, keep_num, keep_den, ctypes.byref(plan), arr, _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "mbd_encode_cassandra")
+
+
+def mbd_probe_stream_read(src, sink, blocks: int, threads: int, stream=None) -> None:
+    """Streaming-read probe over the whole of ``src`` (a device tensor); measurement aid."""
+    check(lib().mbd_probe_stream_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink), int(blocks),
+                                      int(threads), _stream(stream)), "mbd_probe_stream_read")

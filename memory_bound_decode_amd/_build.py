@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libmbd.so")
 
-HIP_SOURCES = ["gemv.hip", "cassandra.hip", "encoder.hip"]
+HIP_SOURCES = ["gemv.hip", "cassandra.hip", "encoder.hip", "probe.hip"]
 CXX_SOURCES = ["packer.cpp"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

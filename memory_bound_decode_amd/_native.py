@@ -62,6 +62,7 @@ SIGNATURES = {
                                   POINTER(MbdEncodePlan), c_void_p]),
     "mbd_encode_cassandra": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int32, c_int32,
                                        POINTER(MbdEncodePlan), POINTER(c_void_p), c_void_p, c_uint64, c_void_p]),
+    "mbd_probe_stream_read": (c_int32, [c_void_p, c_uint64, c_void_p, c_int32, c_int32, c_void_p]),
     "mbd_status_str": (c_char_p, [c_int32]),
     "mbd_last_error": (c_char_p, []),
 }

@@ -27,6 +27,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "hip_check.h"
 #include "mbd_internal.h"
 
 namespace mbd {
@@ -1585,12 +1586,6 @@ namespace {
 
 inline bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
 
-mbd_status hip_check(const char* what) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(MBD_EHIP, "%s: %s", what, hipGetErrorString(e));
-    return MBD_OK;
-}
-
 mbd_status cas_args(const mbd_dweights* w, bool need_verify, CasArgs* a) {
     if (!w) return fail(MBD_EINVAL, "NULL descriptor");
     if (w->fmt != MBD_CASSANDRA) return fail(MBD_EINVAL, "descriptor is not MBD_CASSANDRA");
@@ -1780,15 +1775,18 @@ mbd_status mbd_dequant_mx32(const mbd_dweights* w, float* out, hipStream_t st) {
 extern "C" {
 
 mbd_status mbd_spec_decode(const mbd_dweights* w, uint16_t* w_spec, void* stream) {
+    hip_clear();
     if (w && w->fmt == MBD_CASSANDRA_MX) return mx_spec_decode(w, w_spec, reinterpret_cast<hipStream_t>(stream));
     return decode_dense(w, w_spec, reinterpret_cast<hipStream_t>(stream), false);
 }
 
 mbd_status mbd_verify_restore(const mbd_dweights* w, uint16_t* w_out, void* stream) {
+    hip_clear();
     return decode_dense(w, w_out, reinterpret_cast<hipStream_t>(stream), true);
 }
 
 mbd_status mbd_spec_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y, void* stream) {
+    hip_clear();
     if (w && w->fmt == MBD_CASSANDRA_MX) return mx_spec_gemv(w, x, B, y, reinterpret_cast<hipStream_t>(stream));
     CasArgs a;
     mbd_status s = cas_args(w, false, &a);

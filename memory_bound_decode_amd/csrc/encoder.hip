@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cstring>
 
+#include "hip_check.h"
 #include "mbd_internal.h"
 
 namespace mbd {
@@ -430,12 +431,6 @@ namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-mbd_status enc_hip(const char* what) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(MBD_EHIP, "%s: %s", what, hipGetErrorString(e));
-    return MBD_OK;
-}
-
 mbd_status enc_args(const uint16_t* w, const float* norm, int64_t M, int64_t K, int32_t kn, int32_t kd, void* ws,
                     uint64_t ws_bytes, EncArgs* a) {
     if (!w || !norm || !ws) return fail(MBD_EINVAL, "NULL argument");
@@ -471,7 +466,7 @@ mbd_status launch_select(const EncArgs& a, hipStream_t st) {
     else if (wpt <= 2) hipLaunchKernelGGL((enc_select_kernel<WRITE, 2>), g, b, 0, st, a);
     else if (wpt <= 4) hipLaunchKernelGGL((enc_select_kernel<WRITE, 4>), g, b, 0, st, a);
     else hipLaunchKernelGGL((enc_select_kernel<WRITE, 0>), g, b, 0, st, a);
-    return enc_hip("encoder selection launch");
+    return hip_check("encoder selection launch");
 }
 
 }  // namespace
@@ -487,6 +482,7 @@ mbd_status mbd_encode_workspace_bytes(int64_t M, uint64_t* bytes) {
 
 mbd_status mbd_encode_plan(const uint16_t* w, const float* act_norm, int64_t M, int64_t K, int32_t keep_num,
                            int32_t keep_den, void* ws, uint64_t ws_bytes, mbd_encode_plan_t* plan, void* stream) {
+    hip_clear();
     if (!plan) return fail(MBD_EINVAL, "plan is NULL");
     EncArgs a;
     mbd_status s = enc_args(w, act_norm, M, K, keep_num, keep_den, ws, ws_bytes, &a);
@@ -495,11 +491,11 @@ mbd_status mbd_encode_plan(const uint16_t* w, const float* act_norm, int64_t M, 
     hipLaunchKernelGGL(enc_clear_kernel, dim3(1), dim3(256), 0, st, a.hdr, a.hist);
     if ((s = launch_select<false>(a, st)) != MBD_OK) return s;
     hipLaunchKernelGGL(enc_codebook_kernel, dim3(1), dim3(256), 0, st, a, 0);
-    if ((s = enc_hip("encoder plan launch")) != MBD_OK) return s;
+    if ((s = hip_check("encoder plan launch")) != MBD_OK) return s;
     Header h;
     if (hipMemcpyAsync(&h, a.hdr, sizeof h, hipMemcpyDeviceToHost, st) != hipSuccess ||
         hipStreamSynchronize(st) != hipSuccess)
-        return enc_hip("encoder plan read-back");
+        return hip_check("encoder plan read-back");
     if (h.bad & 1u) return fail(MBD_ERANGE, "bf16 Inf/NaN in w");
     if (h.bad & 2u) return fail(MBD_ERANGE, "act_norm has a negative or non-finite entry");
     const int64_t N = M * K, nk = M * int64_t(a.nk), T = (N + TILE - 1) / TILE;
@@ -521,6 +517,7 @@ mbd_status mbd_encode_plan(const uint16_t* w, const float* act_norm, int64_t M, 
 mbd_status mbd_encode_cassandra(const uint16_t* w, const float* act_norm, int64_t M, int64_t K, int32_t keep_num,
                                 int32_t keep_den, const mbd_encode_plan_t* plan, void* const* sec, void* ws,
                                 uint64_t ws_bytes, void* stream) {
+    hip_clear();
     if (!plan || !sec) return fail(MBD_EINVAL, "NULL argument");
     EncArgs a;
     mbd_status s = enc_args(w, act_norm, M, K, keep_num, keep_den, ws, ws_bytes, &a);
@@ -563,7 +560,7 @@ mbd_status mbd_encode_cassandra(const uint16_t* w, const float* act_norm, int64_
         else if (wpt <= 2) hipLaunchKernelGGL((enc_write_kernel<2>), g, b, 0, st, a, T, ub, cap);
         else hipLaunchKernelGGL((enc_write_kernel<0>), g, b, 0, st, a, T, ub, cap);
     }
-    return enc_hip("encoder launch");
+    return hip_check("encoder launch");
 }
 
 }  // extern "C"

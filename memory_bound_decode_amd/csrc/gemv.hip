@@ -27,6 +27,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "hip_check.h"
 #include "mbd_internal.h"
 
 namespace mbd {
@@ -975,12 +976,6 @@ namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-mbd_status hip_check(const char* what) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(MBD_EHIP, "%s: %s", what, hipGetErrorString(e));
-    return MBD_OK;
-}
-
 #ifndef MBD_B1_IPW
 #define MBD_B1_IPW 4          // items per wave at least (4 KB of codes), few-row kernel
 #endif
@@ -1107,6 +1102,7 @@ mbd_status mbd_dequant_mx32(const mbd_dweights* w, float* out, hipStream_t st);
 extern "C" {
 
 mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y, void* stream) {
+    hip_clear();
     if (!w || !x || !y) return fail(MBD_EINVAL, "NULL argument");
     if (B < 1 || B > 16) return fail(MBD_ESHAPE, "B=%d outside [1, 16]", B);
     if (w->M < 0 || w->K < 1) return fail(MBD_ESHAPE, "bad shape M=%lld K=%lld", (long long)w->M, (long long)w->K);
@@ -1120,10 +1116,12 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128) return fail(MBD_EINVAL, "unknown format %d", w->fmt);
     if (w->K % 128) return fail(MBD_ESHAPE, "K=%lld is not a multiple of 128", (long long)w->K);
     if (w->M > INT32_MAX || w->K > INT32_MAX) return fail(MBD_ESHAPE, "shape too large");
+    const bool ter = w->fmt == MBD_TERNARY_B128;
+    // the kernels address a matrix's codes with 32-bit byte offsets
+    if (w->M * (w->K / (ter ? 4 : 2)) >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "codes beyond 4 GiB");
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2)) return fail(MBD_EALIGN, "codes must be 16-byte aligned");
     if (w->M == 0) return MBD_OK;
-    const bool ter = w->fmt == MBD_TERNARY_B128;
     if (B > 4) {
         // 5..16 rows: the 32-row kernel with activations read per group (at 8 rows
         // it measured even with the few-row kernel, above that faster)
@@ -1153,6 +1151,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
 }
 
 mbd_status mbd_dequant(const mbd_dweights* w, float* out, void* stream) {
+    hip_clear();
     if (!w || !out) return fail(MBD_EINVAL, "NULL argument");
     if (!aligned(out, 16)) return fail(MBD_EALIGN, "w_out must be 16-byte aligned");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1205,6 +1204,7 @@ mbd_status mbd_moe_workspace_bytes(int64_t n_mats, int32_t T, int32_t k, uint64_
 
 mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
                         int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
+    hip_clear();
     if (!w || !route || !x || !y || !ws) return fail(MBD_EINVAL, "NULL argument");
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128)
         return fail(MBD_EINVAL, "expert GEMV supports TERNARY and INT4");

@@ -139,6 +139,12 @@ def test_gemv_argument_errors(L):
     assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_EALIGN
     d = _desc(mbd.MBD_MX32, 16, 48)
     assert L.mbd_gemv(ctypes.byref(d), P16, 1, P16, None) == mbd.MBD_ESHAPE
+    # codes addressed with 32-bit byte offsets: a matrix whose codes reach 4 GiB is refused
+    for fmt, M in ((mbd.MBD_INT4_G128, 1 << 20), (mbd.MBD_TERNARY_B128, 1 << 21)):
+        for B in (1, 8):
+            d = _desc(fmt, M, 8192)
+            assert L.mbd_gemv(ctypes.byref(d), P16, B, P16, None) == mbd.MBD_ESHAPE
+            assert b"4 GiB" in L.mbd_last_error()
 
 
 def test_skip_format_argument_errors(L):
@@ -219,3 +225,4 @@ def test_cassandra_and_moe_argument_errors(L):
     assert L.mbd_moe_gemv(ctypes.byref(e), P16, 2, 4, P16, 0, P16, P16, 1, None) == mbd.MBD_EINVAL  # ws too small
     e.fmt = mbd.MBD_CASSANDRA
     assert L.mbd_moe_gemv(ctypes.byref(e), P16, 2, 4, P16, 0, P16, P16, need.value, None) == mbd.MBD_EINVAL
+

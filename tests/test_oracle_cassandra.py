@@ -177,3 +177,49 @@ def test_mx_invariants():
     # every MX value is exactly a bf16 value
     vb = synth.f32_to_bf16_bits(v.astype(np.float32))
     np.testing.assert_array_equal(bits.bf16_value(vb), v)
+
+
+# ---------------------------------------------------------------- statistics (closed form)
+
+def _stats_matrix(counts, rng):
+    """bf16 [4][1280] whose kept values (the top 384 of each row, norms all 1) have
+    exponent 130 + i exactly counts[i] times per row; the pruned values have exponent
+    100, far below every kept one, so the keep rule cannot pick them."""
+    M, K = 4, 1280
+    assert sum(counts) == cassandra.keep_count(K)
+    w = np.empty((M, K), np.uint16)
+    for r in range(M):
+        exps = np.concatenate([np.full(c, 130 + i) for i, c in enumerate(counts)]
+                              + [np.full(K - sum(counts), 100)])
+        sign = rng.integers(0, 2, K) << 15
+        mant = rng.integers(0, 128, K)
+        w[r] = rng.permutation((sign | (exps << 7) | mant).astype(np.uint16))
+    return w
+
+
+@pytest.mark.parametrize("counts,H,unary", [
+    # four equiprobable exponents: H = 2 bits, codewords 1, 01, 001, 0001 -> 2.5 bits
+    ((96, 96, 96, 96), Fraction(2), Fraction(5, 2)),
+    # p = 1/2, 1/4, 1/8, 1/8: H = 1.75 bits; average codeword 1/2 + 2/4 + 3/8 + 4/8
+    ((192, 96, 48, 48), Fraction(7, 4), Fraction(15, 8)),
+])
+def test_stats_closed_form(counts, H, unary):
+    """Cassandra review 3.3: the exponent entropy and the average unary code length of
+    a histogram known in closed form; bits per weight as exact fractions of M*K.  A
+    natural-log entropy (2 ln 2 = 1.386 for the first case) or probabilities taken
+    over all M*K values instead of the kept ones fails here."""
+    w = _stats_matrix(counts, np.random.default_rng(11))
+    M, K = w.shape
+    norms = np.ones(K, np.float32)
+    sec = cassandra.pack(w, norms)
+    st = cassandra.stats(sec, M, K)
+    n, nk = M * K, M * cassandra.keep_count(K)
+    assert st["kept"] == nk
+    assert st["entropy_bits"] == pytest.approx(float(H), abs=1e-12)
+    assert Fraction(sec["unary_bits"], nk) == unary
+    assert st["unary_avg_bits"] == pytest.approx(float(unary), abs=1e-12)
+    assert Fraction(st["spec_bpw"]).limit_denominator(n) == Fraction(n + 4 * nk, n) + unary * Fraction(nk, n)
+    assert Fraction(st["verify_bpw"]).limit_denominator(n) == Fraction(4 * nk + 16 * (n - nk), n)
+    # the codebook ranks the exponents by count, ties to the smaller exponent
+    order = sorted(range(4), key=lambda i: (-counts[i], i))
+    np.testing.assert_array_equal(sec["codebook"], [130 + i for i in order])
