@@ -259,6 +259,18 @@ mbd_status mbd_moe_gemv(const mbd_dweights* experts, const int32_t* route, int32
                         int32_t k, const uint16_t* x, int32_t x_per_pair, float* y,
                         void* ws, uint64_t ws_bytes, void* stream);
 
+/* mbd_moe_gemv for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the grouping tables in a static
+ * device array of the library (1 MiB per device, held until the process ends; its
+ * address is looked up once per device on the first call there).  Routes whose
+ * workspace (mbd_moe_workspace_bytes) exceeds 1 MiB return MBD_ESHAPE.  Every call
+ * on one device shares that array: calls that overlap on a device race (serialise
+ * them on one stream).  No allocation of any kind, host or device. */
+mbd_status mbd_moe_gemv_noalloc(const mbd_dweights* experts, const int32_t* route, int32_t T,
+                                int32_t k, const uint16_t* x, int32_t x_per_pair, float* y,
+                                void* stream);
+
 /* Draft weights from the speculation data only ([Cassandra] 3.2, path b): bf16
  * w_spec [M][K]; kept values get (S<<15)|(E<<7)|(M_hi<<4), pruned values +0.0.
  * Sections 6-7 are not read and may be NULL.  w_spec 16-byte aligned. */

@@ -162,6 +162,13 @@ def mbd_moe_gemv(dw: DeviceWeights, route, x, x_per_pair: bool, y, ws, stream=No
                              _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)), "mbd_moe_gemv")
 
 
+def mbd_moe_gemv_noalloc(dw: DeviceWeights, route, x, x_per_pair: bool, y, stream=None) -> None:
+    """mbd_moe_gemv without a workspace (the library's static device scratch)."""
+    T, k = int(route.shape[0]), int(route.shape[1])
+    check(lib().mbd_moe_gemv_noalloc(dw.ref(), _ptr(route), T, k, _ptr(x), int(bool(x_per_pair)), _ptr(y),
+                                     _stream(stream)), "mbd_moe_gemv_noalloc")
+
+
 def mbd_spec_decode(dw: DeviceWeights, out, stream=None) -> None:
     check(lib().mbd_spec_decode(dw.ref(), _ptr(out), _stream(stream)), "mbd_spec_decode")
 

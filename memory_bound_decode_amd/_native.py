@@ -54,6 +54,8 @@ SIGNATURES = {
     "mbd_moe_workspace_bytes": (c_int32, [c_int64, c_int32, c_int32, POINTER(c_uint64)]),
     "mbd_moe_gemv": (c_int32, [POINTER(MbdDWeights), c_void_p, c_int32, c_int32, c_void_p, c_int32,
                                c_void_p, c_void_p, c_uint64, c_void_p]),
+    "mbd_moe_gemv_noalloc": (c_int32, [POINTER(MbdDWeights), c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                                       c_void_p, c_void_p]),
     "mbd_spec_decode": (c_int32, [POINTER(MbdDWeights), c_void_p, c_void_p]),
     "mbd_spec_gemv": (c_int32, [POINTER(MbdDWeights), c_void_p, c_int32, c_void_p, c_void_p]),
     "mbd_verify_restore": (c_int32, [POINTER(MbdDWeights), c_void_p, c_void_p]),

@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "hip_check.h"
@@ -1202,9 +1203,14 @@ mbd_status mbd_moe_workspace_bytes(int64_t n_mats, int32_t T, int32_t k, uint64_
     return MBD_OK;
 }
 
-mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
-                        int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
-    hip_clear();
+}  // extern "C"
+
+namespace {
+
+// The expert GEMV behind both entry points; ws is device memory of ws_bytes bytes
+// (the caller's workspace, or this device's static scratch).
+mbd_status moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
+                    int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
     if (!w || !route || !x || !y || !ws) return fail(MBD_EINVAL, "NULL argument");
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128)
         return fail(MBD_EINVAL, "expert GEMV supports TERNARY and INT4");
@@ -1279,6 +1285,65 @@ mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, 
         if (sll) hipLaunchKernelGGL((moe_mq_kernel<false, true>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);
         else hipLaunchKernelGGL((moe_mq_kernel<false, false>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);
     return hip_check("expert gemv launch");
+}
+
+}  // namespace
+
+// Device scratch of the allocation-free expert GEMV: the grouping tables (job
+// count, pair ids, jobs) that the caller's workspace holds otherwise.  Every device
+// the library runs on holds its own copy until the process ends.  Host code never
+// uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr uint64_t kMoeScratchBytes = uint64_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// This device's address of `scratch`, looked up on the first call on the device.
+mbd_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return hip_check("hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MBD_EHIP, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MBD_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MBD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mbd_status mbd_moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
+                        int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
+    hip_clear();
+    return moe_gemv(w, route, T, k, x, x_per_pair, y, ws, ws_bytes, stream);
+}
+
+mbd_status mbd_moe_gemv_noalloc(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k,
+                                const uint16_t* x, int32_t x_per_pair, float* y, void* stream) {
+    hip_clear();
+    if (!w || !route || !x || !y) return fail(MBD_EINVAL, "NULL argument");
+    uint64_t need = 0;
+    mbd_status s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need);
+    if (s != MBD_OK) return s;
+    if (need > kMoeScratchBytes)
+        return fail(MBD_ESHAPE, "route of %d x %d pairs over %lld experts needs %llu bytes of scratch, above the "
+                    "library's %llu", T, k, (long long)w->n_mats, (unsigned long long)need,
+                    (unsigned long long)kMoeScratchBytes);
+    void* ws = nullptr;
+    if ((s = scratch_address(&ws)) != MBD_OK) return s;
+    return moe_gemv(w, route, T, k, x, x_per_pair, y, ws, kMoeScratchBytes, stream);
 }
 
 }  // extern "C"

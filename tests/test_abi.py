@@ -226,3 +226,17 @@ def test_cassandra_and_moe_argument_errors(L):
     e.fmt = mbd.MBD_CASSANDRA
     assert L.mbd_moe_gemv(ctypes.byref(e), P16, 2, 4, P16, 0, P16, P16, need.value, None) == mbd.MBD_EINVAL
 
+
+def test_moe_noalloc_argument_errors(L):
+    """The allocation-free expert GEMV refuses routes whose grouping tables exceed its
+    1 MiB static scratch, and NULL arguments, before any HIP call."""
+    e = _desc(mbd.MBD_TERNARY_B128, 64, 256, n_mats=64)
+    assert L.mbd_moe_gemv_noalloc(None, P16, 2, 4, P16, 0, P16, None) == mbd.MBD_EINVAL
+    assert L.mbd_moe_gemv_noalloc(ctypes.byref(e), None, 2, 4, P16, 0, P16, None) == mbd.MBD_EINVAL
+    need = ctypes.c_uint64()
+    T_ok, T_big = 1024, 8192                          # 8192 pairs fit; 65536 pairs need about 2.3 MiB
+    assert L.mbd_moe_workspace_bytes(64, T_ok, 8, ctypes.byref(need)) == mbd.MBD_OK and need.value <= 1 << 20
+    assert L.mbd_moe_workspace_bytes(64, T_big, 8, ctypes.byref(need)) == mbd.MBD_OK and need.value > 1 << 20
+    assert L.mbd_moe_gemv_noalloc(ctypes.byref(e), P16, T_big, 8, P16, 0, P16, None) == mbd.MBD_ESHAPE
+    assert b"scratch" in L.mbd_last_error()
+    assert L.mbd_moe_gemv_noalloc(ctypes.byref(e), P16, 2, 0, P16, 0, P16, None) == mbd.MBD_ESHAPE   # k = 0
