@@ -703,16 +703,21 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
                 const uint32_t rank = uint32_t(__builtin_popcount(mask & ((1u << n) - 1u)));
                 const bool st = (mask >> n) & 1u;
                 const uint32_t off = tbase[t] + (ws >> 16) * 32u + (st ? (uint32_t(q) * nz + rank) * 8u : 0u);
-                const uint2 v = *reinterpret_cast<const uint2*>(codes + off);
+                const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(codes + off));
                 d.code[t] = make_uint4(v.x, v.y, st ? 1u : 0u, 0u);
             } else if constexpr (TER) {
                 const int h = g >> 1;
                 const bool pair = h < npairs;
                 const uint8_t* base = codes + (pair ? size_t(h) * item[t] + (g & 1) * 8 : size_t(npairs) * item[t]);
-                const uint2 v = *reinterpret_cast<const uint2*>(base + (pair ? coff[t] : coff8[t]));
+                const u32x2_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x2_t*>(base + (pair ? coff[t] : coff8[t])));
                 d.code[t] = make_uint4(v.x, v.y, 0u, 0u);
             } else {
-                d.code[t] = *reinterpret_cast<const uint4*>(codes + size_t(g) * item[t] + coff[t]);
+                // codes stream once: non-temporal, so that the activations every block
+                // reads stay in L2
+                const u32x4_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(codes + size_t(g) * item[t] + coff[t]));
+                d.code[t] = make_uint4(v.x, v.y, v.z, v.w);
             }
             if constexpr (!SL) {
                 const char* sg = reinterpret_cast<const char*>(scales + g);
@@ -980,6 +985,9 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 #ifndef MBD_B1_IPW
 #define MBD_B1_IPW 4          // items per wave at least (4 KB of codes), few-row kernel
 #endif
+#ifndef MBD_B1_WAVES
+#define MBD_B1_WAVES 8192     // few-row kernel: waves a call aims for (fewer items per wave below it)
+#endif
 #ifndef MBD_B1_PF_I4
 #define MBD_B1_PF_I4 4        // INT4: items (groups, 1 KB) in flight per wave
 #endif
@@ -1005,7 +1013,7 @@ BnPlan plan_bn(bool ter, int64_t K, int64_t tiles, int NB) {
     const int64_t IG = ter ? 2 : 1;
     const int64_t ngroups = K / 128, n_items = ter ? (ngroups + 1) / 2 : ngroups;
     const int64_t max_ipw = std::max<int64_t>(1, bn_max_groups(NB, ter) / IG);
-    const int64_t fill = (tiles * n_items + 8191) / 8192;      // items per wave for ~8192 waves
+    const int64_t fill = (tiles * n_items + MBD_B1_WAVES - 1) / MBD_B1_WAVES;   // items per wave for the wave target
     int64_t ipw = std::max<int64_t>((n_items + 15) / 16, std::min<int64_t>(MBD_B1_IPW, fill));
     ipw = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(ipw, max_ipw), n_items));
     p.ipw = int(ipw);
