@@ -377,9 +377,10 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         // The odd last ternary group has 8-byte units: its 16-byte load takes the
         // unit in the low half and 8 bytes past it, which lie inside the codes
         // section or its padding (a load of one width keeps the waits exact).
-        // skip format: bits 2p, 2p + 1 of stf = slot p's two blocks are stored
+        // skip format: bits 2p, 2p + 1 of stf = slot p's two blocks are stored (for
+        // this lane's row); rmk[p] = the two blocks' stored-row masks of the tile
         uint4 w[PF];
-        uint32_t stf = 0;
+        uint32_t stf = 0, rmk[PF];
         auto issue = [&](int p, int i) __attribute__((always_inline)) {
             const int it = it0 + i;
             if constexpr (SK) {
@@ -387,11 +388,12 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
                 // (kq nz + rank) * 8; a lane whose block is not stored reads the
                 // column's first unit (in bounds: codes are padded) and drops it.
                 // The odd last column's partner is the column itself (not computed).
-                uint32_t v[4], stb = 0;
+                uint32_t v[4], stb = 0, rm = 0;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t ws = uint32_t(__builtin_amdgcn_readlane(int(sw), min(2 * i + h, ng - 1)));
                     const uint32_t mask = ws & 0xFFFFu;
+                    rm |= mask << (16 * h);
                     const uint32_t nz = uint32_t(__builtin_popcount(mask));
                     const uint32_t rank = uint32_t(__builtin_popcount(mask & ((1u << m) - 1u)));
                     const bool st = (mask >> m) & 1u;
@@ -402,6 +404,7 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
                 }
                 w[p] = make_uint4(v[0], v[1], v[2], v[3]);
                 stf = (stf & ~(3u << (2 * p))) | (stb << (2 * p));
+                rmk[p] = rm;
             } else {
                 const uint32_t off = (TER && it >= n_full) ? unit * 8 : unit * 16;
                 const u32x4_t v = __builtin_nontemporal_load(
@@ -454,7 +457,10 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         // all its lanes once they have completed
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-        auto group = [&](const uint4 gw, int lg) __attribute__((always_inline)) {
+        // rm (skip format): the group's stored-row mask; an all-zero block that is
+        // not stored gets scale 0, so that it adds exactly nothing instead of the
+        // rounding residue of its offset sums under the stored scale of 1
+        auto group = [&](const uint4 gw, int lg, uint32_t rm) __attribute__((always_inline)) {
             const char* r = rec + lg * 4 * NB * BN_REC + boff;
             f32x4_t c = *reinterpret_cast<const f32x4_t*>(r + 64);
 #pragma unroll
@@ -462,20 +468,27 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
                 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(code_operand<TER>(gw, s, kc),
                                                             *reinterpret_cast<const bf16x8_t*>(r + 16 * s), c, 0, 0, 0);
             const uint2 sc = *reinterpret_cast<const uint2*>(sct + lg * 16 + 4 * kq);
-            acc[0] = fmaf(half_bits_to_f32(uint16_t(sc.x)), c[0], acc[0]);
-            acc[1] = fmaf(half_bits_to_f32(uint16_t(sc.x >> 16)), c[1], acc[1]);
-            acc[2] = fmaf(half_bits_to_f32(uint16_t(sc.y)), c[2], acc[2]);
-            acc[3] = fmaf(half_bits_to_f32(uint16_t(sc.y >> 16)), c[3], acc[3]);
+            float s4[4] = {half_bits_to_f32(uint16_t(sc.x)), half_bits_to_f32(uint16_t(sc.x >> 16)),
+                           half_bits_to_f32(uint16_t(sc.y)), half_bits_to_f32(uint16_t(sc.y >> 16))};
+            if constexpr (SK) {
+                const uint32_t rq = rm >> (4 * kq);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s4[j] = (rq >> j) & 1u ? s4[j] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(s4[j], c[j], acc[j]);
         };
         auto compute = [&](int p, int i) __attribute__((always_inline)) {
             if constexpr (SK) {                          // not stored: code 1 (q = 0) everywhere
                 const bool s0 = (stf >> (2 * p)) & 1u, s1 = (stf >> (2 * p + 1)) & 1u;
-                group(make_uint4(s0 ? w[p].x : 0x55555555u, s0 ? w[p].y : 0x55555555u, 0u, 0u), i * IG);
+                group(make_uint4(s0 ? w[p].x : 0x55555555u, s0 ? w[p].y : 0x55555555u, 0u, 0u), i * IG,
+                      rmk[p] & 0xFFFFu);
                 if (it0 + i < n_full)
-                    group(make_uint4(s1 ? w[p].z : 0x55555555u, s1 ? w[p].w : 0x55555555u, 0u, 0u), i * IG + 1);
+                    group(make_uint4(s1 ? w[p].z : 0x55555555u, s1 ? w[p].w : 0x55555555u, 0u, 0u), i * IG + 1,
+                          rmk[p] >> 16);
             } else {
-                group(w[p], i * IG);
-                if (TER && it0 + i < n_full) group(make_uint4(w[p].z, w[p].w, 0u, 0u), i * IG + 1);
+                group(w[p], i * IG, 0u);
+                if (TER && it0 + i < n_full) group(make_uint4(w[p].z, w[p].w, 0u, 0u), i * IG + 1, 0u);
             }
         };
         int i = 0;
@@ -575,6 +588,7 @@ struct MqGroup {
                                    // path): packing them at issue would wait for the loads
     uint4 xv[4];                   // 32 activations of batch row n
     int g;                         // the group (scales from LDS)
+    uint32_t rm[MQ_TILES];         // skip format: the block column's stored-row mask per tile
 };
 
 // Scales staged in LDS per block, [group][MQ_ROWS], while they fit this budget.
@@ -705,6 +719,7 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
                 const uint32_t off = tbase[t] + (ws >> 16) * 32u + (st ? (uint32_t(q) * nz + rank) * 8u : 0u);
                 const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(codes + off));
                 d.code[t] = make_uint4(v.x, v.y, st ? 1u : 0u, 0u);
+                d.rm[t] = mask;
             } else if constexpr (TER) {
                 const int h = g >> 1;
                 const bool pair = h < npairs;
@@ -769,7 +784,9 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sc = half_bits_to_f32(uint16_t(scr[j]));
+                float sc = half_bits_to_f32(uint16_t(scr[j]));
+                // skip format: a block not stored adds exactly nothing (scale 0)
+                if constexpr (SK) sc = (d.rm[t] >> (4 * q + j)) & 1u ? sc : 0.f;
                 acc[t][j] = fmaf(sc, cg[j], acc[t][j]);
             }
         }

@@ -32,6 +32,21 @@ def rel_l2(y, ref) -> float:
     return float(np.linalg.norm(y - ref) / den) if den > 0 else float(np.linalg.norm(y))
 
 
+def worst_row(y, ref) -> float:
+    """Largest single-element error, relative to the RMS of its own output row:
+    max over b, m of |y[b][m] - ref[b][m]| / rms(ref[b]).  The whole-output rel_l2
+    spreads one wrong element over all M outputs (a factor sqrt(M) smaller); this
+    reports it at full size.  Rows whose reference is all zero are measured in
+    absolute terms."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    ref = np.atleast_2d(np.asarray(ref, dtype=np.float64))
+    y = y.reshape(-1, y.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    rms = np.sqrt(np.mean(ref * ref, axis=1))
+    err = np.abs(y - ref).max(axis=1)
+    return float(np.max(np.where(rms > 0, err / np.where(rms > 0, rms, 1.0), err)))
+
+
 def moe(deq_up: dict, deq_down: dict, routes: np.ndarray, x_bits: np.ndarray,
         a_bits: np.ndarray):
     """(y_up [T][k][M_up], y_down [T][k][M_down]) from per-expert fp64 weights."""

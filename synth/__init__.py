@@ -12,6 +12,7 @@ from .workloads import (  # noqa: F401
     gen_weight_rows,
     gen_weights,
     gen_x,
+    gen_x_outlier_channels,
     gen_act_norms,
     gen_routes,
     gen_down_inputs,

@@ -31,7 +31,7 @@ import numpy as np
 ROW_BLOCK = 512
 
 # Stream identifiers (first element of the spawn key).
-S_W, S_OUTLIER, S_X, S_NORM, S_ROUTE, S_DOWN_X, S_ZERO = 0, 1, 2, 3, 4, 5, 6
+S_W, S_OUTLIER, S_X, S_NORM, S_ROUTE, S_DOWN_X, S_ZERO, S_XCH = 0, 1, 2, 3, 4, 5, 6, 7
 
 # Fraction of all-zero 128-blocks in block-sparse ternary weights: 2 (1 - z) code
 # bits plus 0.14 bits of scales and tables gives 1.74 bits per weight, under the
@@ -140,6 +140,17 @@ def gen_x(wl: Workload, B: int, K: int | None = None) -> np.ndarray:
     """bf16 bits [B][K] of N(0, 1) activations."""
     K = wl.K if K is None else K
     x = stream(wl.seed, S_X, B).standard_normal((B, K))
+    return f32_to_bf16_bits(x.astype(np.float32))
+
+
+def gen_x_outlier_channels(seed: int, B: int, K: int, n_big: int = 8, big: float = 100.0) -> np.ndarray:
+    """bf16 bits [B][K] of activations with uneven input channels: N(0, 1) times a
+    per-channel LogNormal(0, 1) scale (the spread the activation norms have), and
+    ``n_big`` channels (distinct, seeded) ``big`` times larger still."""
+    rng = stream(seed, S_XCH, B)
+    scale = rng.lognormal(0.0, 1.0, K)
+    scale[rng.choice(K, n_big, replace=False)] *= big
+    x = rng.standard_normal((B, K)) * scale[None, :]
     return f32_to_bf16_bits(x.astype(np.float32))
 
 

@@ -1,7 +1,8 @@
 """GPU parity of the device Cassandra encoder ([Cassandra] 3.2-3.3, the online
 encoder of 3.5): all eight sections bit-exact against the oracle's packing on
-ragged shapes, keep fractions, exact score ties and special values, a restore
-of the encoded sections back to the original bits, and the error path."""
+ragged shapes, keep fractions, exact score ties and special values, the full
+4096 x 14336 workload the encoder is timed on, a restore of the encoded sections
+back to the original bits, and the error path."""
 import ctypes
 
 import numpy as np
@@ -100,6 +101,18 @@ def test_encoder_workload_rows_and_restore(dev):
     mbd.check(mbd.lib().mbd_verify_restore(ctypes.byref(d), mbd._ptr(out), None), "mbd_verify_restore")
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), w)
+
+
+def test_encoder_full_workload(dev):
+    """The whole 4096 x 14336 weight the encoder is timed on: all eight sections
+    bit-exact against the oracle's pack (matrix-global codebook ranking, u64 bit
+    offsets and kept prefixes of all 14 336 tiles)."""
+    wl = synth.WORKLOADS["cassandra_spec"]
+    w = synth.gen_weights(wl)
+    norms = synth.gen_act_norms(wl)
+    print("case encoder full 4096x14336", flush=True)
+    plan, _ = _check(dev, w, norms, (3, 10))
+    assert plan.n_kept == wl.M * cassandra.keep_count(wl.K) and plan.n_tiles == wl.M * wl.K // cassandra.TILE
 
 
 def test_encoder_rejects_nonfinite(dev):

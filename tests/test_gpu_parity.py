@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import synth
+from tests._gate import check
 from oracle import bits, cassandra, gemv, int4, mx, ternary
 
 pytestmark = pytest.mark.gpu
@@ -76,7 +77,7 @@ def test_gemv_ragged(dev, kind, M, K, B):
     ref = gemv.gemv(QUANT[kind].dequant(q, s), x)
     y = _run_gemv(dw, x, dev)
     assert np.all(np.isfinite(y))
-    assert gemv.rel_l2(y, ref) <= TOL
+    check(y, ref)
 
 
 # Batch-1 kernel variants the ragged shapes do not reach: activations staged in
@@ -98,7 +99,7 @@ def test_gemv_b1_paths(dev, kind, M, K):
                                      np.random.default_rng(M).integers(0, M, 32)]))
     q, s = QUANT[kind].quantize(w[rows])
     ref = gemv.gemv(QUANT[kind].dequant(q, s), x)
-    assert gemv.rel_l2(y[:, rows], ref) <= TOL
+    check(y[:, rows], ref)
 
 
 @pytest.mark.parametrize("kind", ["ternary", "int4"])
@@ -122,7 +123,7 @@ def test_gemv_ternary_1k_full(dev):
     dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_TERNARY_B128, w), dev)
     q, s = ternary.quantize(w)
     ref = gemv.gemv(ternary.dequant(q, s), x)
-    assert gemv.rel_l2(_run_gemv(dw, x, dev), ref) <= TOL
+    check(_run_gemv(dw, x, dev), ref)
 
 
 @pytest.fixture(scope="module")
@@ -142,9 +143,34 @@ def test_gemv_int4_8k_full(dev, int4_8k_full, B):
     x = synth.gen_x(wl, B)
     print("case int4_8k full B=%d" % B, flush=True)
     y = _run_gemv(dw, x, dev)
-    err = gemv.rel_l2(y, gemv.gemv(W, x))
-    print("int4_8k B=%d rel_l2=%.3e" % (B, err), flush=True)
+    err, worst = check(y, gemv.gemv(W, x))
+    print("int4_8k B=%d rel_l2=%.3e worst_row=%.3e" % (B, err, worst), flush=True)
     assert err <= TOL
+
+
+@pytest.fixture(scope="module")
+def ternary_8k_full(dev):
+    """An 8192 x 8192 ternary matrix (t(4) * 0.02 weights) packed once."""
+    wl = synth.WORKLOADS["ternary_moe"]
+    w = synth.f32_to_bf16_bits(synth.gen_weight_rows(wl.seed + 88, 8192, 8192, wl.dist, wl.scale).astype(np.float32))
+    dw = _mbd().to_device(_mbd().mbd_pack(_mbd().MBD_TERNARY_B128, w), dev)
+    q, s = ternary.quantize(w)
+    return wl, dw, ternary.dequant(q, s)
+
+
+# Activations whose input channels differ in size (LogNormal(0, 1) channel scales
+# and 8 channels x100, the uneven channel norms behind the Wanda score of the
+# Cassandra review, 3.2): the per-group offset sums that the kernels subtract
+# (136 sum x for INT4, the 129 / 33 / 9 weighted sums for ternary) are then
+# dominated by a few channels and must still cancel to within the gate.
+@pytest.mark.parametrize("kind", ["int4", "ternary"])
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_gemv_outlier_channels_full(dev, int4_8k_full, ternary_8k_full, kind, B):
+    wl, dw, W = int4_8k_full if kind == "int4" else ternary_8k_full
+    x = synth.gen_x_outlier_channels(wl.seed + 500 + B, B, 8192)
+    print("case outlier channels %s 8192x8192 B=%d" % (kind, B), flush=True)
+    err, worst = check(_run_gemv(dw, x, dev), gemv.gemv(W, x))
+    print("outlier channels %s B=%d rel_l2=%.3e worst_row=%.3e" % (kind, B, err, worst), flush=True)
 
 
 @pytest.fixture(scope="module")
@@ -162,8 +188,8 @@ def test_gemv_ternary_ffn_full(dev, ternary_ffn_full, B):
     wl, dw, W = ternary_ffn_full
     x = synth.gen_x(wl, B, 14336)
     print("case ternary 4096x14336 full B=%d" % B, flush=True)
-    err = gemv.rel_l2(_run_gemv(dw, x, dev), gemv.gemv(W, x))
-    print("ternary 4096x14336 B=%d rel_l2=%.3e" % (B, err), flush=True)
+    err, worst = check(_run_gemv(dw, x, dev), gemv.gemv(W, x))
+    print("ternary 4096x14336 B=%d rel_l2=%.3e worst_row=%.3e" % (B, err, worst), flush=True)
     assert err <= TOL
 
 
@@ -233,8 +259,8 @@ def test_moe_full(dev, T, which):
     for t in range(T):
         for j in range(wl.topk):
             ref[t, j] = deq[int(routes[t, j])] @ (xv[t * wl.topk + j] if per_pair else xv[t])
-    err = gemv.rel_l2(y.cpu().numpy(), ref)
-    print("moe T=%d %s rel_l2=%.3e" % (T, which, err), flush=True)
+    err, worst = check(y.cpu().numpy(), ref)
+    print("moe T=%d %s rel_l2=%.3e worst_row=%.3e" % (T, which, err, worst), flush=True)
     assert err <= TOL
 
 
@@ -285,8 +311,8 @@ def test_moe_ragged(dev, case):
     assert np.isnan(got[T // 2, k - 1]).all()
     got[T // 2, k - 1] = 0.0
     assert not np.isnan(got).any()
-    err = gemv.rel_l2(got, ref)
-    print("moe ragged rel_l2=%.3e" % err, flush=True)
+    err, worst = check(got, ref)
+    print("moe ragged rel_l2=%.3e worst_row=%.3e" % (err, worst), flush=True)
     assert err <= TOL
 
 
@@ -323,14 +349,14 @@ def _check_cassandra(dev, w, norms, keep, batches, verify_batches):
         if not ref.any():
             assert not got.any()
         else:
-            assert gemv.rel_l2(got, ref) <= TOL, B
+            check(got, ref, what=str(B))
     if K % 4096 == 0:
         for B in verify_batches:
             x = _rand_x(B + 50, B, K)
             y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
             mbd.mbd_gemv(cw, _x_dev(x, dev), y)
             torch.cuda.synchronize()
-            assert gemv.rel_l2(y.cpu().numpy(), gemv.gemv(bits.bf16_value(w), x)) <= TOL, B
+            check(y.cpu().numpy(), gemv.gemv(bits.bf16_value(w), x), what=str(B))
 
 
 CAS_SHAPES = [(1, 4096), (2, 1536), (5, 1000 - 1000 % 128 + 128), (3, 14336), (7, 8192), (33, 384)]
@@ -360,14 +386,14 @@ def test_cassandra_decode_ragged(dev, M, K):
         mbd.mbd_spec_gemv(sw, _x_dev(x, dev), y)
         torch.cuda.synchronize()
         ref = gemv.gemv(bits.bf16_value(spec), x)
-        assert gemv.rel_l2(y.cpu().numpy(), ref) <= TOL
+        check(y.cpu().numpy(), ref)
     if K % 4096 == 0:
         for B in (1, 7):
             x = _rand_x(B + 9, B, K)
             y = torch.full((B, M), float("nan"), dtype=torch.float32, device=dev)
             mbd.mbd_gemv(cw, _x_dev(x, dev), y)
             torch.cuda.synchronize()
-            assert gemv.rel_l2(y.cpu().numpy(), gemv.gemv(bits.bf16_value(w), x)) <= TOL
+            check(y.cpu().numpy(), gemv.gemv(bits.bf16_value(w), x))
 
 
 @pytest.mark.parametrize("M,K,keep", [(4, 4096, (1, 1)), (3, 8192, (0, 1)), (5, 12288, (1, 2)), (17, 4096, (3, 10)),
@@ -416,8 +442,8 @@ def test_cassandra_spec_full(dev, spec_full):
     y = torch.empty((1, M), dtype=torch.float32, device=dev)
     mbd.mbd_spec_gemv(sw, _x_dev(x, dev), y)
     torch.cuda.synchronize()
-    err = gemv.rel_l2(y.cpu().numpy(), gemv.gemv(bits.bf16_value(expect), x))
-    print("cassandra spec gemv rel_l2=%.3e" % err, flush=True)
+    err, worst = check(y.cpu().numpy(), gemv.gemv(bits.bf16_value(expect), x))
+    print("cassandra spec gemv rel_l2=%.3e worst_row=%.3e" % (err, worst), flush=True)
     assert err <= TOL
 
 
@@ -444,8 +470,8 @@ def test_cassandra_verify_full(dev, verify_full):
     mbd.mbd_gemv(cw, _x_dev(x, dev), y)
     torch.cuda.synchronize()
     ref = gemv.gemv(bits.bf16_value(w), x)
-    err = gemv.rel_l2(y.cpu().numpy(), ref)
-    print("cassandra verify gemm rel_l2=%.3e" % err, flush=True)
+    err, worst = check(y.cpu().numpy(), ref)
+    print("cassandra verify gemm rel_l2=%.3e worst_row=%.3e" % (err, worst), flush=True)
     assert err <= TOL
 
 
@@ -477,8 +503,8 @@ def test_cassandra_draft_verify_step(dev):
         spec = np.where(cassandra.keep_mask(w, norms), w & 0xFFF0, 0).astype(np.uint16)
         for t in range(N):
             x = xs[l * N + t:l * N + t + 1]
-            assert gemv.rel_l2(yd[l, t].cpu().numpy(), gemv.gemv(bits.bf16_value(spec), x)) <= TOL
-        assert gemv.rel_l2(Y[l].cpu().numpy(), gemv.gemv(bits.bf16_value(w), X)) <= TOL
+            check(yd[l, t].cpu().numpy(), gemv.gemv(bits.bf16_value(spec), x))
+        check(Y[l].cpu().numpy(), gemv.gemv(bits.bf16_value(w), X))
 
 
 def test_mx_full(dev, verify_full):
@@ -491,8 +517,8 @@ def test_mx_full(dev, verify_full):
     torch.cuda.synchronize()
     sec = mx.encode(w)
     ref = gemv.gemv(mx.value(sec, M, K), x)
-    err = gemv.rel_l2(y.cpu().numpy(), ref)
-    print("mx gemm rel_l2=%.3e" % err, flush=True)
+    err, worst = check(y.cpu().numpy(), ref)
+    print("mx gemm rel_l2=%.3e worst_row=%.3e" % (err, worst), flush=True)
     assert err <= TOL
 
 
@@ -511,7 +537,7 @@ def test_mx_ragged_and_dequant(dev, M, K, B):
     y = torch.empty((B, M), dtype=torch.float32, device=dev)
     mbd.mbd_gemv(dw, _x_dev(x, dev), y)
     torch.cuda.synchronize()
-    assert gemv.rel_l2(y.cpu().numpy(), gemv.gemv(mx.value(sec, M, K), x)) <= TOL
+    check(y.cpu().numpy(), gemv.gemv(mx.value(sec, M, K), x))
 
 
 def test_verify_gemm_needs_tile_aligned_k(dev):
@@ -550,4 +576,4 @@ def test_gemv_random_shapes(dev, kind, M, K, B):
     q, s = QUANT[kind].quantize(w)
     y = _run_gemv(dw, x, dev)
     assert np.all(np.isfinite(y))
-    assert gemv.rel_l2(y, gemv.gemv(QUANT[kind].dequant(q, s), x)) <= TOL
+    check(y, gemv.gemv(QUANT[kind].dequant(q, s), x))

@@ -3,6 +3,7 @@ agreement at size, and the MoE routing definition."""
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import synth
 from oracle import bits, gemv, ternary
@@ -58,3 +59,21 @@ def test_moe_definition_small():
 def test_rel_l2():
     assert gemv.rel_l2([1.0, 0.0], [1.0, 0.0]) == 0.0
     assert abs(gemv.rel_l2([1.0, 1.0], [1.0, 0.0]) - 1.0) < 1e-15
+
+
+def test_worst_row():
+    ref = np.array([[3.0, 4.0, 0.0, 0.0], [1.0, 1.0, 1.0, 1.0]])   # row RMS 2.5 and 1
+    assert gemv.worst_row(ref, ref) == 0.0
+    y = ref.copy()
+    y[0, 2] += 0.5                                                  # 0.5 / 2.5
+    assert gemv.worst_row(y, ref) == pytest.approx(0.2, abs=1e-15)
+    y[1, 3] -= 0.3                                                  # 0.3 / 1 dominates
+    assert gemv.worst_row(y, ref) == pytest.approx(0.3, abs=1e-15)
+    assert gemv.worst_row([[0.0, 0.25]], [[0.0, 0.0]]) == 0.25    # all-zero row: absolute
+    # one wrong element among many: rel_l2 dilutes it by sqrt(M), worst_row does not
+    M = 8192
+    ref = np.ones((1, M))
+    y = ref.copy()
+    y[0, 17] += 0.05
+    assert gemv.rel_l2(y, ref) == pytest.approx(0.05 / np.sqrt(M), rel=1e-12)
+    assert gemv.worst_row(y, ref) == pytest.approx(0.05, rel=1e-12)

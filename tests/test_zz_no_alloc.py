@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import synth
+from tests._gate import check
 from oracle import bits, gemv, int4, ternary
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +70,6 @@ def test_noalloc_matches_workspace_entry(dev, kind):
             xv = bits.bf16_value(xb)
             ref = np.stack([[deq[routes[t, j]] @ (xv[t * k + j] if per_pair else xv[t]) for j in range(k)]
                             for t in range(T)])
-            err = gemv.rel_l2(b.astype(np.float64), ref)
-            print("noalloc %s T=%d rel_l2=%.3e" % (kind, T, err), flush=True)
+            err, worst = check(b.astype(np.float64), ref)
+            print("noalloc %s T=%d rel_l2=%.3e worst_row=%.3e" % (kind, T, err, worst), flush=True)
             assert err <= 1e-3
