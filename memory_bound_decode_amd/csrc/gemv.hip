@@ -59,21 +59,25 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
 
 // Masks used by the unpackers, held in registers.
 struct UnpackConsts {
-    uint32_t magic, m2a, m2b, m2c, m4;
+    uint32_t magic, mg1, mg2, m2a, m2b, m2c, m4;
     __device__ __forceinline__ void init() {
         magic = 0x43004300u;   // bf16 128.0 in both halves
+        mg1 = 0x42004200u;     // bf16 32.0
+        mg2 = 0x41004100u;     // bf16 8.0
         m2a = 0x00030003u; m2b = 0x000C000Cu; m2c = 0x00300030u;
         m4 = 0x000F000Fu;
         // an opaque copy keeps them in VGPRs instead of being folded back into literals
-        asm volatile("" : "+v"(magic), "+v"(m2a), "+v"(m2b), "+v"(m2c), "+v"(m4));
+        asm volatile("" : "+v"(magic), "+v"(mg1), "+v"(mg2), "+v"(m2a), "+v"(m2b), "+v"(m2c), "+v"(m4));
     }
 };
 
 // A operand of MFMA step s (0..3) from the words of one scale group: INT4 words
 // x, y, z, w (step s = word s, 8 codes), ternary words x, y (step s = half s % 2
 // of word s / 2).  Ternary pair p of a word is read at mantissa bits 2 (p % 3)
-// after a shift by 6 (p / 3): value 128 + c 4^(p % 3), matched by activations
-// divided by 4^(p % 3).
+// after a shift by 6 (p / 3), under an exponent that makes the field's unit 1:
+// class p % 3 = 0, 1, 2 gives 128 + c, 32 + c, 8 + c (bf16 128, 32, 8 with the
+// field at mantissa bits 0, 2, 4), so the activations stay as they are and only
+// the constant part differs by class: 129, 33, 9 times x for q = c - 1.
 template <bool TER>
 __device__ __forceinline__ bf16x8_t code_operand(const uint4 c, int s, const UnpackConsts& k) {
     uint32_t o[4];
@@ -82,14 +86,14 @@ __device__ __forceinline__ bf16x8_t code_operand(const uint4 c, int s, const Unp
         const uint32_t s6 = v >> 6, s12 = v >> 12;
         if ((s & 1) == 0) {
             o[0] = and_or(v, k.m2a, k.magic);
-            o[1] = and_or(v, k.m2b, k.magic);
-            o[2] = and_or(v, k.m2c, k.magic);
+            o[1] = and_or(v, k.m2b, k.mg1);
+            o[2] = and_or(v, k.m2c, k.mg2);
             o[3] = and_or(s6, k.m2a, k.magic);
         } else {
-            o[0] = and_or(s6, k.m2b, k.magic);
-            o[1] = and_or(s6, k.m2c, k.magic);
+            o[0] = and_or(s6, k.m2b, k.mg1);
+            o[1] = and_or(s6, k.m2c, k.mg2);
             o[2] = and_or(s12, k.m2a, k.magic);
-            o[3] = and_or(s12, k.m2b, k.magic);
+            o[3] = and_or(s12, k.m2b, k.mg1);
         }
     } else {
         const uint32_t v = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
@@ -264,15 +268,13 @@ __global__ __launch_bounds__(1024) void moe_group_kernel(const int* __restrict__
 // groups; ternary: group pairs), in rounds when K is long.  Each wave stages
 // what its own items need in its own LDS area, so no wave waits for another
 // before computing:
-//   rec[g][kq][t]  80 bytes: activations of row t, columns [128g + 32kq, +32)
-//                  (ternary: divided by 4^class, exact, so that one accumulator
-//                  covers the three position classes of the unpack) and the
-//                  group's -bias of row t four times, the initial C values of
-//                  the group's MFMA chain;
+//   rec[g][kq][t]  80 bytes: activations of row t, columns [128g + 32kq, +32),
+//                  and the group's -bias of row t four times, the initial C
+//                  values of the group's MFMA chain;
 //   sct[g][16]     the tile's fp16 scales of group g.
 // bias = sum over the group of (code value - q) x: 136 sum x for INT4 (code value
-// q + 136), sum (1 + 128 / 4^class) x for ternary (code value 128 + (q + 1) 4^class
-// against x / 4^class).  The waves' partial rows meet in LDS at the end.
+// q + 136), sum (1 + 128 / 4^class) x for ternary (code value 128 / 4^class + q + 1,
+// class 0, 1, 2: 129, 33, 9).  The waves' partial rows meet in LDS at the end.
 constexpr int BN_REC = 80;
 
 // Groups one wave stages per round: at most 8, and at most 16 / NB so that the
@@ -427,16 +429,13 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
                 for (int jj = 0; jj < 4; ++jj) {
                     if constexpr (TER) {
                         // columns 8 sl + 2jj, +1 (a quarter starts on a word boundary): pair
-                        // (4 sl + jj) % 8 of a 16-code word, class pair % 3, weight 1 + 128 / 4^class
+                        // (4 sl + jj) % 8 of a 16-code word, class pair % 3, constant part
+                        // 129, 33, 9 (exact in bf16)
                         const int ce = jj % 3, co = (4 + jj) % 3;    // class for an even / odd slice
-                        const bool odd = sl & 1;
-                        const uint32_t wpair = odd ? (co == 0 ? 0x43014301u : co == 1 ? 0x42044204u : 0x41104110u)
-                                                   : (ce == 0 ? 0x43014301u : ce == 1 ? 0x42044204u : 0x41104110u);
-                        const float f = odd ? (co == 0 ? 1.f : co == 1 ? 0.25f : 0.0625f)
-                                            : (ce == 0 ? 1.f : ce == 1 ? 0.25f : 0.0625f);
-                        part = dot2(v4[jj], wpair, part);    // 129, 33, 9 are exact in bf16
-                        const float lo = bf16_to_f32(v4[jj] & 0xFFFFu) * f, hi = bf16_to_f32(v4[jj] >> 16) * f;
-                        xo[jj] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+                        const uint32_t wpair = (sl & 1) ? (co == 0 ? 0x43014301u : co == 1 ? 0x42044204u : 0x41104110u)
+                                                        : (ce == 0 ? 0x43014301u : ce == 1 ? 0x42044204u : 0x41104110u);
+                        part = dot2(v4[jj], wpair, part);
+                        xo[jj] = v4[jj];
                     } else {
                         part = dot2(v4[jj], 0x3F803F80u, part);    // (1.0, 1.0)
                         xo[jj] = v4[jj];
@@ -552,9 +551,10 @@ __global__ __launch_bounds__(1024) void moe_b1_kernel(BnArgs a) {
 // become bf16 MFMA operands directly, and the activations are read per group
 // straight from memory (no staging).
 // A code c of a pair-friendly word, OR'ed into the bf16 pattern of 128, is the
-// exact value 128 + c = q + K0 (K0 = 136 for INT4, 129 for ternary), so
-// v_mfma_f32_16x16x32_bf16 over one 128-column scale group gives
-// sum (q + K0) x; subtracting K0 * sum x and applying the group's fp16 scale
+// exact value 128 + c = q + K0 (K0 = 136 for INT4; ternary 129, 33 or 9 by
+// position class, see code_operand), so v_mfma_f32_16x16x32_bf16 over one
+// 128-column scale group gives sum (q + K0) x; subtracting sum K0 x and applying
+// the group's fp16 scale
 // once per group gives the dequantized dot product.  A block is 32 rows (two
 // 16-row tiles) by all of K; its waves take the 128-column groups round robin,
 // with the next group's loads in flight while one is computed, and the waves'
@@ -625,20 +625,12 @@ struct MqArgs {
     int by_expert;          // block index = expert * row_blocks + row block (route set)
 };
 
-// A operand of MFMA step s from the lane's codes of one group, every pair shifted
-// to mantissa bits 0.. (value q + K0): the activations here are the raw rows.
-template <bool TER>
-__device__ __forceinline__ bf16x8_t mq_operand(const uint4 c, int s, const UnpackConsts& k) {
-    if constexpr (TER) {
-        const uint32_t w = (s < 2) ? c.x : c.y;        // 16 codes per word
-        const int p0 = 4 * (s & 1);
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) o[p] = and_or(w >> (2 * (p0 + p)), k.m2a, k.magic);
-        return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-    } else {
-        return code_operand<false>(c, s, k);           // INT4 fields already sit at bit 0 after the shift
-    }
+// Ternary constant part of step s's k slots (negated, bf16 pairs): slot pair p of
+// the step is word pair 4 (s % 2) + p, of class (4 (s % 2) + p) % 3 (the classes
+// of code_operand): -129, -33 or -9.
+__device__ __forceinline__ uint32_t ter_nk0(int s, int p) {
+    const int cl = (4 * (s & 1) + p) % 3;
+    return cl == 0 ? 0xC301C301u : cl == 1 ? 0xC204C204u : 0xC110C110u;
 }
 
 // Rows [row_base, row_base + MQ_ROWS) of one matrix; nb <= 16 batch rows whose
@@ -750,19 +742,27 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     for (int t = 0; t < MQ_TILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // Lanes n >= nb carry batch row 0's activations: B column n only reaches
     // output column n, which is not stored.
-    // -K0 sum x per batch column, on the matrix cores: A = -K0 everywhere (exact in
-    // bf16) against the group's activations puts -K0 sum_k x[n][k] in every row of
-    // column n; each tile's chain starts from it.
+    // -sum K0 x per batch column, on the matrix cores: A = -K0 of each k slot in
+    // every row (exact in bf16) against the group's activations puts
+    // -sum_k K0_k x[n][k] in every row of column n; each tile's chain starts from it.
     UnpackConsts kc;
     kc.init();
-    const uint32_t nk0 = TER ? 0xC301C301u : 0xC308C308u;   // bf16 -129 / -136, twice
-    const bf16x8_t ak0 = __builtin_bit_cast(bf16x8_t, make_uint4(nk0, nk0, nk0, nk0));
+    // A of the constant-part MFMAs: INT4 -136 everywhere; ternary by position class
+    // (even / odd steps)
+    auto nk_operand = [](int s) __attribute__((always_inline)) {
+        if constexpr (TER) {
+            return __builtin_bit_cast(bf16x8_t, make_uint4(ter_nk0(s, 0), ter_nk0(s, 1), ter_nk0(s, 2), ter_nk0(s, 3)));
+        } else {
+            return __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
+        }
+    };
+    const bf16x8_t ak0 = nk_operand(0), ak1 = nk_operand(1);
     auto compute = [&](const MqGroup& d) {
         const uint4* xb = d.xv;
         f32x4_t cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak0, __builtin_bit_cast(bf16x8_t, xb[s]), cb, 0, 0, 0);
+            cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s & 1 ? ak1 : ak0, __builtin_bit_cast(bf16x8_t, xb[s]), cb, 0, 0, 0);
 #pragma unroll
         for (int t = 0; t < MQ_TILES; ++t) {
             f32x4_t cg = cb;
@@ -772,7 +772,7 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mq_operand<TER>(cw, s, kc),
+                cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(code_operand<TER>(cw, s, kc),
                                                              __builtin_bit_cast(bf16x8_t, xb[s]), cg, 0, 0, 0);
             uint32_t scr[4];
             if constexpr (SL) {
