@@ -358,7 +358,7 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         // e / 16, tile row e % 16).
         // at most 8 groups x 16 rows of scales: two passes
         constexpr int SU = XU < 2 ? XU : 2;
-        const float inv_ng = 1.f / float(ng);
+        const float inv_ng = NB == 1 ? 0.f : 1.f / float(ng);
         uint4 xv[XU];
         int jr[XU], se[SU];                  // jr: record byte offset * 4 + slice
         uint32_t sv[SU];
@@ -366,7 +366,7 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         for (int u = 0; u < XU; ++u) {
             const int j = min(lane + 64 * u, njobs - 16 + (lane & 15));
             const int gt = j >> 4;
-            const int t = int((float(gt) + 0.5f) * inv_ng);   // gt / ng, exact for gt < 128
+            const int t = NB == 1 ? 0 : int((float(gt) + 0.5f) * inv_ng);   // gt / ng, exact for gt < 128
             const int gl = gt - t * ng, q = (j >> 2) & 3, sl = j & 3;
             jr[u] = (((gl * 4 + q) * NB + t) * BN_REC) * 4 + sl;
             xv[u] = *reinterpret_cast<const uint4*>(xrow(t) + (g0 + gl) * 128 + q * 32 + sl * 8);
