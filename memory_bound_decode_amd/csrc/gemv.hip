@@ -10,10 +10,11 @@
 // shift) yields an element pair, and four pairs are one lane's MFMA A operand.
 // The constant part of the code values ("bias": K0 sum x over a scale group) is
 // removed once per group, and the group's fp16 scale applied once per group.
-// On a 16-lane SIMD a wave64 VALU op takes 4 clocks: a dot2 formulation (one op
-// per weight pair on top of the unpack) costs about as many SIMD clocks as HBM
-// needs to deliver the bytes it consumes, so even batch 1 uses the matrix cores
-// and leaves only the unpack on the VALU.
+// On a 16-lane SIMD a wave64 VALU op takes 4 clocks, and these kernels are bound
+// by VALU issue and latency: a dot2 formulation would add one op per weight pair
+// to the unpack (16 wave ops per KB of INT4 codes, 32 per KB of ternary, on top
+// of about 60 and 90), while the matrix cores are a separate pipe, so even batch
+// 1 uses them and leaves only the unpack on the VALU.
 //
 // Codes are stored tile-interleaved (include/mbd.h): for each 16-row tile and
 // 128-column group (ternary: pair of groups), lane l = 16 kq + m of a wave finds
