@@ -1124,15 +1124,20 @@ __global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const 
                                                            __builtin_bit_cast(bf16x8_t, bv), accB, 0, 0, 0);
         }
     };
-    // two chunk buffers, so a buffer is never copied while its loads are in flight
+    // two chunk buffers, so a buffer is never copied while its loads are in flight;
+    // the scheduling fences keep each chunk's loads issued before the other
+    // chunk's compute (left to itself the compiler sinks them below it, and the
+    // wave then has one chunk in flight instead of two)
     MxChunk c0, c1;
     int c = wave;
     if (c < nchunks) load(c, c0);
     for (; c < nchunks; c += 2 * MX_WAVES) {
         const int cn = c + MX_WAVES;
         load(min(cn, nchunks - 1), c1);
+        __builtin_amdgcn_sched_barrier(0);
         compute(c, c0);
         load(min(cn + MX_WAVES, nchunks - 1), c0);
+        __builtin_amdgcn_sched_barrier(0);
         if (cn < nchunks) compute(cn, c1);
     }
 #pragma unroll
