@@ -813,6 +813,9 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
         for (int p = 0; p < MQ_DEPTH; ++p) {
             const int ln = min(i + p + MQ_DEPTH - 1, cnt - 1);
             load(ln, gidx(ln), gb[(p + MQ_DEPTH - 1) % MQ_DEPTH]);
+            // the loads go out before this group's compute (left to itself the
+            // compiler sinks them below it, and no load overlaps any compute)
+            __builtin_amdgcn_sched_barrier(0);
             if (i + p < cnt) compute(gb[p]);
         }
     }
