@@ -471,7 +471,9 @@ def time_workload(wl, steps, warmup, use_graph=None):
         for i in range(warmup):
             wl.launch(i)
         host_us = (time.perf_counter() - t0) * 1e6 / max(1, warmup)
-        hold_us = 400.0 + 2.0 * host_us * steps
+        # a wide margin: the host can queue more slowly during the timed loop than
+        # during the warm-up, and a GPU that catches up with it times the gaps
+        hold_us = 1000.0 + 4.0 * host_us * steps
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
