@@ -360,20 +360,30 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
         // at most 8 groups x 16 rows of scales: two passes
         constexpr int SU = XU < 2 ? XU : 2;
         const float inv_ng = NB == 1 ? 0.f : 1.f / float(ng);
+        (void)inv_ng;
         uint4 xv[XU];
         int jr[XU], se[SU];                  // jr: record byte offset * 4 + slice
         uint32_t sv[SU];
 #pragma unroll
         for (int u = 0; u < XU; ++u) {
             const int j = min(lane + 64 * u, njobs - 16 + (lane & 15));
-            const int gt = j >> 4;
-            const int t = NB == 1 ? 0 : int((float(gt) + 0.5f) * inv_ng);   // gt / ng, exact for gt < 128
-            const int gl = gt - t * ng, q = (j >> 2) & 3, sl = j & 3;
-            jr[u] = (((gl * 4 + q) * NB + t) * BN_REC) * 4 + sl;
-            xv[u] = *reinterpret_cast<const uint4*>(xrow(t) + (g0 + gl) * 128 + q * 32 + sl * 8);
+            if constexpr (NB == 1) {
+                // job j = 16 gl + 4 q + sl: columns 8 j .. +8 of the round's groups,
+                // record gl 4 + q (80 bytes each), slice sl
+                jr[u] = (j >> 2) * (BN_REC * 4) + (j & 3);
+                xv[u] = *reinterpret_cast<const uint4*>(xrow(0) + (g0 * 128 + 8 * j));
+            } else {
+                const int gt = j >> 4;
+                const int t = int((float(gt) + 0.5f) * inv_ng);   // gt / ng, exact for gt < 128
+                const int gl = gt - t * ng, q = (j >> 2) & 3, sl = j & 3;
+                jr[u] = (((gl * 4 + q) * NB + t) * BN_REC) * 4 + sl;
+                xv[u] = *reinterpret_cast<const uint4*>(xrow(t) + (g0 + gl) * 128 + q * 32 + sl * 8);
+            }
             if (u < SU) {
                 se[u] = min(lane + 64 * u, 16 * ng - 1);
-                sv[u] = scales[size_t(row0 + min(se[u] & 15, R - 1)) * ngroups + g0 + (se[u] >> 4)];
+                // 32-bit element offset: a matrix's codes stay under 4 GiB (every entry
+                // point checks it), so M K / 128 < 2^27
+                sv[u] = scales[uint32_t((row0 + min(se[u] & 15, R - 1)) * ngroups + g0 + (se[u] >> 4))];
             }
         }
 
@@ -1238,16 +1248,25 @@ namespace {
 
 // The expert GEMV behind both entry points; ws is device memory of ws_bytes bytes
 // (the caller's workspace, or this device's static scratch).
-mbd_status moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
-                    int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
-    if (!w || !route || !x || !y || !ws) return fail(MBD_EINVAL, "NULL argument");
+// The expert GEMV's checks of the weights and shape, made before any HIP call.
+mbd_status moe_check(const mbd_dweights* w) {
     if (w->fmt != MBD_TERNARY_B128 && w->fmt != MBD_INT4_G128)
         return fail(MBD_EINVAL, "expert GEMV supports TERNARY and INT4");
     if (w->M < 1 || w->K < 128 || w->K % 128 || w->M > INT32_MAX || w->K > INT32_MAX)
         return fail(MBD_ESHAPE, "bad expert shape");
-    uint64_t need = 0;
-    mbd_status s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need);
+    // the kernels address one matrix's codes and scales with 32-bit offsets
+    if (w->M * (w->K / (w->fmt == MBD_TERNARY_B128 ? 4 : 2)) >= (int64_t(1) << 32))
+        return fail(MBD_ESHAPE, "expert codes beyond 4 GiB");
+    return MBD_OK;
+}
+
+mbd_status moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
+                    int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
+    if (!w || !route || !x || !y || !ws) return fail(MBD_EINVAL, "NULL argument");
+    mbd_status s = moe_check(w);
     if (s != MBD_OK) return s;
+    uint64_t need = 0;
+    if ((s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need)) != MBD_OK) return s;
     if (ws_bytes < need) return fail(MBD_EINVAL, "workspace of %llu bytes, need %llu", (unsigned long long)ws_bytes, (unsigned long long)need);
     if (!aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 16) || !aligned(route, 4) ||
         !aligned(w->sec[0], 16) || !aligned(w->sec[1], 2))
@@ -1363,9 +1382,10 @@ mbd_status mbd_moe_gemv_noalloc(const mbd_dweights* w, const int32_t* route, int
                                 const uint16_t* x, int32_t x_per_pair, float* y, void* stream) {
     hip_clear();
     if (!w || !route || !x || !y) return fail(MBD_EINVAL, "NULL argument");
-    uint64_t need = 0;
-    mbd_status s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need);
+    mbd_status s = moe_check(w);
     if (s != MBD_OK) return s;
+    uint64_t need = 0;
+    if ((s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need)) != MBD_OK) return s;
     if (need > kMoeScratchBytes)
         return fail(MBD_ESHAPE, "route of %d x %d pairs over %lld experts needs %llu bytes of scratch, above the "
                     "library's %llu", T, k, (long long)w->n_mats, (unsigned long long)need,

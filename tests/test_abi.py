@@ -240,3 +240,10 @@ def test_moe_noalloc_argument_errors(L):
     assert L.mbd_moe_gemv_noalloc(ctypes.byref(e), P16, T_big, 8, P16, 0, P16, None) == mbd.MBD_ESHAPE
     assert b"scratch" in L.mbd_last_error()
     assert L.mbd_moe_gemv_noalloc(ctypes.byref(e), P16, 2, 0, P16, 0, P16, None) == mbd.MBD_ESHAPE   # k = 0
+    # one expert matrix's codes and scales are addressed with 32-bit offsets: 4 GiB of
+    # codes per matrix is refused, on both entry points
+    big = _desc(mbd.MBD_INT4_G128, 1 << 20, 8192, n_mats=2)
+    assert L.mbd_moe_gemv_noalloc(ctypes.byref(big), P16, 1, 2, P16, 0, P16, None) == mbd.MBD_ESHAPE
+    assert b"4 GiB" in L.mbd_last_error()
+    assert L.mbd_moe_gemv(ctypes.byref(big), P16, 1, 2, P16, 0, P16, P16, 1 << 20, None) == mbd.MBD_ESHAPE
+    assert b"4 GiB" in L.mbd_last_error()
