@@ -273,14 +273,21 @@ __global__ __launch_bounds__(NT) void enc_rowbits_kernel(EncArgs a) {
     rk[t] = a.rank_of[t];
     __syncthreads();
     const int64_t r = blockIdx.x;
-    const int nwords = int(a.K / 32), wpt = (nwords + NT - 1) / NT;
-    const int w0 = min(nwords, t * wpt), w1 = min(nwords, w0 + wpt);
-    const uint16_t* wr = a.w + r * a.K;
+    // The row's sum does not depend on the order, so thread t takes the 8-value
+    // chunks t, t + NT, ...: one 16-byte load of the row (consecutive threads,
+    // consecutive chunks) and the chunk's bitmap byte (bit i = value 8c + i).
+    // Rows start 16-byte aligned (w is, and K is a multiple of 128).
+    const int nch = int(a.K / 8);
+    const uint4* wr = reinterpret_cast<const uint4*>(a.w + r * a.K);
+    const uint8_t* bm = reinterpret_cast<const uint8_t*>(a.bitmap + (r * a.K) / 32);
     uint64_t b = 0;
-    for (int wd = w0; wd < w1; ++wd) {
-        const uint32_t bm = a.bitmap[(r * a.K) / 32 + wd];
-        for (int i = 0; i < 32; ++i)
-            if ((bm >> i) & 1u) b += rk[(wr[32 * wd + i] >> 7) & 0xFF] + 1;
+    for (int c = t; c < nch; c += NT) {
+        const uint32_t m = bm[c];
+        const uint4 v = wr[c];
+        const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if ((m >> i) & 1u) b += rk[(e[i >> 1] >> (16 * (i & 1) + 7)) & 0xFFu] + 1;
     }
     uint64_t total;
     block_excl_scan<uint64_t>(b, scan, &total);
