@@ -114,8 +114,14 @@ constexpr int NS = 512;                 // threads per row in the selection
 // Sum of v over the workgroup (NS threads); `slot` alternates between calls so
 // that one barrier per call suffices.
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t (*part)[NS / 64], int slot) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    // 16-lane row sums with DPP moves (no LDS round trips), then the four rows'
+    // sums from lanes 0, 16, 32, 48
+    v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
+    v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+    v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x141, 0xF, 0xF, true));   // row_half_mirror
+    v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x140, 0xF, 0xF, true));   // row_mirror
+    v = uint32_t(__builtin_amdgcn_readlane(int(v), 0)) + uint32_t(__builtin_amdgcn_readlane(int(v), 16)) +
+        uint32_t(__builtin_amdgcn_readlane(int(v), 32)) + uint32_t(__builtin_amdgcn_readlane(int(v), 48));
     if ((threadIdx.x & 63) == 0) part[slot][threadIdx.x >> 6] = v;
     __syncthreads();
     uint32_t s = 0;
