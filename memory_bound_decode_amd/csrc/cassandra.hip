@@ -306,6 +306,12 @@ __global__ __launch_bounds__(256) void spec_gemv_kernel(CasArgs a, const uint16_
 // walk with the words read from memory and a linear start search.
 
 constexpr int STAGE_UW = 128;   // unary words staged per wave
+// Tile flags from the staging (wave-uniform): a cursor's loop over empty words
+// runs only in tiles that have such a word (codewords end within the next word and
+// bitmap words hold both kinds of bit almost always).
+constexpr uint32_t GAP_UNARY = 1;  // a unary word without a one bit, or the words are not staged
+constexpr uint32_t GAP_EMPTY = 2;  // a bitmap word without a kept position
+constexpr uint32_t GAP_FULL = 4;   // a bitmap word without a pruned position
 constexpr int NIB_CHUNK = 32;   // kept values per aligned nibble window (128 bits)
 constexpr int GRP = 4;          // kept values decoded before their LDS reads are issued
 constexpr int PRU_CHUNK = 32;   // pruned values per aligned register window
@@ -366,8 +372,9 @@ __device__ __forceinline__ int select32(uint32_t w, int r) {
     return pos;
 }
 
-// Cursor over the tile's unary codewords.
-template <bool FAST>
+// Cursor over the tile's unary codewords.  GAPS: the tile may hold a staged word
+// without a one bit (a codeword longer than 32 bits), so a refill may loop.
+template <bool FAST, bool GAPS = true>
 struct UnaryCursor {
     int k;          // current word
     uint32_t cw;    // its unconsumed bits
@@ -407,11 +414,13 @@ struct UnaryCursor {
     __device__ __forceinline__ int next(const CasArgs& a, const TileHdr& h, const WaveArea& W) {
         if constexpr (FAST) {
             // branch-free refill from the word read ahead; a further empty word
-            // (a codeword longer than 32 bits) takes the loop
+            // (a codeword longer than 32 bits) takes the loop, in tiles flagged at
+            // staging only
             const bool e = cw == 0;
             cw = e ? nx : cw;
             k += e;
-            while (cw == 0) cw = word(a, h, W, ++k);
+            if constexpr (GAPS)
+                while (cw == 0) cw = word(a, h, W, ++k);
             nx = W.uw[k + 1];
         } else {
             while (cw == 0) cw = word(a, h, W, ++k);
@@ -425,8 +434,8 @@ struct UnaryCursor {
 };
 
 // Cursor over set bits (kept positions) or clear bits (pruned positions) of the
-// tile's bitmap.
-template <bool ZEROS>
+// tile's bitmap.  GAPS: the tile may hold a word without a bit of the walked kind.
+template <bool ZEROS, bool GAPS = true>
 struct BitCursor {
     int k;
     uint32_t cw;
@@ -458,7 +467,8 @@ struct BitCursor {
         const bool e = cw == 0;              // branch-free refill; a further empty word loops
         cw = e ? nx : cw;
         k += e;
-        while (cw == 0) cw = word(W, ++k);
+        if constexpr (GAPS)
+            while (cw == 0) cw = word(W, ++k);
         nx = word(W, k + 1);
         const int pos = 32 * k + __builtin_ctz(cw);
         cw &= cw - 1u;
@@ -484,11 +494,11 @@ __device__ __forceinline__ void nib_align(const uint32_t (&raw)[5], int64_t n, u
 // sink.stage(u, rank, spec_nib, lo_nib) for each value of the group (u = its
 // slot), sink.skip(u) for slots past the lane's count, then sink.commit().  The
 // first nibble windows (nibble kp0 + j0) come preloaded.
-template <bool FAST, bool LO, class Sink>
+template <bool FAST, bool LO, bool GAPS, class Sink>
 __device__ __forceinline__ void walk_kept(const CasArgs& a, const TileHdr& h, const WaveArea& W, int j0, int cnt,
                                           const uint32_t (&sraw)[5], const uint32_t (&lraw)[5], Sink& sink) {
     if (cnt <= 0) return;
-    UnaryCursor<FAST> uc;
+    UnaryCursor<FAST, GAPS> uc;
     uc.start(a, h, W, j0);
     uint32_t sw[4], lw[4];
     const int64_t n0 = h.kp0 + j0;
@@ -552,11 +562,11 @@ __device__ __forceinline__ void pru_load(const CasArgs& a, int64_t e, uint32_t (
     raw[16] = src[16];
 }
 
-template <class Emit>
+template <bool GAPS, class Emit>
 __device__ __forceinline__ void walk_pruned(const CasArgs& a, const TileHdr& h, const WaveArea& W, int p0, int cnt,
                                             const uint32_t (&raw0)[PRU_WORDS], Emit&& emit) {
     if (cnt <= 0) return;
-    BitCursor<true> zc;
+    BitCursor<true, GAPS> zc;
     zc.start(W, p0);
     const int64_t e0 = (h.f0 - h.kp0) + p0;          // pruned stream index of the first value
     uint32_t raw[PRU_WORDS], nxt[PRU_WORDS];
@@ -653,9 +663,10 @@ __device__ __forceinline__ void tile_issue(const CasArgs& a, const TileHdr& h, i
 
 // Stage the tile's bitmap (and, when it fits, its unary words) with prefix
 // counts, from the words tile_issue loaded.
-__device__ __forceinline__ void tile_stage(const CasArgs& a, const TileWords& tw, WaveArea& W) {
+__device__ __forceinline__ uint32_t tile_stage(const CasArgs& a, const TileWords& tw, WaveArea& W) {
     const int lane = lane_id();
     const TileHdr& h = tw.h;
+    uint32_t gaps = GAP_UNARY;
     if (h.nuw <= STAGE_UW) {
         auto mask = [&](uint32_t v, int k) {
             const int64_t b0 = (h.ws + k) * 32;
@@ -671,6 +682,8 @@ __device__ __forceinline__ void tile_stage(const CasArgs& a, const TileWords& tw
         const int tot0 = __shfl(inc, 63, 64) & 0xFFFF;
         W.uw[lane] = u0;
         W.uw[lane + 64] = u1;
+        const bool zu = (lane < h.nuw && u0 == 0u) || (lane + 64 < h.nuw && u1 == 0u);
+        gaps = __ballot(zu) ? GAP_UNARY : 0u;
         W.up[lane] = uint16_t((inc & 0xFFFF) - c0);
         W.up[lane + 64] = uint16_t(tot0 + (inc >> 16) - c1);
     }
@@ -682,14 +695,18 @@ __device__ __forceinline__ void tile_stage(const CasArgs& a, const TileWords& tw
     W.bw[2 * lane + 1] = b1;
     const int pc = __popc(b0) + __popc(b1);
     W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+    if (__ballot(b0 == 0u || b1 == 0u)) gaps |= GAP_EMPTY;
+    if (__ballot(b0 == ~0u || b1 == ~0u)) gaps |= GAP_FULL;
     wave_sync_lds();
+    return gaps;
 }
 
 // ------------------------------------------------------------------ sinks
 
 // Kept values scattered as bf16 bits into an LDS tile.
+template <bool GAPS>
 struct ScatterSink {
-    BitCursor<false> kc;
+    BitCursor<false, GAPS> kc;
     const WaveArea* W;
     const uint8_t* cb;
     uint16_t* d;
@@ -718,9 +735,9 @@ struct ScatterSink {
 // Kept values times activations (batch 1 or 2), into one accumulator per row, or,
 // when the tile meets two rows (SPLIT), kept index < jb into accA and the rest
 // into accB.  Slots past the lane's count read the LUT's zero entry.
-template <int BMAX, bool SPLIT>
+template <int BMAX, bool SPLIT, bool GAPS>
 struct DotSink {
-    BitCursor<false> kc;
+    BitCursor<false, GAPS> kc;
     const WaveArea* W;
     const float* lut;
     const uint16_t* xs;
@@ -781,21 +798,28 @@ __device__ __forceinline__ void decode_tile_issued(const CasArgs& a, const TileW
     const TileHdr& h = tw.h;
     uint32_t lraw[5];
     if constexpr (RESTORE) nib_load(a.lo_nib, h.kp0 + tw.j0, lraw);
-    tile_stage(a, tw, W);
-    ScatterSink sk;
-    sk.W = &W;
-    sk.cb = cb;
-    sk.d = d;
-    if (tw.cnt > 0) sk.kc.start(W, tw.j0);
-    if (h.nuw <= STAGE_UW) walk_kept<true, RESTORE>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
-    else walk_kept<false, RESTORE>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
-    if constexpr (RESTORE) {
-        int p0, pc;
-        lane_share(h.tl - h.nk, 64, lane_id(), p0, pc);
-        uint32_t praw[PRU_WORDS];
-        pru_load(a, (h.f0 - h.kp0) + p0, praw);
-        walk_pruned(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
-    }
+    // a tile without empty words (nearly all) takes the walks without their loops
+    // over empty words; the flag is wave-uniform
+    const uint32_t gaps = tile_stage(a, tw, W);
+    auto body = [&](auto g) __attribute__((always_inline)) {
+        constexpr bool G = decltype(g)::value;
+        ScatterSink<G> sk;
+        sk.W = &W;
+        sk.cb = cb;
+        sk.d = d;
+        if (tw.cnt > 0) sk.kc.start(W, tw.j0);
+        if (h.nuw <= STAGE_UW) walk_kept<true, RESTORE, G>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
+        else walk_kept<false, RESTORE, G>(a, h, W, tw.j0, tw.cnt, tw.sraw, lraw, sk);
+        if constexpr (RESTORE) {
+            int p0, pc;
+            lane_share(h.tl - h.nk, 64, lane_id(), p0, pc);
+            uint32_t praw[PRU_WORDS];
+            pru_load(a, (h.f0 - h.kp0) + p0, praw);
+            walk_pruned<G>(a, h, W, p0, pc, praw, [&](int pos, uint32_t v) { d[pos] = uint16_t(v); });
+        }
+    };
+    if (gaps) body(std::true_type{});
+    else body(std::false_type{});
 }
 
 // Kept values (and, when restoring, pruned values) of a tile are scattered into
@@ -889,7 +913,7 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
     auto process = [&](const TileWords& cur) __attribute__((always_inline)) {
         const TileHdr h = cur.h;
         const int j0 = cur.j0, cnt = cur.cnt;
-        tile_stage(a, cur, W);
+        const uint32_t gaps = tile_stage(a, cur, W);
         const int64_t row_a = h.f0 / K;
         const int bnd = int(min<int64_t>(h.tl, (row_a + 1) * K - h.f0));   // first position of the next row
         int jb = h.nk;                                                      // kept values before bnd
@@ -900,9 +924,9 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
                                             : __popc(lo & ((1u << rem) - 1u)));
         }
         float vA[BMAX], vB[BMAX];
-        auto run = [&](auto split) {
-            constexpr bool SPLIT = decltype(split)::value;
-            DotSink<BMAX, SPLIT> sk;
+        auto run = [&](auto split, auto g) {
+            constexpr bool SPLIT = decltype(split)::value, G = decltype(g)::value;
+            DotSink<BMAX, SPLIT, G> sk;
             sk.W = &W;
             sk.lut = lutf;
             sk.xs = xs;
@@ -916,16 +940,23 @@ __global__ __launch_bounds__(1024) void spec_gemv_kept_kernel(CasArgs a, const u
             for (int b = 0; b < BMAX; ++b) sk.accA[b] = sk.accB[b] = 0.f;
             if (cnt > 0) sk.kc.start(W, j0);
             uint32_t none[5];
-            if (h.nuw <= STAGE_UW) walk_kept<true, false>(a, h, W, j0, cnt, cur.sraw, none, sk);
-            else walk_kept<false, false>(a, h, W, j0, cnt, cur.sraw, none, sk);
+            if (h.nuw <= STAGE_UW) walk_kept<true, false, G>(a, h, W, j0, cnt, cur.sraw, none, sk);
+            else walk_kept<false, false, G>(a, h, W, j0, cnt, cur.sraw, none, sk);
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 vA[b] = sk.accA[b];
                 vB[b] = SPLIT ? sk.accB[b] : 0.f;
             }
         };
-        if (bnd < h.tl) run(std::true_type{});
-        else run(std::false_type{});
+        // a tile without empty words (nearly all) takes the walk without its loops
+        // over empty words; the flag is wave-uniform
+        if (gaps) {
+            if (bnd < h.tl) run(std::true_type{}, std::true_type{});
+            else run(std::false_type{}, std::true_type{});
+        } else {
+            if (bnd < h.tl) run(std::true_type{}, std::false_type{});
+            else run(std::false_type{}, std::false_type{});
+        }
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) {
 #pragma unroll

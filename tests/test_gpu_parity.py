@@ -419,6 +419,29 @@ def test_cassandra_long_codes(dev, keep):
     _check_cassandra(dev, w, norms, keep, (1, 2), (1, 16))
 
 
+def test_cassandra_gap_words(dev):
+    """Tiles with empty words: kept values with ~45 rare large exponents (codewords
+    longer than 32 bits, so a staged unary word holds no one bit, in tiles whose
+    stream still fits the staged words), 32-column blocks that every row prunes
+    (bitmap words without a kept position) and blocks that every row keeps (words
+    without a pruned position).  These tiles run the cursors' loops over empty
+    words; the other tiles of the same matrix skip them."""
+    print("case cassandra gap words", flush=True)
+    rng = np.random.default_rng(23)
+    M, K = 4, 12288
+    v = rng.standard_t(4, (M, K)) * 0.02
+    for r in range(M):
+        cols = rng.choice(np.arange(4096, 8192), 45, replace=False)      # the second tile of the row
+        v[r, cols] = np.ldexp(1.0 + rng.integers(0, 128, 45) / 128.0, np.arange(1, 46)) * rng.choice([-1.0, 1.0], 45)
+    w = synth.f32_to_bf16_bits(v.astype(np.float32))
+    norms = rng.lognormal(0, 1, K).astype(np.float32)
+    norms[256:288] = 1e-6                      # pruned in every row
+    norms[8192 + 512:8192 + 544] = 1e6         # kept in every row
+    sec = cassandra.pack(w, norms)
+    assert sec["codebook"].size > 40           # codewords longer than 32 bits exist
+    _check_cassandra(dev, w, norms, (3, 10), (1, 2), (1, 16))
+
+
 @pytest.fixture(scope="module")
 def spec_full():
     wl = synth.WORKLOADS["cassandra_spec"]
