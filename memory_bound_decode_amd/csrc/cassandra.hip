@@ -1448,9 +1448,12 @@ __global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecAr
         W.bw[2 * lane + 1] = L.b1;
         const int pc = __popc(L.b0) + __popc(L.b1);
         W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+        // a tile without a bitmap word free of kept positions (nearly all) walks
+        // with the cursor compiled without its loop over empty words
+        const bool gaps = __ballot(L.b0 == 0u || L.b1 == 0u) != 0;
         wave_sync_lds();
-        if (L.cnt > 0) {
-            BitCursor<false> kc;
+        auto scatter = [&](auto g) __attribute__((always_inline)) {
+            BitCursor<false, decltype(g)::value> kc;
             kc.start(W, int(L.first));
             const uint32_t j0 = L.kp0 + L.first;
             uint32_t q0 = L.q[0] >> (4 * (j0 & 7)), q1 = L.q[1], q2 = L.q[2], q3 = L.q[3], q4 = L.q[4],
@@ -1476,6 +1479,10 @@ __global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecAr
                     scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
                 }
             }
+        };
+        if (L.cnt > 0) {
+            if (gaps) scatter(std::true_type{});
+            else scatter(std::false_type{});
         }
         wave_sync_lds();
         const int tl = int(min<int64_t>(TILE, a.N - t * TILE));
@@ -1522,6 +1529,7 @@ __global__ __launch_bounds__(1024) void mx_spec_gemv_kept_kernel(MxSpecArgs a, c
         W.bw[2 * lane + 1] = L.b1;
         const int pc = __popc(L.b0) + __popc(L.b1);
         W.bp[lane] = uint16_t(wave_incl_add(pc) - pc);
+        const bool gaps = __ballot(L.b0 == 0u || L.b1 == 0u) != 0;   // as in the draft decode
         wave_sync_lds();
         const int64_t f0 = t * TILE;
         const int tl = int(min<int64_t>(TILE, a.N - f0));
@@ -1531,8 +1539,8 @@ __global__ __launch_bounds__(1024) void mx_spec_gemv_kept_kernel(MxSpecArgs a, c
         float accA[BMAX], accB[BMAX];
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) accA[b] = accB[b] = 0.f;
-        if (L.cnt > 0) {
-            BitCursor<false> kc;
+        auto dot = [&](auto g) __attribute__((always_inline)) {
+            BitCursor<false, decltype(g)::value> kc;
             kc.start(W, int(L.first));
             const uint32_t j0 = L.kp0 + L.first;
             uint32_t q0 = L.q[0] >> (4 * (j0 & 7)), q1 = L.q[1], q2 = L.q[2], q3 = L.q[3], q4 = L.q[4],
@@ -1568,6 +1576,10 @@ __global__ __launch_bounds__(1024) void mx_spec_gemv_kept_kernel(MxSpecArgs a, c
                     scale = ldexpf(1.f, int(xe & 0xFFu) - 130);
                 }
             }
+        };
+        if (L.cnt > 0) {
+            if (gaps) dot(std::true_type{});
+            else dot(std::false_type{});
         }
 #pragma unroll
         for (int b = 0; b < BMAX; ++b) {
