@@ -521,7 +521,15 @@ __device__ __forceinline__ void walk_kept(const CasArgs& a, const TileHdr& h, co
 #pragma unroll
                 for (int u = 0; u < GRP; ++u) {
                     const int i = GRP * g + u;
-                    if (i < rem) {
+                    if constexpr (FAST && !GAPS && Sink::kDrop) {
+                        // loop-free cursors: a lane past its share (at most GRP - 1
+                        // steps, the group guard stops it) steps on, at most one
+                        // word a step inside its staging area, and drops the slot
+                        const int rank = uc.next(a, h, W);
+                        sink.stage(u, rank, (sw[i / 8] >> (4 * (i % 8))) & 15u,
+                                   LO ? (lw[i / 8] >> (4 * (i % 8))) & 15u : 0u);
+                        sink.drop(u, i >= rem);
+                    } else if (i < rem) {
                         const int rank = uc.next(a, h, W);
                         sink.stage(u, rank, (sw[i / 8] >> (4 * (i % 8))) & 15u,
                                    LO ? (lw[i / 8] >> (4 * (i % 8))) & 15u : 0u);
@@ -706,6 +714,7 @@ __device__ __forceinline__ uint32_t tile_stage(const CasArgs& a, const TileWords
 // Kept values scattered as bf16 bits into an LDS tile.
 template <bool GAPS>
 struct ScatterSink {
+    static constexpr bool kDrop = true;     // the walk may stage past the share and drop (measured faster)
     BitCursor<false, GAPS> kc;
     const WaveArea* W;
     const uint8_t* cb;
@@ -722,6 +731,11 @@ struct ScatterSink {
         rk[u] = 0;
         nib[u] = 0;
     }
+    // a staged slot past the lane's share: nothing is written
+    __device__ __forceinline__ void drop(int u, bool past) {
+        pos[u] = past ? -1 : pos[u];
+        rk[u] = past ? 0 : rk[u];
+    }
     __device__ __forceinline__ void commit() {
         uint32_t E[GRP];
 #pragma unroll
@@ -737,6 +751,7 @@ struct ScatterSink {
 // into accB.  Slots past the lane's count read the LUT's zero entry.
 template <int BMAX, bool SPLIT, bool GAPS>
 struct DotSink {
+    static constexpr bool kDrop = false;    // guarded per value (staging past the share measured slower)
     BitCursor<false, GAPS> kc;
     const WaveArea* W;
     const float* lut;
@@ -760,6 +775,11 @@ struct DotSink {
         idx[u] = zero;
         if constexpr (SPLIT) inA[u] = true;
         ++j;
+    }
+    // a staged slot past the lane's share: weight 0.0 times a real activation
+    __device__ __forceinline__ void drop(int u, bool past) {
+        col[u] = past ? 0 : col[u];
+        idx[u] = past ? zero : idx[u];
     }
     __device__ __forceinline__ void commit() {
         float w[GRP], xv[GRP][BMAX];
