@@ -864,9 +864,9 @@ __global__ __launch_bounds__(64 * DD_WAVES) void decode_dense_kernel(CasArgs a, 
     // the first is decoded (more tiles per wave measured slower)
     auto clear = [&]() {
         if constexpr (!RESTORE) {
-            uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
+            uint4* d4 = reinterpret_cast<uint4*>(d) + lane;       // pruned positions read +0.0
 #pragma unroll
-            for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < 8; ++i) d4[64 * i] = make_uint4(0, 0, 0, 0);   // lane-contiguous: no bank conflicts
         }
     };
     const int64_t t0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 2 * DD_WAVES + wave);
@@ -1461,9 +1461,9 @@ __global__ __launch_bounds__(64 * MXD_WAVES) void mx_spec_decode_kernel(MxSpecAr
     uint16_t* d = dense[wave];
     WaveArea& W = areas[wave];
     auto decode = [&](int64_t t, const MxKept& L) {
-        uint4* d4 = reinterpret_cast<uint4*>(d) + 8 * lane;   // pruned positions read +0.0
+        uint4* d4 = reinterpret_cast<uint4*>(d) + lane;       // pruned positions read +0.0
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < 8; ++i) d4[64 * i] = make_uint4(0, 0, 0, 0);   // lane-contiguous: no bank conflicts
         W.bw[2 * lane] = L.b0;
         W.bw[2 * lane + 1] = L.b1;
         const int pc = __popc(L.b0) + __popc(L.b1);
