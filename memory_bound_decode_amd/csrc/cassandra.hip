@@ -1112,33 +1112,41 @@ __device__ __forceinline__ uint4 mx_to_bf16x8(uint2 m8, float scale, uint32_t sg
     return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-// Block = 32 rows (two 16-row MFMA tiles) x all K.  K is walked in 128-column
-// chunks, chunk c by wave c % MX_WAVES.  In a chunk, lane (n, q) = (lane % 16,
-// lane / 16) holds the 32-element MX group q of row n of each tile (32 bytes of
-// magnitudes, its exponent and sign word) and the same 32 activation columns of
-// batch row n; the MFMA k slots of sub-step s take the group's elements
-// 8s..8s+7, the same columns on both operands.  The next chunk's loads are issued
-// before the current chunk is computed.  Partial tiles are summed across the
-// waves at the end.
+// Block = 32 rows (two 16-row MFMA tiles) x all K, one block per CU.  K is
+// walked in rounds of MX_SLAB columns, one 128-column chunk per wave: chunk c by
+// wave c % MX_WAVES.  In a chunk, lane (n, q) = (lane % 16, lane / 16) holds the
+// 32-element MX group q of row n of each tile (32 bytes of magnitudes, its
+// exponent and sign word); the MFMA k slots of sub-step s take the group's
+// elements 8s..8s+7, and batch row n's same 32 columns come from LDS.  The
+// block stages each round's activation slab (all 16 batch rows) in LDS with
+// lane-contiguous 16-byte loads, double-buffered: read by each wave straight
+// from global memory, every activation load touched 32 cache lines for 1 KB and
+// cost as much time as the weights.  The next round's weights and slab are
+// loaded while the current chunk is computed.  Partial tiles are summed across
+// the waves at the end.
 constexpr int MX_WAVES = 16;
+constexpr int MX_SLAB = MX_WAVES * 128;             // activation columns per round
+constexpr int MX_XROW = MX_SLAB + 8;                // u16 per staged row: rows 4 banks apart
+constexpr size_t MX_LDS = size_t(2) * 16 * MX_XROW * 2;
+static_assert(MX_SLAB / 8 * 16 == 4 * 64 * MX_WAVES, "a slab is four 16-byte pieces per thread");
+static_assert(MX_LDS >= sizeof(float) * MX_WAVES * 2 * 64 * 4, "the partial tiles reuse the slab buffers");
 
 struct MxChunk {
     uint4 ma0, ma1, mb0, mb1;   // magnitudes, tiles A and B
     uint32_t ea, eb, sa, sb;    // exponents, sign words
-    uint4 xv[4];                // activations
 };
 
 __global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const uint16_t* __restrict__ x, int B,
                                                                float* __restrict__ y) {
-    __shared__ float red[MX_WAVES][2][64][4];
+    extern __shared__ __attribute__((aligned(16))) uint4 mxl4[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(mxl4);           // [2][16][MX_XROW]
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 15, q = lane >> 4;
     const int64_t K = a.K, G = K / 32;
     const int64_t r0 = int64_t(blockIdx.x) * 32;
     const int64_t rA = min<int64_t>(r0 + n, a.M - 1), rB = min<int64_t>(r0 + 16 + n, a.M - 1);
     const int nchunks = int((K + 127) / 128);
-    const bool xv_ok = n < B;
-    const uint16_t* xrow = x + int64_t(xv_ok ? n : 0) * K;
+    const int nrounds = int((K + MX_SLAB - 1) / MX_SLAB);
     auto load = [&](int c, MxChunk& d) {
         // the group's columns; a chunk past K (only when K % 128 != 0) reloads group 0
         int64_t g = int64_t(c) * 4 + q;
@@ -1151,12 +1159,26 @@ __global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const 
         d.eb = a.exp[rB * G + g];
         d.sa = a.sign[rA * G + g];
         d.sb = a.sign[rB * G + g];
-        const uint4* px = reinterpret_cast<const uint4*>(xrow + g * 32);
+    };
+    // slab r: piece p = threadIdx.x + 1024 i is batch row p / 256, columns
+    // r MX_SLAB + 8 (p % 256) + [0, 8); rows past B and columns past K read zero
+    auto x_issue = [&](int r, uint4 (&v)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d.xv[i] = px[i];
+        for (int i = 0; i < 4; ++i) {
+            const int p = int(threadIdx.x) + 64 * MX_WAVES * i, row = p >> 8;
+            const int64_t col = int64_t(r) * MX_SLAB + 8 * (p & 255);
+            v[i] = row < B && col < K ? *reinterpret_cast<const uint4*>(x + row * K + col) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto x_store = [&](int buf, const uint4 (&v)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = int(threadIdx.x) + 64 * MX_WAVES * i, row = p >> 8;
+            *reinterpret_cast<uint4*>(xs + (buf * 16 + row) * MX_XROW + 8 * (p & 255)) = v[i];
+        }
     };
     f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int c, const MxChunk& d) {
+    auto compute = [&](int c, const MxChunk& d, int buf) {
         const bool live = int64_t(c) * 4 + q < G;    // group past K: contributes nothing
         const float sa = live ? __builtin_ldexpf(1.f, int(d.ea) - 134) : 0.f;
         const float sb = live ? __builtin_ldexpf(1.f, int(d.eb) - 134) : 0.f;
@@ -1164,9 +1186,10 @@ __global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const 
                              make_uint2(d.ma1.x, d.ma1.y), make_uint2(d.ma1.z, d.ma1.w)};
         const uint2 mb[4] = {make_uint2(d.mb0.x, d.mb0.y), make_uint2(d.mb0.z, d.mb0.w),
                              make_uint2(d.mb1.x, d.mb1.y), make_uint2(d.mb1.z, d.mb1.w)};
+        const uint16_t* xb = xs + (buf * 16 + n) * MX_XROW + wave * 128 + q * 32;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const uint4 bv = xv_ok ? d.xv[s] : make_uint4(0, 0, 0, 0);
+            const uint4 bv = *reinterpret_cast<const uint4*>(xb + 8 * s);
             const uint4 av = mx_to_bf16x8(ma[s], sa, (d.sa >> (8 * s)) & 0xFFu);
             const uint4 aw = mx_to_bf16x8(mb[s], sb, (d.sb >> (8 * s)) & 0xFFu);
             accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
@@ -1175,26 +1198,39 @@ __global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const 
                                                            __builtin_bit_cast(bf16x8_t, bv), accB, 0, 0, 0);
         }
     };
-    // two chunk buffers, so a buffer is never copied while its loads are in flight;
-    // the scheduling fences keep each chunk's loads issued before the other
-    // chunk's compute (left to itself the compiler sinks them below it, and the
-    // wave then has one chunk in flight instead of two)
+    // Round r reads slab buffer r % 2 and weight buffer r % 2; the barrier that
+    // ends a round orders its slab reads before the next round's slab stores into
+    // the other buffer.  The scheduling fences keep each round's loads issued
+    // before its compute (left to itself the compiler sinks them below it).
     MxChunk c0, c1;
-    int c = wave;
-    if (c < nchunks) load(c, c0);
-    for (; c < nchunks; c += 2 * MX_WAVES) {
-        const int cn = c + MX_WAVES;
-        load(min(cn, nchunks - 1), c1);
+    uint4 xr[4];
+    x_issue(0, xr);
+    load(min(wave, nchunks - 1), c0);
+    x_store(0, xr);
+    __syncthreads();
+    for (int r = 0; r < nrounds; r += 2) {
+        const bool more = r + 1 < nrounds;             // block-uniform
+        if (more) x_issue(r + 1, xr);
+        load(min(MX_WAVES * (r + 1) + wave, nchunks - 1), c1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(c, c0);
-        load(min(cn + MX_WAVES, nchunks - 1), c0);
+        if (MX_WAVES * r + wave < nchunks) compute(MX_WAVES * r + wave, c0, 0);
+        if (more) x_store(1, xr);
+        __syncthreads();
+        if (!more) break;
+        const bool more2 = r + 2 < nrounds;
+        if (more2) x_issue(r + 2, xr);
+        load(min(MX_WAVES * (r + 2) + wave, nchunks - 1), c0);
         __builtin_amdgcn_sched_barrier(0);
-        if (cn < nchunks) compute(cn, c1);
+        if (MX_WAVES * (r + 1) + wave < nchunks) compute(MX_WAVES * (r + 1) + wave, c1, 1);
+        if (more2) x_store(0, xr);
+        __syncthreads();
     }
+    // the slab buffers are free after the last barrier
+    float* red = reinterpret_cast<float*>(mxl4);      // [MX_WAVES][2][64][4]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        red[wave][0][lane][j] = accA[j];
-        red[wave][1][lane][j] = accB[j];
+        red[((wave * 2 + 0) * 64 + lane) * 4 + j] = accA[j];
+        red[((wave * 2 + 1) * 64 + lane) * 4 + j] = accB[j];
     }
     __syncthreads();
     // C[row = 4q + j][col = n]; waves 0 and 1 sum tiles A and B
@@ -1202,7 +1238,7 @@ __global__ __launch_bounds__(64 * MX_WAVES) void mx_gemm_kernel(MxArgs a, const 
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < MX_WAVES; ++w)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s4[j] += red[w][wave][lane][j];
+            for (int j = 0; j < 4; ++j) s4[j] += red[((w * 2 + wave) * 64 + lane) * 4 + j];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t r = r0 + 16 * wave + 4 * q + j;
@@ -1822,8 +1858,11 @@ mbd_status mbd_gemv_mx32(const mbd_dweights* w, const uint16_t* x, int32_t B, fl
     if (w->M == 0) return MBD_OK;
     MxArgs a{static_cast<const uint8_t*>(w->sec[0]), static_cast<const uint32_t*>(w->sec[1]),
              static_cast<const uint8_t*>(w->sec[2]), w->M, w->K};
+    static std::atomic<int> lds_done{0};
+    mbd_status s = lds_limit(reinterpret_cast<const void*>(mx_gemm_kernel), lds_done, MX_LDS, "MX GEMM");
+    if (s != MBD_OK) return s;
     const unsigned blocks = unsigned((w->M + 31) / 32);
-    hipLaunchKernelGGL(mx_gemm_kernel, dim3(blocks), dim3(64 * MX_WAVES), 0, st, a, x, B, y);
+    hipLaunchKernelGGL(mx_gemm_kernel, dim3(blocks), dim3(64 * MX_WAVES), MX_LDS, st, a, x, B, y);
     return hip_check("MX GEMM launch");
 }
 

@@ -545,7 +545,9 @@ def test_mx_full(dev, verify_full):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("M,K,B", [(16, 32, 1), (33, 96, 5), (40, 4096, 16)])
+# K = 4128 and 6176: an odd and an even number of 2048-column activation slabs,
+# the last holding one 32-column group
+@pytest.mark.parametrize("M,K,B", [(16, 32, 1), (33, 96, 5), (40, 4096, 16), (17, 4128, 16), (48, 6176, 7)])
 def test_mx_ragged_and_dequant(dev, M, K, B):
     mbd = _mbd()
     w = _rand_w(M + K, M, K)
