@@ -240,7 +240,9 @@ mbd_status mbd_dequant(const mbd_dweights* w, float* w_out, void* stream);
  * TERNARY and INT4: B in [1, 16].  MX32: B in [1, 16] (MFMA bf16, the Cassandra-2
  * verify GEMM).  CASSANDRA: the target-side verify GEMM over the restored weight
  * (speculation + verification data merged on the fly, [Cassandra] 3.2), B in [1, 16].
- * x: bf16 [B][K], 16-byte aligned.  y: fp32 [B][M], 4-byte aligned. */
+ * x: bf16 [B][K], 16-byte aligned.  y: fp32 [B][M], 4-byte aligned.  TERNARY,
+ * TERNARY_SKIP and INT4 at B > 4 address the activations with 32-bit element
+ * offsets: B·K of 2^32 or more returns MBD_ESHAPE. */
 mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* y,
                     void* stream);
 
@@ -253,7 +255,9 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
  * rows unwritten; an id repeated within a token is outside this contract (with at
  * most 16 tokens, pairs past an expert's 16th may be left unwritten).  ws: device workspace of at least
  * mbd_moe_workspace_bytes(n_mats, T, k) bytes, 16-byte aligned, contents
- * overwritten.  Calls that share a workspace must not overlap. */
+ * overwritten.  Calls that share a workspace must not overlap.  With T > 1 the
+ * activations are addressed with 32-bit element offsets: x's rows (T, or T·k with
+ * x_per_pair) times K of 2^32 or more returns MBD_ESHAPE. */
 mbd_status mbd_moe_workspace_bytes(int64_t n_mats, int32_t T, int32_t k, uint64_t* bytes);
 mbd_status mbd_moe_gemv(const mbd_dweights* experts, const int32_t* route, int32_t T,
                         int32_t k, const uint16_t* x, int32_t x_per_pair, float* y,

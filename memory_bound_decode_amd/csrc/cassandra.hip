@@ -79,12 +79,6 @@ __device__ __forceinline__ int wave_incl_max(int v) {
     return v;
 }
 
-__device__ __forceinline__ void wave_sync_lds() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Rolling window over a packed nibble stream starting at nibble index n.
 struct NibWin {
     uint64_t cur;
@@ -1714,16 +1708,6 @@ mbd_status cas_args(const mbd_dweights* w, bool need_verify, CasArgs* a) {
     a->N = w->M * w->K;
     a->T = (a->N + TILE - 1) / TILE;
     a->n_sym = w->n_sym;
-    return MBD_OK;
-}
-
-// Raise a kernel's dynamic LDS limit once per process (idempotent, so a race
-// between first calls only repeats the call).
-mbd_status lds_limit(const void* kern, std::atomic<int>& done, size_t bytes, const char* what) {
-    if (done.load(std::memory_order_acquire) >= int(bytes)) return MBD_OK;
-    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes)) != hipSuccess)
-        return fail(MBD_EHIP, "cannot raise the %s LDS limit to %zu bytes", what, bytes);
-    done.store(int(bytes), std::memory_order_release);
     return MBD_OK;
 }
 

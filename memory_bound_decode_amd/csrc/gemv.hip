@@ -597,7 +597,7 @@ struct MqGroup {
     uint4 code[MQ_TILES];          // INT4: 4 words (32 codes); ternary: .x, .y (32 codes)
     uint32_t sc[MQ_TILES][4];      // raw fp16 scales of the lane's 4 output rows (global
                                    // path): packing them at issue would wait for the loads
-    uint4 xv[4];                   // 32 activations of batch row n
+    uint4 xv[4];                   // activation pieces (layout in mq_core)
     int g;                         // the group (scales from LDS)
     uint32_t rm[MQ_TILES];         // skip format: the block column's stored-row mask per tile
 };
@@ -614,6 +614,10 @@ inline size_t mq_scale_lds(int ngroups, bool sl) { return sl ? size_t(ngroups) *
 inline size_t mq_lds_bytes(int nw, int ngroups, bool sl) {
     return mq_scale_lds(ngroups, sl) + size_t(nw) * MQ_TILES * 64 * 4 * sizeof(float);
 }
+// Each wave's activation rows for one group, [16][MQ_XROW] bf16, after the parts
+// above: rows 4 banks apart.
+constexpr int MQ_XROW = 128 + 8;
+inline size_t mq_x_lds(int nw) { return size_t(nw) * 16 * MQ_XROW * 2; }
 #ifndef MBD_MQ_DEPTH
 #define MBD_MQ_DEPTH 2        // group buffers per wave
 #endif
@@ -645,14 +649,15 @@ __device__ __forceinline__ uint32_t ter_nk0(int s, int p) {
 }
 
 // Rows [row_base, row_base + MQ_ROWS) of one matrix; nb <= 16 batch rows whose
-// activations / outputs are xrow(b) / yrow(b).  SL: the block's fp16 scales are
+// activations / outputs are rows xrow(b) of a.x (x + xrow(b) K; the launchers
+// keep a.x's rows times K below 2^32) / yrow(b).  SL: the block's fp16 scales are
 // staged in LDS once (coalesced row runs) and a lane reads its 4 rows' scales of
 // a group with one 8-byte LDS read, instead of 4 global loads per tile and group.
 // SK: the ternary skip format; the
 // waves take single block columns, and lane j of sw holds the slab word of this
 // wave's column j / MQ_TILES in tile j % MQ_TILES (the launcher keeps a wave's
 // columns times MQ_TILES within 64).
-template <bool TER, bool SK, bool SL, bool DYN_RED, class XRow, class YRow>
+template <bool TER, bool SK, bool SL, bool DYN_RED, bool XS, class XRow, class YRow>
 __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int row_base, int nb, XRow xrow,
                                         YRow yrow) {
@@ -662,13 +667,16 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
     uint16_t* mq_sc = reinterpret_cast<uint16_t*>(mq_lds);                // SL: [ngroups][MQ_ROWS]
     float* red;                                                            // [nw][MQ_TILES][64][4]
+    float* after = mq_lds + (SL ? (a.K >> 7) * (MQ_ROWS / 2) : 0);
     if constexpr (DYN_RED) {
-        red = mq_lds + (SL ? (a.K >> 7) * (MQ_ROWS / 2) : 0);
+        red = after;
+        after += nw * MQ_TILES * 64 * 4;
     } else {
         __shared__ float red_s[MQ_MAXW * MQ_TILES * 64 * 4];
         red = red_s;
     }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint16_t* xw = reinterpret_cast<uint16_t*>(after) + wave * 16 * MQ_XROW;   // XS: this wave's activation rows
     const int n = lane & 15, q = lane >> 4;
     const int K = a.K, M = a.M, ngroups = K >> 7;
     const uint32_t row_bytes = uint32_t(K) / BPR;
@@ -699,7 +707,25 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
         __syncthreads();
     }
     const bool xlive = n < nb;
-    const uint16_t* xr = xrow(xlive ? n : 0);
+    // Activations.  MFMA order: lane (n, q) takes batch row n (row 0 past nb),
+    // columns 32 q + 8 s + [0, 8) at step s of the group; read that way, one load
+    // instruction touches 32 cache lines for 1 KB.  XS: piece i of lane l is 16
+    // bytes of batch row 4 i + l / 16 (row 0 past nb) at column 8 (l % 16), so 16
+    // lanes read a row's 256 bytes (pieces whose four rows are all past nb are not
+    // loaded), and the compute passes them through the wave's LDS rows into MFMA
+    // order.  The round trip pays from 12 batch rows, or from 8 with 16 waves.
+    uint32_t xo[4];                                        // XS: element offsets in a.x
+    const uint16_t* xr = a.x;                              // !XS: batch row n
+    if constexpr (XS) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rb = 4 * i + (lane >> 4);
+            xo[i] = uint32_t(xrow(rb < nb ? rb : 0)) * uint32_t(K) + 8u * uint32_t(lane & 15);
+        }
+    } else {
+        xr = a.x + size_t(xrow(xlive ? n : 0)) * size_t(K);
+    }
+    const uint16_t* xq = xw + (xlive ? n : 0) * MQ_XROW + 32 * q;
     // skip format: byte offset of each tile's stored blocks, and the slab words
     uint32_t tbase[MQ_TILES];
     uint32_t sw = 0;
@@ -744,9 +770,16 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
             }
         }
         d.g = g;
-        const uint4* px = reinterpret_cast<const uint4*>(xr + size_t(g) * 128 + 32 * q);
+        if constexpr (XS) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d.xv[i] = px[i];
+            for (int i = 0; i < 4; ++i)
+                d.xv[i] = 4 * i < nb ? *reinterpret_cast<const uint4*>(a.x + (xo[i] + uint32_t(g) * 128u))
+                                     : make_uint4(0, 0, 0, 0);
+        } else {
+            const uint4* px = reinterpret_cast<const uint4*>(xr + size_t(g) * 128 + 32 * q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d.xv[i] = px[i];
+        }
     };
     f32x4_t acc[MQ_TILES];
 #pragma unroll
@@ -769,7 +802,20 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     };
     const bf16x8_t ak0 = nk_operand(0), ak1 = nk_operand(1);
     auto compute = [&](const MqGroup& d) {
-        const uint4* xb = d.xv;
+        uint4 xb[4];
+        if constexpr (XS) {
+            // into MFMA order through the wave's LDS rows (the previous group's
+            // reads completed before its MFMAs)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * i < nb) *reinterpret_cast<uint4*>(xw + (4 * i + (lane >> 4)) * MQ_XROW + 8 * (lane & 15)) = d.xv[i];
+            wave_sync_lds();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xb[s] = *reinterpret_cast<const uint4*>(xq + 8 * s);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xb[s] = d.xv[s];
+        }
         f32x4_t cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -852,12 +898,11 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     }
 }
 
-template <bool TER, bool SK, bool SL>
+template <bool TER, bool SK, bool SL, bool XS>
 __global__ __launch_bounds__(64 * MQ_MAXW) void gemv_mq_kernel(MqArgs a) {
-    const uint16_t* x = a.x;
     float* y = a.y;
-    const int K = a.K, M = a.M;
-    mq_core<TER, SK, SL, false>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return x + (size_t)b * K; },
+    const int M = a.M;
+    mq_core<TER, SK, SL, false, XS>(a, a.codes, a.scales, blockIdx.x * MQ_ROWS, a.B, [=](int b) { return b; },
                  [=](int b) { return y + (size_t)b * M; });
 }
 
@@ -910,16 +955,15 @@ __global__ __launch_bounds__(64 * MQ_MAXW) void moe_mq_kernel(MqArgs a) {
         e = jd.x;
         cnt = jd.z;
     }
-    const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M, topk = a.topk, xpp = a.x_per_pair;
     const size_t per_codes = (size_t)M * K / (TER ? 4 : 2), per_scales = (size_t)M * (K / 128);
     if (cnt == 0) return;
-    mq_core<TER, false, SL, true>(
+    mq_core<TER, false, SL, true, false>(
         a, a.codes + (size_t)e * per_codes, a.scales + (size_t)e * per_scales, rb * MQ_ROWS, min(16, cnt),
         [=](int b) {
             const int p = pids[b];
-            return x + (size_t)(xpp ? p : p / topk) * K;
+            return xpp ? p : p / topk;
         },
         [=](int b) { return y + (size_t)pids[b] * M; });
 }
@@ -1055,6 +1099,37 @@ BnPlan plan_bn(bool ter, int64_t K, int64_t tiles, int NB) {
     return p;
 }
 
+// The 32-row kernels with lds bytes of dynamic LDS, each kernel's limit raised
+// first (the activation rows take up to 68 KiB).
+template <bool TER, bool SK, bool SL, bool XS>
+mbd_status launch_mq1(unsigned blocks, int nw, size_t lds, hipStream_t st, const MqArgs& m) {
+    static std::atomic<int> done{0};
+    const mbd_status s = lds_limit(reinterpret_cast<const void*>(gemv_mq_kernel<TER, SK, SL, XS>), done, lds,
+                                   "batched GEMV");
+    if (s != MBD_OK) return s;
+    hipLaunchKernelGGL((gemv_mq_kernel<TER, SK, SL, XS>), dim3(blocks), dim3(64 * nw), lds, st, m);
+    return MBD_OK;
+}
+
+// Activations staged through LDS (XS) from 12 batch rows, or from 8 with 16 waves
+// (measured: INT4 8192 x 8192 B = 16 15.0 -> 12.6 us, B = 8 10.9 -> 11.3; INT4
+// 8192 x 28672 B = 8 32.1 -> 27.8 us).
+template <bool TER, bool SK, bool SL>
+mbd_status launch_mq(unsigned blocks, int nw, size_t lds, hipStream_t st, const MqArgs& m) {
+    if (m.B >= 12 || (m.B >= 8 && nw >= 16))
+        return launch_mq1<TER, SK, SL, true>(blocks, nw, lds + mq_x_lds(nw), st, m);
+    return launch_mq1<TER, SK, SL, false>(blocks, nw, lds, st, m);
+}
+
+template <bool TER, bool SL>
+mbd_status launch_moe_mq(unsigned grid, int nw, size_t lds, hipStream_t st, const MqArgs& m) {
+    static std::atomic<int> done{0};
+    const mbd_status s = lds_limit(reinterpret_cast<const void*>(moe_mq_kernel<TER, SL>), done, lds, "expert GEMV");
+    if (s != MBD_OK) return s;
+    hipLaunchKernelGGL((moe_mq_kernel<TER, SL>), dim3(grid), dim3(64 * nw), lds, st, m);
+    return MBD_OK;
+}
+
 // gemv_bn_kernel for the plan's row count and staging passes, or moe_b1_kernel.
 template <bool TER, bool SK, bool MOE>
 mbd_status launch_bn(const BnPlan& pl, const BnArgs& a, unsigned grid, hipStream_t st) {
@@ -1101,6 +1176,7 @@ mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float*
     const int ngroups = int(w->K / 128);
     const int nw_mq = mq_waves(w->K, MBD_MQ_GPW_GEMV);
     if (B > 4 && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
+        if (int64_t(B) * w->K >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
         m.scales = static_cast<const uint16_t*>(w->sec[1]);
@@ -1110,10 +1186,9 @@ mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float*
         const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
         const bool sll = size_t(ngroups) * MQ_ROWS * 2 <= size_t(MQ_SCALE_LDS);
         const size_t lds = mq_scale_lds(ngroups, sll);
-        if (sll)
-            hipLaunchKernelGGL((gemv_mq_kernel<true, true, true>), dim3(blocks), dim3(64 * nw_mq), lds, st, m);
-        else
-            hipLaunchKernelGGL((gemv_mq_kernel<true, true, false>), dim3(blocks), dim3(64 * nw_mq), lds, st, m);
+        const mbd_status s = sll ? launch_mq<true, true, true>(blocks, nw_mq, lds, st, m)
+                                 : launch_mq<true, true, false>(blocks, nw_mq, lds, st, m);
+        if (s != MBD_OK) return s;
         return hip_check("batched gemv launch");
     }
     for (int b0 = 0; b0 < B; b0 += 4) {
@@ -1165,6 +1240,7 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (B > 4) {
         // 5..16 rows: the 32-row kernel with activations read per group (at 8 rows
         // it measured even with the few-row kernel, above that faster)
+        if (int64_t(B) * w->K >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
         m.scales = static_cast<const uint16_t*>(w->sec[1]);
@@ -1173,10 +1249,11 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
         const unsigned blocks = unsigned((w->M + MQ_ROWS - 1) / MQ_ROWS);
         const bool sll = size_t(w->K / 128) * MQ_ROWS * 2 <= size_t(MQ_SCALE_LDS);
         const size_t lds = mq_scale_lds(int(w->K / 128), sll);
-        if (ter && sll) hipLaunchKernelGGL((gemv_mq_kernel<true, false, true>), dim3(blocks), dim3(64 * nw), lds, st, m);
-        else if (ter) hipLaunchKernelGGL((gemv_mq_kernel<true, false, false>), dim3(blocks), dim3(64 * nw), lds, st, m);
-        else if (sll) hipLaunchKernelGGL((gemv_mq_kernel<false, false, true>), dim3(blocks), dim3(64 * nw), lds, st, m);
-        else hipLaunchKernelGGL((gemv_mq_kernel<false, false, false>), dim3(blocks), dim3(64 * nw), lds, st, m);
+        const mbd_status s = ter && sll ? launch_mq<true, false, true>(blocks, nw, lds, st, m)
+                             : ter      ? launch_mq<true, false, false>(blocks, nw, lds, st, m)
+                             : sll      ? launch_mq<false, false, true>(blocks, nw, lds, st, m)
+                                        : launch_mq<false, false, false>(blocks, nw, lds, st, m);
+        if (s != MBD_OK) return s;
         return hip_check("batched gemv launch");
     }
     const int tiles = int((w->M + 15) / 16);
@@ -1260,11 +1337,20 @@ mbd_status moe_check(const mbd_dweights* w) {
     return MBD_OK;
 }
 
+// Past one token the 32-row kernel addresses the activation rows with 32-bit
+// element offsets.
+mbd_status moe_x_check(const mbd_dweights* w, int32_t T, int32_t k, int32_t x_per_pair) {
+    if (T > 1 && int64_t(x_per_pair ? int64_t(T) * k : T) * w->K >= (int64_t(1) << 32))
+        return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
+    return MBD_OK;
+}
+
 mbd_status moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int32_t k, const uint16_t* x,
                     int32_t x_per_pair, float* y, void* ws, uint64_t ws_bytes, void* stream) {
     if (!w || !route || !x || !y || !ws) return fail(MBD_EINVAL, "NULL argument");
     mbd_status s = moe_check(w);
     if (s != MBD_OK) return s;
+    if ((s = moe_x_check(w, T, k, x_per_pair)) != MBD_OK) return s;
     uint64_t need = 0;
     if ((s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need)) != MBD_OK) return s;
     if (ws_bytes < need) return fail(MBD_EINVAL, "workspace of %llu bytes, need %llu", (unsigned long long)ws_bytes, (unsigned long long)need);
@@ -1320,18 +1406,18 @@ mbd_status moe_gemv(const mbd_dweights* w, const int32_t* route, int32_t T, int3
     m.n_pairs = P; m.n_experts = E; m.topk = k; m.x_per_pair = x_per_pair ? 1 : 0;
     m.row_blocks = int((w->M + MQ_ROWS - 1) / MQ_ROWS);
     const int nw = mq_waves(w->K, MBD_MQ_GPW);
-    // scales staged while the block's dynamic LDS stays within 60 KiB (under the
-    // 64 KiB a launch gets without raising the kernel's limit, with its static part)
+    // scales staged while the block's dynamic LDS stays within 60 KiB (a short
+    // expert matrix's few waves keep several blocks per CU)
     const bool sll = mq_lds_bytes(nw, int(w->K / 128), true) <= size_t(60 * 1024);
     const size_t lds = mq_lds_bytes(nw, int(w->K / 128), sll);
     const int64_t grid = (by_expert ? int64_t(E) : max_jobs) * m.row_blocks;
     if (grid > INT32_MAX) return fail(MBD_ESHAPE, "expert grid too large");
-    if (ter)
-        if (sll) hipLaunchKernelGGL((moe_mq_kernel<true, true>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);
-        else hipLaunchKernelGGL((moe_mq_kernel<true, false>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);
-    else
-        if (sll) hipLaunchKernelGGL((moe_mq_kernel<false, true>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);
-        else hipLaunchKernelGGL((moe_mq_kernel<false, false>), dim3(unsigned(grid)), dim3(64 * nw), lds, st, m);
+    const unsigned g = unsigned(grid);
+    const mbd_status ls = ter && sll ? launch_moe_mq<true, true>(g, nw, lds, st, m)
+                          : ter      ? launch_moe_mq<true, false>(g, nw, lds, st, m)
+                          : sll      ? launch_moe_mq<false, true>(g, nw, lds, st, m)
+                                     : launch_moe_mq<false, false>(g, nw, lds, st, m);
+    if (ls != MBD_OK) return ls;
     return hip_check("expert gemv launch");
 }
 
@@ -1384,6 +1470,7 @@ mbd_status mbd_moe_gemv_noalloc(const mbd_dweights* w, const int32_t* route, int
     if (!w || !route || !x || !y) return fail(MBD_EINVAL, "NULL argument");
     mbd_status s = moe_check(w);
     if (s != MBD_OK) return s;
+    if ((s = moe_x_check(w, T, k, x_per_pair)) != MBD_OK) return s;
     uint64_t need = 0;
     if ((s = mbd_moe_workspace_bytes(w->n_mats, T, k, &need)) != MBD_OK) return s;
     if (need > kMoeScratchBytes)

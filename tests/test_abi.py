@@ -145,6 +145,11 @@ def test_gemv_argument_errors(L):
             d = _desc(fmt, M, 8192)
             assert L.mbd_gemv(ctypes.byref(d), P16, B, P16, None) == mbd.MBD_ESHAPE
             assert b"4 GiB" in L.mbd_last_error()
+    # batch 5..16 addresses the activations with 32-bit element offsets: B K >= 2^32 is refused
+    for fmt in (mbd.MBD_INT4_G128, mbd.MBD_TERNARY_B128):
+        d = _desc(fmt, 16, 1 << 28)
+        assert L.mbd_gemv(ctypes.byref(d), P16, 16, P16, None) == mbd.MBD_ESHAPE
+        assert b"2^32" in L.mbd_last_error()
 
 
 def test_skip_format_argument_errors(L):
@@ -247,3 +252,10 @@ def test_moe_noalloc_argument_errors(L):
     assert b"4 GiB" in L.mbd_last_error()
     assert L.mbd_moe_gemv(ctypes.byref(big), P16, 1, 2, P16, 0, P16, P16, 1 << 20, None) == mbd.MBD_ESHAPE
     assert b"4 GiB" in L.mbd_last_error()
+    # with T > 1 the activations are addressed with 32-bit element offsets: x's rows
+    # (T k with x_per_pair) times K of 2^32 or more is refused, on both entry points
+    wide = _desc(mbd.MBD_TERNARY_B128, 1, 1 << 30, n_mats=2)
+    assert L.mbd_moe_gemv(ctypes.byref(wide), P16, 2, 2, P16, 1, P16, P16, 1 << 20, None) == mbd.MBD_ESHAPE
+    assert b"2^32" in L.mbd_last_error()
+    assert L.mbd_moe_gemv_noalloc(ctypes.byref(wide), P16, 2, 2, P16, 1, P16, None) == mbd.MBD_ESHAPE
+    assert b"2^32" in L.mbd_last_error()

@@ -589,6 +589,22 @@ def _random_cases(n, seed):
     return out
 
 
+# The batch 5..16 kernel stages the activations through LDS from 12 batch rows, or
+# from 8 when its blocks have 16 waves (K >= 16384); at 9 and 10 rows the third
+# piece of four rows is partly past the batch.
+@pytest.mark.parametrize("kind", ["ternary", "int4"])
+@pytest.mark.parametrize("M,K,B", [(45, 16384, 9), (40, 16512, 10), (33, 2048, 13), (70, 17408, 8), (19, 16384, 7)])
+def test_gemv_staged_activation_batches(dev, kind, M, K, B):
+    print("case staged gemv", kind, M, K, B, flush=True)
+    w = _rand_w(M * 17 + K + B, M, K)
+    x = _rand_x(B * 5 + K, B, K)
+    dw = _mbd().to_device(_mbd().mbd_pack(_fmt(kind), w), dev)
+    q, s = QUANT[kind].quantize(w)
+    y = _run_gemv(dw, x, dev)
+    assert np.all(np.isfinite(y))
+    check(y, gemv.gemv(QUANT[kind].dequant(q, s), x))
+
+
 @pytest.mark.parametrize("kind", ["ternary", "int4"])
 @pytest.mark.parametrize("M,K,B", _random_cases(12, 2026))
 def test_gemv_random_shapes(dev, kind, M, K, B):

@@ -117,7 +117,7 @@ def skip_full(dev):
     return wl, w, _pack(w, dev)
 
 
-@pytest.mark.parametrize("B", [1, 4, 8])
+@pytest.mark.parametrize("B", [1, 4, 8, 16])
 def test_skip_gemv_full(dev, skip_full, B):
     wl, w, dw = skip_full
     M, K = w.shape
