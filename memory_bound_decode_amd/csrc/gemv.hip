@@ -1111,12 +1111,12 @@ mbd_status launch_mq1(unsigned blocks, int nw, size_t lds, hipStream_t st, const
     return MBD_OK;
 }
 
-// Activations staged through LDS (XS) from 12 batch rows, or from 8 with 16 waves
+// Activations staged through LDS (XS) from 12 batch rows, or always with 16 waves
 // (measured: INT4 8192 x 8192 B = 16 15.0 -> 12.6 us, B = 8 10.9 -> 11.3; INT4
-// 8192 x 28672 B = 8 32.1 -> 27.8 us).
+// 8192 x 28672 B = 8 32.1 -> 27.8 us, B = 4 28.6 -> 26.6 us).
 template <bool TER, bool SK, bool SL>
 mbd_status launch_mq(unsigned blocks, int nw, size_t lds, hipStream_t st, const MqArgs& m) {
-    if (m.B >= 12 || (m.B >= 8 && nw >= 16))
+    if (m.B >= 12 || nw >= 16)
         return launch_mq1<TER, SK, SL, true>(blocks, nw, lds + mq_x_lds(nw), st, m);
     return launch_mq1<TER, SK, SL, false>(blocks, nw, lds, st, m);
 }
@@ -1175,7 +1175,9 @@ mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float*
     const int tiles = int((w->M + 15) / 16);
     const int ngroups = int(w->K / 128);
     const int nw_mq = mq_waves(w->K, MBD_MQ_GPW_GEMV);
-    if (B > 4 && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
+    // from 2 rows with 16-wave blocks (8192 x 28672: B = 2 28.4 -> 24.5 us, B = 4
+    // 30.9 -> 24.5 us against the few-row kernel)
+    if ((B > 4 || (B >= 2 && nw_mq >= 16)) && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
         if (int64_t(B) * w->K >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
@@ -1237,9 +1239,11 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2)) return fail(MBD_EALIGN, "codes must be 16-byte aligned");
     if (w->M == 0) return MBD_OK;
-    if (B > 4) {
+    if (B > 4 || (B == 4 && mq_waves(w->K, MBD_MQ_GPW_GEMV) >= 16)) {
         // 5..16 rows: the 32-row kernel with activations read per group (at 8 rows
-        // it measured even with the few-row kernel, above that faster)
+        // it measured even with the few-row kernel, above that faster); 4 rows too
+        // when its blocks have 16 waves (K >= 16384: INT4 8192 x 28672 29.9 -> 26.6
+        // us, ternary 26.0 -> 23.6 us; at 2 rows ternary measured 3% slower)
         if (int64_t(B) * w->K >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);

@@ -590,10 +590,11 @@ def _random_cases(n, seed):
 
 
 # The batch 5..16 kernel stages the activations through LDS from 12 batch rows, or
-# from 8 when its blocks have 16 waves (K >= 16384); at 9 and 10 rows the third
-# piece of four rows is partly past the batch.
+# whenever its blocks have 16 waves (K >= 16384), where it also takes 4 rows; at 9
+# and 10 rows the third piece of four rows is partly past the batch.
 @pytest.mark.parametrize("kind", ["ternary", "int4"])
-@pytest.mark.parametrize("M,K,B", [(45, 16384, 9), (40, 16512, 10), (33, 2048, 13), (70, 17408, 8), (19, 16384, 7)])
+@pytest.mark.parametrize("M,K,B", [(45, 16384, 9), (40, 16512, 10), (33, 2048, 13), (70, 17408, 8), (19, 16384, 7),
+                                   (21, 16384, 4), (38, 16384, 3)])
 def test_gemv_staged_activation_batches(dev, kind, M, K, B):
     print("case staged gemv", kind, M, K, B, flush=True)
     w = _rand_w(M * 17 + K + B, M, K)
