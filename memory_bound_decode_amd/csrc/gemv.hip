@@ -302,12 +302,24 @@ struct BnArgs {
     int n_experts, topk, x_per_pair;
 };
 
+// Code loads: non-temporal (NT) where a dense matrix streams once, plain where
+// that measured faster (expert matrices: T = 1 11.30 -> 10.90 us, T = 8 56.5 ->
+// 54.2 us; the 32-row kernel's ternary pairs, whose two 8-byte halves of a unit
+// load one group apart: 8192 x 28672 B = 8 26.5 -> 25.0 us).  On the dense
+// few-row kernel plain loads were slower (INT4 8192 x 28672 21.1 -> 22.6 us).
+template <bool NT, class T>
+__device__ __forceinline__ T code_load(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // Tile `tile` of one matrix against nb <= NB activation rows xrow(t); output row
 // n of the tile goes to yrow(n).  XU: staging passes of 64 lanes.  SK (ternary
 // only): the skip format.  An item is still a pair of block columns; lane (m, kq)
 // finds its 8 bytes of each through the column's slab word, or, when tile row m's
-// block is all-zero and not stored, uses code 1 (q = 0) in every field.
-template <bool TER, bool SK, int PF, int NB, int XU, class XRow, class YRow>
+// block is all-zero and not stored, uses code 1 (q = 0) in every field.  NTL:
+// non-temporal code loads.
+template <bool TER, bool SK, int PF, int NB, int XU, bool NTL, class XRow, class YRow>
 __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restrict__ codes,
                                         const uint16_t* __restrict__ scales, int nb, XRow xrow, YRow yrow,
                                         int tile) {
@@ -420,8 +432,7 @@ __device__ __forceinline__ void bn_core(const BnArgs& a, const uint8_t* __restri
                 rmk[p] = rm;
             } else {
                 const uint32_t off = (TER && it >= n_full) ? unit * 8 : unit * 16;
-                const u32x4_t v = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t*>(tcodes + size_t(it) * 64 * R + off));
+                const u32x4_t v = code_load<NTL>(reinterpret_cast<const u32x4_t*>(tcodes + size_t(it) * 64 * R + off));
                 w[p] = make_uint4(v.x, v.y, v.z, v.w);
             }
         };
@@ -536,7 +547,7 @@ __global__ __launch_bounds__(1024) void gemv_bn_kernel(BnArgs a) {
     const uint16_t* x = a.x;
     float* y = a.y;
     const int K = a.K, M = a.M;
-    bn_core<TER, SK, PF, NB, XU>(a, a.codes, a.scales, a.B, [=](int t) { return x + size_t(t) * K; },
+    bn_core<TER, SK, PF, NB, XU, true>(a, a.codes, a.scales, a.B, [=](int t) { return x + size_t(t) * K; },
                              [=](int n) { return y + size_t(n) * M; }, blockIdx.x);
 }
 
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(1024) void moe_b1_kernel(BnArgs a) {
     const size_t per_codes = size_t(M) * K / (TER ? 4 : 2), per_scales = size_t(M) * (K / 128);
     const uint16_t* xr = a.x + size_t(a.x_per_pair ? p : p / a.topk) * K;
     float* yr = a.y + size_t(p) * M;
-    bn_core<TER, false, PF, 1, XU>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales, 1,
+    bn_core<TER, false, PF, 1, XU, false>(a, a.codes + size_t(e) * per_codes, a.scales + size_t(e) * per_scales, 1,
                             [=](int) { return xr; }, [=](int) { return yr; }, tile);
 }
 
@@ -753,8 +764,7 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
                 const int h = g >> 1;
                 const bool pair = h < npairs;
                 const uint8_t* base = codes + (pair ? size_t(h) * item[t] + (g & 1) * 8 : size_t(npairs) * item[t]);
-                const u32x2_t v = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x2_t*>(base + (pair ? coff[t] : coff8[t])));
+                const u32x2_t v = code_load<false>(reinterpret_cast<const u32x2_t*>(base + (pair ? coff[t] : coff8[t])));
                 d.code[t] = make_uint4(v.x, v.y, 0u, 0u);
             } else {
                 // codes stream once: non-temporal, so that the activations every block
