@@ -724,7 +724,7 @@ __device__ __forceinline__ void mq_core(const MqArgs& a, const uint8_t* __restri
     // bytes of batch row 4 i + l / 16 (row 0 past nb) at column 8 (l % 16), so 16
     // lanes read a row's 256 bytes (pieces whose four rows are all past nb are not
     // loaded), and the compute passes them through the wave's LDS rows into MFMA
-    // order.  The round trip pays from 12 batch rows, or from 8 with 16 waves.
+    // order.  The round trip pays from 12 batch rows, or with 16 waves per block.
     uint32_t xo[4];                                        // XS: element offsets in a.x
     const uint16_t* xr = a.x;                              // !XS: batch row n
     if constexpr (XS) {
