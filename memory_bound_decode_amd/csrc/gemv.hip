@@ -604,6 +604,13 @@ inline int mq_waves(int64_t K, int gpw) {
     return int(std::max<int64_t>(1, std::min<int64_t>(MQ_MAXW, (K / 128) / gpw)));
 }
 
+// Few batch rows on the 32-row kernel (activations through LDS) pay only when its
+// blocks have 16 waves and there is a block for every one of the 256 CUs (at
+// 4096 x 16384, 128 blocks, B = 3 took 13.6 against 10.2 us on the few-row kernel).
+inline bool mq_wide(int64_t M, int64_t K) {
+    return mq_waves(K, MBD_MQ_GPW_GEMV) >= 16 && (M + MQ_ROWS - 1) / MQ_ROWS >= 256;
+}
+
 struct MqGroup {
     uint4 code[MQ_TILES];          // INT4: 4 words (32 codes); ternary: .x, .y (32 codes)
     uint32_t sc[MQ_TILES][4];      // raw fp16 scales of the lane's 4 output rows (global
@@ -1191,9 +1198,9 @@ mbd_status gemv_skip(const mbd_dweights* w, const uint16_t* x, int32_t B, float*
     const int tiles = int((w->M + 15) / 16);
     const int ngroups = int(w->K / 128);
     const int nw_mq = mq_waves(w->K, MBD_MQ_GPW_GEMV);
-    // from 2 rows with 16-wave blocks (8192 x 28672: B = 2 28.4 -> 24.5 us, B = 4
-    // 30.9 -> 24.5 us against the few-row kernel)
-    if ((B > 4 || (B >= 2 && nw_mq >= 16)) && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
+    // from 2 rows on wide shapes (8192 x 28672: B = 2 28.4 -> 24.5 us, B = 4 30.9 ->
+    // 24.5 us against the few-row kernel)
+    if ((B > 4 || (B >= 2 && mq_wide(w->M, w->K))) && (ngroups + nw_mq - 1) / nw_mq * MQ_TILES <= 64) {
         if (int64_t(B) * w->K >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);
@@ -1255,11 +1262,12 @@ mbd_status mbd_gemv(const mbd_dweights* w, const uint16_t* x, int32_t B, float* 
     if (!w->sec[0] || !w->sec[1]) return fail(MBD_EINVAL, "codes/scales section is NULL");
     if (!aligned(w->sec[0], 16) || !aligned(w->sec[1], 2)) return fail(MBD_EALIGN, "codes must be 16-byte aligned");
     if (w->M == 0) return MBD_OK;
-    if (B > 4 || (B == 4 && mq_waves(w->K, MBD_MQ_GPW_GEMV) >= 16)) {
+    if (B > 4 || (B >= (ter ? 3 : 2) && mq_wide(w->M, w->K))) {
         // 5..16 rows: the 32-row kernel with activations read per group (at 8 rows
-        // it measured even with the few-row kernel, above that faster); 4 rows too
-        // when its blocks have 16 waves (K >= 16384: INT4 8192 x 28672 29.9 -> 26.6
-        // us, ternary 26.0 -> 23.6 us; at 2 rows ternary measured 3% slower)
+        // it measured even with the few-row kernel, above that faster); on wide
+        // shapes from 2 INT4 or 3 ternary rows (8192 x 28672, against the few-row
+        // kernel: INT4 B = 2 27.1 -> 26.1 us, B = 3 29.3 -> 26.1, B = 4 29.9 -> 26.6;
+        // ternary B = 3 24.5 -> 23.1, B = 4 26.0 -> 23.6; ternary B = 2 within 1%)
         if (int64_t(B) * w->K >= (int64_t(1) << 32)) return fail(MBD_ESHAPE, "activations of 2^32 elements or more");
         MqArgs m{};
         m.codes = static_cast<const uint8_t*>(w->sec[0]);

@@ -193,6 +193,42 @@ def test_gemv_ternary_ffn_full(dev, ternary_ffn_full, B):
     assert err <= TOL
 
 
+@pytest.fixture(scope="module")
+def wide_full(dev):
+    """8192 x 16384 INT4 and ternary matrices (t(4) * 0.02 weights) packed once: the
+    smallest shape with 16-wave blocks on every CU, where 2..4 batch rows take the
+    32-row kernel."""
+    wl = synth.WORKLOADS["ternary_moe"]
+    M, K = 8192, 16384
+    mbd = _mbd()
+    out = {}
+    for i, (kind, fmt) in enumerate((("int4", mbd.MBD_INT4_G128), ("ternary", mbd.MBD_TERNARY_B128))):
+        w = synth.f32_to_bf16_bits(synth.gen_weight_rows(wl.seed + 99 + i, M, K, wl.dist, wl.scale).astype(np.float32))
+        out[kind] = (w, mbd.to_device(mbd.mbd_pack(fmt, w), dev))
+    return wl, out
+
+
+# B = 1 and ternary B = 2 stay on the few-row kernel; the rest of 2..4, and 6, run
+# on the 32-row kernel with the activations through LDS.  Sampled rows against the
+# oracle (the whole fp64 matrix would take 1 GB).
+@pytest.mark.parametrize("kind", ["int4", "ternary"])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 6])
+def test_gemv_wide_few_rows(dev, wide_full, kind, B):
+    wl, mats = wide_full
+    w, dw = mats[kind]
+    M, K = w.shape
+    x = synth.gen_x(wl, B, K)
+    print("case wide %s %dx%d B=%d" % (kind, M, K, B), flush=True)
+    y = _run_gemv(dw, x, dev)
+    assert np.all(np.isfinite(y))
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(M - 40, M),
+                                     np.random.default_rng(B).integers(0, M, 80)]))
+    q, s = QUANT[kind].quantize(w[rows])
+    err, worst = check(y[:, rows], gemv.gemv(QUANT[kind].dequant(q, s), x))
+    print("wide %s B=%d rel_l2=%.3e worst_row=%.3e" % (kind, B, err, worst), flush=True)
+    assert err <= TOL
+
+
 def test_gemv_deterministic(dev):
     wl = synth.WORKLOADS["int4_8k"]
     w = synth.gen_weights(wl, 0, 1024)
@@ -590,8 +626,9 @@ def _random_cases(n, seed):
 
 
 # The batch 5..16 kernel stages the activations through LDS from 12 batch rows, or
-# whenever its blocks have 16 waves (K >= 16384), where it also takes 4 rows; at 9
-# and 10 rows the third piece of four rows is partly past the batch.
+# whenever its blocks have 16 waves (K >= 16384); at 9 and 10 rows the third piece
+# of four rows is partly past the batch.  (3 and 4 rows here, with few blocks, stay
+# on the few-row kernel.)
 @pytest.mark.parametrize("kind", ["ternary", "int4"])
 @pytest.mark.parametrize("M,K,B", [(45, 16384, 9), (40, 16512, 10), (33, 2048, 13), (70, 17408, 8), (19, 16384, 7),
                                    (21, 16384, 4), (38, 16384, 3)])

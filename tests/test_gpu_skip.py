@@ -57,7 +57,8 @@ def _pack(w, dev):
     return mbd.to_device(mbd.mbd_pack(mbd.MBD_TERNARY_SKIP, w), dev)
 
 
-# (29, 16384): 16-wave blocks, where 2..4 rows take the 32-row kernel too
+# (29, 16384): 16-wave blocks of the 32-row kernel (from 5 rows; with one block, 2..4
+# rows stay on the few-row kernel, which the full 8192 x 28672 case below does not)
 RAGGED = [(1, 128), (3, 384), (100, 1152), (333, 1536), (64, 4096), (17, 8320), (5, 128 * 45), (29, 16384)]
 
 
