@@ -69,6 +69,11 @@ void gemv_errors() {
             d = desc(fmts[f], rows[f], 8192);
             expect(mbd_gemv(&d, X16, B, Y16, nullptr), MBD_ESHAPE, "gemv codes of 4 GiB");
         }
+    // batch 5..16 addresses the activations with 32-bit element offsets
+    for (int f = 0; f < 2; ++f) {
+        d = desc(fmts[f], 16, int64_t(1) << 28);
+        expect(mbd_gemv(&d, X16, 16, Y16, nullptr), MBD_ESHAPE, "gemv activations of 2^32 elements");
+    }
     d = desc(MBD_INT4_G128, 16, 256);
     expect(mbd_dequant(&d, nullptr, nullptr), MBD_EINVAL, "dequant NULL output");
     expect(mbd_dequant(&d, static_cast<float*>(fake(0x10004)), nullptr), MBD_EALIGN, "dequant misaligned output");
@@ -169,6 +174,9 @@ void moe_errors() {
     mbd_dweights big = desc(MBD_INT4_G128, int64_t(1) << 20, 8192, 0, 0x1000, 2);
     expect(mbd_moe_gemv_noalloc(&big, R16, 1, 2, X16, 0, Y16, nullptr), MBD_ESHAPE, "noalloc codes of 4 GiB");
     expect(mbd_moe_gemv(&big, R16, 1, 2, X16, 0, Y16, ws, 1 << 20, nullptr), MBD_ESHAPE, "moe codes of 4 GiB");
+    mbd_dweights wide = desc(MBD_TERNARY_B128, 1, int64_t(1) << 30, 0, 0x1000, 2);
+    expect(mbd_moe_gemv(&wide, R16, 2, 2, X16, 1, Y16, ws, 1 << 20, nullptr), MBD_ESHAPE, "moe activations of 2^32 elements");
+    expect(mbd_moe_gemv_noalloc(&wide, R16, 2, 2, X16, 1, Y16, nullptr), MBD_ESHAPE, "noalloc activations of 2^32 elements");
 }
 
 void probe_errors() {
